@@ -1,0 +1,145 @@
+"""Seeded synthetic inputs for the MoE layer workloads.
+
+One element definition, two independent implementations:
+
+* ``synth_host.c``  (gcc, OpenMP)  -> numpy arrays on the host, used by the
+  oracle to regenerate exactly the rows / experts it needs;
+* ``synth_dev.hip`` (hipcc, gfx950) -> tensors filled directly in HBM, used
+  by the GPU path and the benchmark.
+
+Element ``i`` of tensor ``(seed, stream, index)`` is an Irwin-Hall(8)
+approximately-normal variate built from one Philox4x32-10 call (see the
+header of ``synth_host.c``), scaled to the requested standard deviation with
+one fp32 multiply, and optionally rounded to bf16 (nearest-even).  Nothing of
+the MoE layer's arithmetic lives in this module.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+HOST_LIB = os.path.join(_HERE, "libsynth_host.so")
+DEV_LIB = os.path.join(_HERE, "libsynth_dev.so")
+
+# Standard deviation of c = 2*d - 524280, d a sum of eight uniform 16-bit integers.
+_C_STD = math.sqrt(8.0 / 3.0 * (2.0**32 - 1.0))
+
+
+def scale_for(sigma: float) -> float:
+    """fp32 multiplier that maps the integer variate to standard deviation sigma."""
+    return float(np.float32(sigma / _C_STD))
+
+
+_host = None
+_dev = None
+
+
+def _host_lib():
+    global _host
+    if _host is None:
+        if not os.path.exists(HOST_LIB):
+            raise RuntimeError(f"{HOST_LIB} is missing: run __graft_entry__.build() first")
+        lib = ctypes.CDLL(HOST_LIB)
+        u32, i64, u64, f32, vp = (ctypes.c_uint32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float,
+                                  ctypes.c_void_p)
+        lib.synth_philox4x32_10.argtypes = [vp, vp, vp]
+        lib.synth_philox4x32_10.restype = None
+        for name in ("synth_fill_f32", "synth_fill_bf16"):
+            fn = getattr(lib, name)
+            fn.argtypes = [u32, u32, u32, u64, i64, f32, vp]
+            fn.restype = None
+        for name in ("synth_fill_rows_f32", "synth_fill_rows_bf16"):
+            fn = getattr(lib, name)
+            fn.argtypes = [u32, u32, u32, i64, vp, i64, f32, vp]
+            fn.restype = None
+        _host = lib
+    return _host
+
+
+def _dev_lib():
+    global _dev
+    if _dev is None:
+        if not os.path.exists(DEV_LIB):
+            raise RuntimeError(f"{DEV_LIB} is missing: run __graft_entry__.build() first")
+        lib = ctypes.CDLL(DEV_LIB)
+        lib.synth_dev_fill.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint32,
+                                       ctypes.c_uint32, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                                       ctypes.c_void_p]
+        lib.synth_dev_fill.restype = ctypes.c_int
+        _dev = lib
+    return _dev
+
+
+def philox4x32_10(counter, key):
+    """Raw generator call (4 x uint32 counter, 2 x uint32 key) -> 4 x uint32."""
+    c = np.asarray(counter, dtype=np.uint32).copy()
+    k = np.asarray(key, dtype=np.uint32).copy()
+    out = np.zeros(4, dtype=np.uint32)
+    _host_lib().synth_philox4x32_10(c.ctypes.data, k.ctypes.data, out.ctypes.data)
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) to float32."""
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def host_tensor(seed: int, stream: int, index: int, shape, sigma: float, dtype: str,
+                elem0: int = 0) -> np.ndarray:
+    """Elements [elem0, elem0 + prod(shape)) of tensor (seed, stream, index).
+
+    dtype 'bf16' returns uint16 bit patterns, 'f32' returns float32.
+    """
+    n = int(np.prod(shape))
+    lib = _host_lib()
+    if dtype == "bf16":
+        out = np.empty(n, dtype=np.uint16)
+        lib.synth_fill_bf16(seed, stream, index, elem0, n, scale_for(sigma), out.ctypes.data)
+    elif dtype == "f32":
+        out = np.empty(n, dtype=np.float32)
+        lib.synth_fill_f32(seed, stream, index, elem0, n, scale_for(sigma), out.ctypes.data)
+    else:
+        raise ValueError(dtype)
+    return out.reshape(shape)
+
+
+def host_rows(seed: int, stream: int, index: int, cols: int, rows, sigma: float, dtype: str) -> np.ndarray:
+    """Selected rows of the [*, cols] tensor (seed, stream, index)."""
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    lib = _host_lib()
+    if dtype == "bf16":
+        out = np.empty((rows.size, cols), dtype=np.uint16)
+        lib.synth_fill_rows_bf16(seed, stream, index, cols, rows.ctypes.data, rows.size, scale_for(sigma),
+                                 out.ctypes.data)
+    elif dtype == "f32":
+        out = np.empty((rows.size, cols), dtype=np.float32)
+        lib.synth_fill_rows_f32(seed, stream, index, cols, rows.ctypes.data, rows.size, scale_for(sigma),
+                                out.ctypes.data)
+    else:
+        raise ValueError(dtype)
+    return out
+
+
+def device_fill(tensor, seed: int, stream: int, index0: int, n_index: int, per_index: int, sigma: float):
+    """Fill a contiguous torch tensor on the GPU with n_index stacked tensors of
+    per_index elements, tensor j being (seed, stream, index0 + j)."""
+    import torch
+
+    if not tensor.is_contiguous() or tensor.numel() != n_index * per_index:
+        raise ValueError("device_fill: tensor must be contiguous with n_index*per_index elements")
+    if tensor.dtype == torch.bfloat16:
+        is_bf16 = 1
+    elif tensor.dtype == torch.float32:
+        is_bf16 = 0
+    else:
+        raise ValueError(f"device_fill: unsupported dtype {tensor.dtype}")
+    stream_ptr = torch.cuda.current_stream(tensor.device).cuda_stream
+    rc = _dev_lib().synth_dev_fill(tensor.data_ptr(), is_bf16, seed, stream, index0, n_index, per_index,
+                                   scale_for(sigma), stream_ptr)
+    if rc != 0:
+        raise RuntimeError(f"synth_dev_fill failed with status {rc}")
+    return tensor

@@ -1,0 +1,87 @@
+// Seeded synthetic inputs for the MoE layer workloads, device side.
+//
+// Independent twin of synth_host.c: the same element definition, written
+// again for the GPU so that multi-gigabyte weight stacks are produced in HBM
+// in milliseconds while the host can regenerate any single expert, row or
+// element bit-for-bit.  No arithmetic of the MoE layer lives here.
+//
+// Generator: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11), ten rounds
+// with multipliers 0xD2511F53 / 0xCD9E8D57 and key increments
+// 0x9E3779B9 / 0xBB67AE85.  Element e of tensor (seed, stream, index):
+//   counter = (e lo32, e hi32, index, 0), key = (seed, stream)
+//   d = sum of the eight 16-bit halves of the four output words
+//   value = fl32((float)(2*d - 524280) * scale), bf16 by round-to-nearest-even.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+__device__ __forceinline__ void philox_round(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3,
+                                             uint32_t k0, uint32_t k1) {
+  const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+  const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+  const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+  const uint32_t n1 = (uint32_t)p1;
+  const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+  const uint32_t n3 = (uint32_t)p0;
+  c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+}
+
+__device__ __forceinline__ float element_value(uint32_t seed, uint32_t stream, uint32_t index,
+                                               uint64_t e, float scale) {
+  uint32_t c0 = (uint32_t)e, c1 = (uint32_t)(e >> 32), c2 = index, c3 = 0u;
+  uint32_t k0 = seed, k1 = stream;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    philox_round(c0, c1, c2, c3, k0, k1);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  const int32_t d = (int32_t)((c0 & 0xffffu) + (c0 >> 16) + (c1 & 0xffffu) + (c1 >> 16) +
+                              (c2 & 0xffffu) + (c2 >> 16) + (c3 & 0xffffu) + (c3 >> 16));
+  const int32_t c = 2 * d - 524280;
+  return __fmul_rn((float)c, scale);
+}
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// out is a stack of n_index tensors of per_index elements each, tensor j
+// being (seed, stream, index0 + j).
+template <bool BF16>
+__global__ void synth_fill_kernel(void* __restrict__ out, uint32_t seed, uint32_t stream,
+                                  uint32_t index0, int64_t per_index, int64_t total, float scale) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total; g += stride) {
+    const int64_t j = g / per_index;
+    const int64_t e = g - j * per_index;
+    const float v = element_value(seed, stream, index0 + (uint32_t)j, (uint64_t)e, scale);
+    if (BF16)
+      static_cast<uint16_t*>(out)[g] = bf16_rne(v);
+    else
+      static_cast<float*>(out)[g] = v;
+  }
+}
+
+}  // namespace
+
+extern "C" int synth_dev_fill(void* out, int32_t is_bf16, uint32_t seed, uint32_t stream,
+                              uint32_t index0, int64_t n_index, int64_t per_index, float scale,
+                              void* hip_stream) {
+  if (out == nullptr || n_index < 0 || per_index < 0) return 1;
+  const int64_t total = n_index * per_index;
+  if (total == 0) return 0;
+  const int threads = 256;
+  int64_t blocks = (total + threads - 1) / threads;
+  if (blocks > 65536) blocks = 65536;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (is_bf16)
+    synth_fill_kernel<true><<<(unsigned)blocks, threads, 0, s>>>(out, seed, stream, index0, per_index,
+                                                                 total, scale);
+  else
+    synth_fill_kernel<false><<<(unsigned)blocks, threads, 0, s>>>(out, seed, stream, index0, per_index,
+                                                                  total, scale);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}

@@ -1,0 +1,105 @@
+/*
+ * Seeded synthetic inputs for the MoE layer workloads, host side.
+ *
+ * This module holds no arithmetic of the MoE layer itself: it only turns
+ * (seed, stream, index, element) into a number.  The device twin
+ * (synth_dev.hip) implements the same definition independently so that a
+ * tensor generated on the GPU and the same tensor regenerated here on the
+ * host are bit-identical.
+ *
+ * Generator: Philox4x32-10, the counter-based generator of Salmon, Moraes,
+ * Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11):
+ * ten rounds of two 32x32->64 multiplies (constants 0xD2511F53 and
+ * 0xCD9E8D57), with the key advanced by the Weyl constants 0x9E3779B9 and
+ * 0xBB67AE85 between rounds.
+ *
+ * Element definition (used identically on both sides):
+ *   key     = (seed, stream)
+ *   counter = (elem & 0xffffffff, elem >> 32, index, 0)
+ *   r[0..3] = philox4x32_10(counter, key)
+ *   d       = sum of the eight 16-bit halves of r[0..3]      (0 .. 524280)
+ *   c       = 2*d - 524280                                   (even, |c| <= 524280)
+ *   value   = (float)c * scale      one correctly rounded fp32 multiply
+ * where scale = fl32(sigma / sqrt(8/3 * (2^32 - 1))) is supplied by the
+ * caller, so that value has mean 0 and standard deviation sigma.  The sum of
+ * eight uniforms (Irwin-Hall, n = 8) is an approximately normal variate with
+ * support +-4.9 sigma; it uses only exact integer arithmetic plus one IEEE
+ * multiply, so host and device agree bit for bit.  bf16 output rounds the
+ * fp32 value to nearest-even.
+ */
+#include <stdint.h>
+#include <stddef.h>
+
+static inline void mulhilo32(uint32_t a, uint32_t b, uint32_t *hi, uint32_t *lo) {
+  uint64_t p = (uint64_t)a * (uint64_t)b;
+  *hi = (uint32_t)(p >> 32);
+  *lo = (uint32_t)p;
+}
+
+void synth_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4]) {
+  uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+  uint32_t k0 = key_in[0], k1 = key_in[1];
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+    uint32_t hi0, lo0, hi1, lo1;
+    mulhilo32(0xD2511F53u, c0, &hi0, &lo0);
+    mulhilo32(0xCD9E8D57u, c2, &hi1, &lo1);
+    uint32_t n0 = hi1 ^ c1 ^ k0;
+    uint32_t n1 = lo1;
+    uint32_t n2 = hi0 ^ c3 ^ k1;
+    uint32_t n3 = lo0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+static inline float synth_value(uint32_t seed, uint32_t stream, uint32_t index, uint64_t elem,
+                                float scale) {
+  uint32_t ctr[4] = {(uint32_t)elem, (uint32_t)(elem >> 32), index, 0u};
+  uint32_t key[2] = {seed, stream};
+  uint32_t r[4];
+  synth_philox4x32_10(ctr, key, r);
+  int32_t d = 0;
+  for (int i = 0; i < 4; ++i) d += (int32_t)(r[i] & 0xffffu) + (int32_t)(r[i] >> 16);
+  int32_t c = 2 * d - 524280;
+  return (float)c * scale;  /* (float)c is exact: |c| < 2^24 */
+}
+
+static inline uint16_t f32_to_bf16_rne(float f) {
+  union { float f; uint32_t u; } v;
+  v.f = f;
+  uint32_t lsb = (v.u >> 16) & 1u;
+  return (uint16_t)((v.u + 0x7fffu + lsb) >> 16);
+}
+
+/* Fill out[i] for i in [0, n): element (elem0 + i) of tensor (seed, stream, index). */
+void synth_fill_f32(uint32_t seed, uint32_t stream, uint32_t index, uint64_t elem0, int64_t n,
+                    float scale, float *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = synth_value(seed, stream, index, elem0 + (uint64_t)i, scale);
+}
+
+void synth_fill_bf16(uint32_t seed, uint32_t stream, uint32_t index, uint64_t elem0, int64_t n,
+                     float scale, uint16_t *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i)
+    out[i] = f32_to_bf16_rne(synth_value(seed, stream, index, elem0 + (uint64_t)i, scale));
+}
+
+/* Rows of a [rows, cols] tensor: row_ids[j] selects the row; out is [n_rows, cols]. */
+void synth_fill_rows_bf16(uint32_t seed, uint32_t stream, uint32_t index, int64_t cols,
+                          const int64_t *row_ids, int64_t n_rows, float scale, uint16_t *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < n_rows; ++j)
+    for (int64_t c = 0; c < cols; ++c)
+      out[j * cols + c] = f32_to_bf16_rne(
+          synth_value(seed, stream, index, (uint64_t)(row_ids[j] * cols + c), scale));
+}
+
+void synth_fill_rows_f32(uint32_t seed, uint32_t stream, uint32_t index, int64_t cols,
+                         const int64_t *row_ids, int64_t n_rows, float scale, float *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < n_rows; ++j)
+    for (int64_t c = 0; c < cols; ++c)
+      out[j * cols + c] = synth_value(seed, stream, index, (uint64_t)(row_ids[j] * cols + c), scale);
+}

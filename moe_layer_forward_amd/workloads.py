@@ -1,0 +1,186 @@
+"""The five synthetic workloads of the K2 MoE layer, and how their inputs are made.
+
+Shapes and distributions (all draws seeded, see ``synth``):
+
+==========  =====  ====  ====  ===  ==  ======  ==================================
+name          T      H     I    E   K  dtype   routing
+==========  =====  ====  ====  ===  ==  ======  ==================================
+tiny           64   256   128   16   2  f32     sigmoid router
+decode         64  7168  2048  384   8  bf16    sigmoid router
+prefill      8192  7168  2048  384   8  bf16    sigmoid router (near-uniform)
+skew         4096  7168  2048  384   8  bf16    router + Zipf-shaped logit offsets
+ep_share    16384  7168  2048    3   1  bf16    pre-dispatched ids/weights, no router
+==========  =====  ====  ====  ===  ==  ======  ==================================
+
+Each has one always-on shared expert of the routed experts' shape and the
+routed scaling factor 2.827.
+
+Distributions: activations N(0, 1); router weight N(0, 0.02); gate/up
+N(0, 1/sqrt(H)); down N(0, 1/sqrt(I)) -- "N(0, a)" reads a as a standard
+deviation.  Draws are Irwin-Hall(8) approximately-normal variates (see
+``synth``).  The four full-shape workloads share one weight set (seed 100);
+their activations use the workload number (2..5) as seed; tiny uses seed 1.
+
+Synthetic streams: 0 activations, 1 router, 2 gate, 3 up, 4 down, 5/6/7 shared
+gate/up/down (Philox, index = expert id); 8 skew permutation, 9 EP-share ids,
+10 EP-share weights (numpy PCG64 from SeedSequence([seed, stream])).
+
+Skew offsets: o_e = -1.1 * ln(r_e) added to expert e's logit before the
+sigmoid, r a seeded permutation of 1..E -- a Zipf(s = 1.1)-shaped popularity
+prior.  Exact Zipf counts are impossible under top-8 (the hottest expert
+would need more picks than there are tokens), so the offsets shape the
+logits and the realised histogram is reported.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import synth
+
+RSF_K2 = 2.827
+
+S_X, S_ROUTER, S_GATE, S_UP, S_DOWN, S_SGATE, S_SUP, S_SDOWN = range(8)
+S_SKEW, S_EP_IDS, S_EP_W = 8, 9, 10
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int
+    H: int
+    I: int
+    E: int
+    K: int
+    dtype: str                    # 'bf16' | 'f32'
+    x_seed: int
+    w_seed: int
+    routing: str = "router"       # 'router' | 'skew' | 'preassigned'
+    n_shared: int = 1
+    rsf: float = RSF_K2
+    sigma_x: float = 1.0
+    sigma_router: float = 0.02
+    extra: dict = field(default_factory=dict, compare=False)
+
+    @property
+    def sigma_gate_up(self) -> float:
+        return 1.0 / math.sqrt(self.H)
+
+    @property
+    def sigma_down(self) -> float:
+        return 1.0 / math.sqrt(self.I)
+
+    @property
+    def pairs(self) -> int:
+        return self.T * self.K
+
+    def with_tokens(self, T: int) -> "Workload":
+        return Workload(self.name, T, self.H, self.I, self.E, self.K, self.dtype, self.x_seed, self.w_seed,
+                        self.routing, self.n_shared, self.rsf, self.sigma_x, self.sigma_router)
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 64, 256, 128, 16, 2, "f32", x_seed=1, w_seed=1),
+    "decode": Workload("decode", 64, 7168, 2048, 384, 8, "bf16", x_seed=2, w_seed=100),
+    "prefill": Workload("prefill", 8192, 7168, 2048, 384, 8, "bf16", x_seed=3, w_seed=100),
+    "skew": Workload("skew", 4096, 7168, 2048, 384, 8, "bf16", x_seed=4, w_seed=100, routing="skew"),
+    "ep_share": Workload("ep_share", 16384, 7168, 2048, 3, 1, "bf16", x_seed=5, w_seed=100,
+                         routing="preassigned"),
+}
+
+
+def custom(name, T, H, I, E, K, dtype="bf16", x_seed=11, w_seed=12, routing="router", n_shared=1):
+    """A workload with the same recipe at other sizes (parity cases)."""
+    return Workload(name, T, H, I, E, K, dtype, x_seed, w_seed, routing, n_shared)
+
+
+# --------------------------------------------------------------------------- host side
+def _np_rng(seed: int, stream: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream])))
+
+
+def logit_offsets(w: Workload):
+    """fp32 [E] skew offsets, or None."""
+    if w.routing != "skew":
+        return None
+    r = _np_rng(w.x_seed, S_SKEW).permutation(w.E) + 1
+    return (-1.1 * np.log(r.astype(np.float64))).astype(np.float32)
+
+
+def preassigned(w: Workload):
+    """(ids int32 [T,K], weights fp32 [T,K]) for the pre-dispatched EP share."""
+    ids = _np_rng(w.x_seed, S_EP_IDS).integers(0, w.E, size=(w.T, w.K)).astype(np.int32)
+    wts = (_np_rng(w.x_seed, S_EP_W).uniform(0.05, 0.6, size=(w.T, w.K)) * w.rsf).astype(np.float32)
+    return ids, wts
+
+
+def _to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return synth.bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def host_x_rows(w: Workload, rows) -> np.ndarray:
+    return _to_f64(synth.host_rows(w.x_seed, S_X, 0, w.H, rows, w.sigma_x, w.dtype), w.dtype)
+
+
+def host_x(w: Workload) -> np.ndarray:
+    return host_x_rows(w, np.arange(w.T))
+
+
+def host_router(w: Workload) -> np.ndarray:
+    return _to_f64(synth.host_tensor(w.w_seed, S_ROUTER, 0, (w.E, w.H), w.sigma_router, w.dtype), w.dtype)
+
+
+def host_expert(w: Workload, e: int):
+    """(W_gate [I,H], W_up [I,H], W_down [H,I]) of routed expert e, float64."""
+    g = synth.host_tensor(w.w_seed, S_GATE, e, (w.I, w.H), w.sigma_gate_up, w.dtype)
+    u = synth.host_tensor(w.w_seed, S_UP, e, (w.I, w.H), w.sigma_gate_up, w.dtype)
+    d = synth.host_tensor(w.w_seed, S_DOWN, e, (w.H, w.I), w.sigma_down, w.dtype)
+    return _to_f64(g, w.dtype), _to_f64(u, w.dtype), _to_f64(d, w.dtype)
+
+
+def host_shared(w: Workload):
+    if w.n_shared == 0:
+        return None
+    g = synth.host_tensor(w.w_seed, S_SGATE, 0, (w.I, w.H), w.sigma_gate_up, w.dtype)
+    u = synth.host_tensor(w.w_seed, S_SUP, 0, (w.I, w.H), w.sigma_gate_up, w.dtype)
+    d = synth.host_tensor(w.w_seed, S_SDOWN, 0, (w.H, w.I), w.sigma_down, w.dtype)
+    return _to_f64(g, w.dtype), _to_f64(u, w.dtype), _to_f64(d, w.dtype)
+
+
+# --------------------------------------------------------------------------- device side
+def device_inputs(w: Workload, device="cuda"):
+    """All inputs of the workload, resident in HBM (torch tensors)."""
+    import torch
+
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    t = {}
+    t["x"] = synth.device_fill(torch.empty((w.T, w.H), dtype=dt, device=device), w.x_seed, S_X, 0, 1,
+                               w.T * w.H, w.sigma_x)
+    if w.routing != "preassigned":
+        t["w_router"] = synth.device_fill(torch.empty((w.E, w.H), dtype=dt, device=device), w.w_seed, S_ROUTER,
+                                          0, 1, w.E * w.H, w.sigma_router)
+    t["w_gate"] = synth.device_fill(torch.empty((w.E, w.I, w.H), dtype=dt, device=device), w.w_seed, S_GATE, 0,
+                                    w.E, w.I * w.H, w.sigma_gate_up)
+    t["w_up"] = synth.device_fill(torch.empty((w.E, w.I, w.H), dtype=dt, device=device), w.w_seed, S_UP, 0,
+                                  w.E, w.I * w.H, w.sigma_gate_up)
+    t["w_down"] = synth.device_fill(torch.empty((w.E, w.H, w.I), dtype=dt, device=device), w.w_seed, S_DOWN, 0,
+                                    w.E, w.H * w.I, w.sigma_down)
+    if w.n_shared:
+        t["ws_gate"] = synth.device_fill(torch.empty((w.I, w.H), dtype=dt, device=device), w.w_seed, S_SGATE, 0,
+                                         1, w.I * w.H, w.sigma_gate_up)
+        t["ws_up"] = synth.device_fill(torch.empty((w.I, w.H), dtype=dt, device=device), w.w_seed, S_SUP, 0, 1,
+                                       w.I * w.H, w.sigma_gate_up)
+        t["ws_down"] = synth.device_fill(torch.empty((w.H, w.I), dtype=dt, device=device), w.w_seed, S_SDOWN, 0,
+                                         1, w.H * w.I, w.sigma_down)
+    off = logit_offsets(w)
+    if off is not None:
+        t["logit_offset"] = torch.from_numpy(off).to(device)
+    if w.routing == "preassigned":
+        ids, wts = preassigned(w)
+        t["topk_ids"] = torch.from_numpy(ids).to(device)
+        t["topk_weights"] = torch.from_numpy(wts).to(device)
+    return t
