@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the K2 MoE layer forward on one MI355X.
+
+One step = one call of the whole layer (router GEMM, top-K, permutation, grouped gate/up and down
+SwiGLU GEMMs, combine) on a batch of synthetic tokens whose inputs and weights are already resident
+in HBM.  The printed line's value is the decode workload (T=64, the 384-expert K2 layer); the
+prefill workload (T=8192) is measured in the same run and reported beside it.  Per-kernel times
+come from HIP events recorded around every kernel launch inside the timed steps.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|skew|ep_share|tiny]
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "K2 MoE layer tokens/s at T=64 decode & T=8192 prefill; % HBM / % MFMA peak"
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+BF16_PEAK = 2.5e15         # dense bf16 MFMA FLOP/s
+F32_PEAK = 157.3e12        # fp32 vector FLOP/s
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw HIP events (the runtime torch has loaded), recorded by the library around each kernel."""
+
+    def __init__(self, n):
+        import torch  # noqa: F401
+
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev[i] = h
+        self.n = n
+
+    def slice(self, start, count):
+        return ctypes.cast(ctypes.byref(self.ev, start * ctypes.sizeof(ctypes.c_void_p)),
+                           ctypes.POINTER(ctypes.c_void_p)), count
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.ev[a], self.ev[b])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(self.ev[i])
+
+
+def kernel_work(name, w, n_groups_active, rows):
+    """Algorithmic (bytes, flops) of one launch of a grouped GEMM kernel: the weights of every group
+    with rows read once, the token rows / h read once, the outputs written once."""
+    eb = 2 if w.dtype == "bf16" else 4
+    if name.startswith("gateup"):
+        wbytes = n_groups_active * 2 * w.I * w.H * eb
+        return wbytes + w.T * w.H * eb + rows * w.I * eb, rows * 2 * 2 * w.I * w.H
+    if name.startswith("down"):
+        wbytes = n_groups_active * w.H * w.I * eb
+        return wbytes + rows * w.I * eb + rows * w.H * eb, rows * 2 * w.H * w.I
+    return None, None
+
+
+def layer_work(w, n_touched):
+    """Algorithmic bytes and flops of the whole layer: every touched expert's and the shared expert's
+    weights once, the router weight, x read and y written once."""
+    eb = 2 if w.dtype == "bf16" else 4
+    n_exp = n_touched + w.n_shared
+    bytes_ = n_exp * 3 * w.H * w.I * eb + 2 * w.T * w.H * eb
+    flops = (w.T * w.K + w.T * w.n_shared) * 2 * 3 * w.H * w.I
+    if w.routing != "preassigned":
+        bytes_ += w.E * w.H * eb
+        flops += 2 * w.T * w.E * w.H
+    return bytes_, flops
+
+
+def run(w, weights, steps, warmup):
+    import numpy as np
+    import torch
+
+    import moe_layer_forward_amd as moe
+    from moe_layer_forward_amd import workloads as wl
+
+    acts = wl.device_activations(w)
+    cfg = moe.config_for(w)
+    T = w.T
+    y = torch.empty((T, w.H), dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32, device="cuda")
+    if w.routing == "preassigned":
+        ws = moe.alloc_workspace(cfg, moe.MOE_OP_FORWARD_ROUTED, T)
+        wg, wu, wd = (weights[k][:w.E] for k in ("w_gate", "w_up", "w_down"))
+
+        def step():
+            moe.moe_forward_routed(cfg, acts["x"], acts["topk_ids"], acts["topk_weights"], wg, wu, wd,
+                                   weights["ws_gate"], weights["ws_up"], weights["ws_down"], workspace=ws, out=y)
+    else:
+        ws = moe.alloc_workspace(cfg, moe.MOE_OP_FORWARD, T)
+
+        def step():
+            moe.moe_forward(cfg, acts["x"], weights["w_router"], weights["w_gate"], weights["w_up"],
+                            weights["w_down"], weights["ws_gate"], weights["ws_up"], weights["ws_down"],
+                            logit_offset=acts.get("logit_offset"), workspace=ws, out=y)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # kernels per step (the library reports what it launched)
+    probe = HipEvents(64)
+    moe.moe_profile_events(*probe.slice(0, 64))
+    step()
+    torch.cuda.synchronize()
+    names = [moe.moe_profile_kernel(i) for i in range(moe.moe_profile_count())]
+    moe.moe_profile_events(None, 0)
+    probe.close()
+    per = 2 * len(names)
+    ev = HipEvents(per * steps)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        moe.moe_profile_events(*ev.slice(i * per, per))
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    moe.moe_profile_events(None, 0)
+
+    kern = {n: 0.0 for n in names}
+    for i in range(steps):
+        for j, n in enumerate(names):
+            kern[n] += ev.elapsed_ms(i * per + 2 * j, i * per + 2 * j + 1) / steps
+    ev.close()
+    ms = (t1 - t0) * 1e3 / steps
+
+    # routing actually realised (counts touched experts for the byte accounting)
+    if w.routing == "preassigned":
+        ids = acts["topk_ids"]
+    else:
+        ids, _ = moe.moe_route(cfg, acts["x"], weights["w_router"], logit_offset=acts.get("logit_offset"))
+    counts = np.bincount(ids.cpu().numpy().ravel(), minlength=w.E)
+    n_touched = int((counts > 0).sum())
+    rows = T * w.K + T * w.n_shared
+    lb, lf = layer_work(w, n_touched)
+    dom = max(kern, key=kern.get)
+    kb, kf = kernel_work(dom, w, n_touched + w.n_shared, rows)
+    dom_s = kern[dom] * 1e-3
+    peak_flops = BF16_PEAK if w.dtype == "bf16" else F32_PEAK
+    if kb is not None and kf / kb < peak_flops / HBM_PEAK:
+        roof = {"bound": "hbm", "achieved": kb / dom_s / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": kb / dom_s / HBM_PEAK, "traffic": None, "kernel": dom,
+                "bytes_per_launch": kb, "flops_per_launch": kf, "avg_launch_us": kern[dom] * 1e3}
+    elif kb is not None:
+        roof = {"bound": "mfma", "achieved": kf / dom_s / 1e12, "peak": peak_flops / 1e12, "unit": "TFLOP/s",
+                "frac": kf / dom_s / peak_flops, "traffic": None, "kernel": dom,
+                "bytes_per_launch": kb, "flops_per_launch": kf, "avg_launch_us": kern[dom] * 1e3}
+    else:
+        roof = None
+    s = ms * 1e-3
+    layer = {"GB_s": lb / s / 1e9, "TFLOP_s": lf / s / 1e12, "hbm_frac": lb / s / HBM_PEAK,
+             "mfma_frac": lf / s / peak_flops, "alg_bytes": lb, "alg_flops": lf, "touched_experts": n_touched,
+             "rows_per_expert_max": int(counts.max()), "experts_le2_rows": int((counts <= 2).sum())}
+    return {"tokens_per_s": T / s, "ms_per_step": ms, "roofline": roof, "layer": layer,
+            "kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()}}
+
+
+def cpu_baseline(w, n_tokens):
+    """The oracle as it stands, on the first n_tokens tokens of the workload, on the host cores.
+    Only the oracle's own arithmetic is timed (weight regeneration excluded)."""
+    import numpy as np
+
+    import oracle
+    from moe_layer_forward_amd import workloads as wl
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    tokens = np.arange(n_tokens)
+    x = wl.host_x_rows(w, tokens)
+    router = wl.host_router(w)
+    gen = [0.0]
+
+    def expert(e):
+        g0 = time.perf_counter()
+        r = wl.host_expert(w, e)
+        gen[0] += time.perf_counter() - g0
+        return r
+
+    shared = wl.host_shared(w)
+    t0 = time.perf_counter()
+    oracle.moe_forward(x, router, expert, shared, w.K, w.rsf, logit_offset=wl.logit_offsets(w))
+    el = time.perf_counter() - t0 - gen[0]
+    return {"value": n_tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n_tokens} tokens of the {w.name} workload (T={w.T}), all {w.K}+{w.n_shared} experts "
+                      f"each, float64 numpy; {el:.2f} s of oracle arithmetic, weight regeneration not timed"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skew", "ep_share", "tiny"])
+    ap.add_argument("--also", default="prefill", help="second workload measured in the same run ('none' to skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=6, help="tokens in the oracle's CPU-baseline sample (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this implementation runs on one GPU; --gpus must be 1 (sharding across GPUs is "
+              "described in DESIGN.md but not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from moe_layer_forward_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    main_w = wl.WORKLOADS[args.workload]
+    weights_cache = {}
+
+    def weights_for(w):
+        key = (w.w_seed, w.dtype, w.H, w.I, w.E if w.w_seed != 100 else 384)
+        if key not in weights_cache:
+            src = wl.WORKLOADS["decode"] if w.w_seed == 100 else w
+            log(f"generating weights for {src.name} ...")
+            weights_cache[key] = wl.device_weights(src)
+            torch.cuda.synchronize()
+        return weights_cache[key]
+
+    log(f"running {main_w.name} ...")
+    res = run(main_w, weights_for(main_w), args.steps, args.warmup)
+    out = {
+        "metric": METRIC, "value": res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": main_w.dtype, "data": "synthetic (seeded Irwin-Hall(8) ~normal draws)",
+        "config": {"workload": main_w.name, "T": main_w.T, "H": main_w.H, "I": main_w.I, "E": main_w.E,
+                   "K": main_w.K, "n_shared": main_w.n_shared, "routed_scaling_factor": main_w.rsf,
+                   "parallelism": "1 GPU"},
+        "roofline": res["roofline"], "layer": res["layer"], "kernels_us": res["kernels_us"],
+    }
+    if args.also != "none" and args.also != args.workload:
+        w2 = wl.WORKLOADS[args.also]
+        log(f"running {w2.name} ...")
+        r2 = run(w2, weights_for(w2), args.steps, args.warmup)
+        out[w2.name] = {"value": r2["tokens_per_s"], "unit": "tokens/s", "ms_per_step": r2["ms_per_step"],
+                        "config": {"workload": w2.name, "T": w2.T}, "roofline": r2["roofline"],
+                        "layer": r2["layer"], "kernels_us": r2["kernels_us"]}
+    weights_cache.clear()
+    torch.cuda.empty_cache()
+    if args.cpu_tokens > 0:
+        log("timing the oracle on the host ...")
+        out["cpu_baseline"] = cpu_baseline(main_w, min(args.cpu_tokens, main_w.T))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) forward pass of the Kimi-K2 MoE FFN layer.
+ *
+ * Sources cited below (the section on the page):
+ *   [DEEP]        "Kimi K2.5 模型架构深度拆解" (pillumina.github.io/posts/architecture/kimi-k2.5):
+ *                 §4.2 routing, §4.3 expert FFN, §10.2 MoE data flow Steps 1-7.
+ *   [QA]          "Kimi K2.5 架构 QA" (cctoctofx.netlify.app/posts/qa/kimi-k2.5-qa):
+ *                 Q2.1 parameters, Q2.3 routed_scaling_factor, Q7.2 bias buffer, Q8.3 dispatch.
+ *   [ZH-INFRA]    Zhihu answer by a K2 inference engineer on the K2 config:
+ *                 §2.1 num_experts = 384, §2.4 n_group = 1.
+ *   [ZH-PRETRAIN] Zhihu answer by a K2 pretraining author, "架构 / 异": scaling factor 2.5 -> 2.827.
+ *
+ * The layer, per token t (rows are independent):
+ *   l_e = x_t . Wr_e (+ o_e);  s_e = sigmoid(l_e);  key_e = s_e + b_e
+ *   S_t = top-K keys over all E experts (no groups), ties -> smaller id
+ *   w_te = rsf * s_e / sum_{S_t} s          (the bias b selects only)
+ *   F(x) = W_down (SiLU(W_gate x) * (W_up x))
+ *   y_t  = sum_{e in S_t} w_te F_e(x_t) + F_shared(x_t)
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked "host".  The config struct
+ *     is a host struct read during the call only.
+ *   - Tensors are row-major and contiguous.  Weights use the nn.Linear
+ *     [out, in] layout: w_gate/w_up [E, I, H], w_down [E, H, I].
+ *   - dtype (config) is the element type of x, y, the router weight and the
+ *     expert weights: MOE_BF16 (fp32 accumulation, the intermediate h rounded
+ *     to bf16) or MOE_F32.  Routing scores/weights are always fp32, ids int32.
+ *   - Ownership: the caller allocates every buffer; the library allocates and
+ *     frees nothing and keeps no pointer after a call returns.  Scratch comes
+ *     from the caller's `workspace` (device, 256-byte aligned), sized by
+ *     moe_workspace_size().
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Work is
+ *     enqueued asynchronously; no call copies to the host or synchronises.
+ *     Group sizes never leave the device.
+ *   - Errors: arguments are checked synchronously before anything is
+ *     launched.  On failure the call returns a moe_status, launches nothing and
+ *     sets a thread-local message readable with moe_last_error().  T == 0 (or no
+ *     rows) returns MOE_OK and launches nothing.  A failed launch returns
+ *     MOE_ERR_DEVICE.  Faults during execution surface at the caller's next
+ *     synchronisation.  Calls are reentrant; calls that share a workspace must
+ *     be ordered on one stream.
+ *   - Supported shapes: hidden_size and moe_intermediate_size multiples of 128;
+ *     1 <= top_k <= min(64, n_routed_experts); n_routed_experts <= 512; n_group == topk_group == 1;
+ *     n_shared_experts 0 or 1; norm_topk_prob == 1.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* NULL where a pointer is required, negative size, K > E, ...      */
+  MOE_ERR_UNSUPPORTED = 2, /* a valid configuration this library does not implement             */
+  MOE_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than moe_workspace_size()               */
+  MOE_ERR_DEVICE = 4       /* a HIP launch failed                                               */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Which call a workspace is sized for (moe_workspace_size). */
+typedef enum {
+  MOE_OP_ROUTE = 0,
+  MOE_OP_PERMUTE = 1,
+  MOE_OP_GROUPED_SWIGLU = 2,
+  MOE_OP_COMBINE = 3,
+  MOE_OP_FORWARD = 4,
+  MOE_OP_FORWARD_ROUTED = 5
+} moe_op;
+
+/* The MoE config fields of the K2 layer ([DEEP] §4.2-§4.3; [ZH-INFRA] §2.4). Host struct. */
+typedef struct moe_config {
+  int32_t hidden_size;           /* H: 7168                                                */
+  int32_t moe_intermediate_size; /* I: 2048                                                */
+  int32_t n_routed_experts;      /* E: 384                                                 */
+  int32_t top_k;                 /* K: 8                                                   */
+  int32_t n_shared_experts;      /* 0 or 1 (K2: 1, weight 1, never scaled)                 */
+  int32_t n_group;               /* must be 1: the router has no expert groups             */
+  int32_t topk_group;            /* must be 1                                              */
+  int32_t norm_topk_prob;        /* must be 1: weights are normalised to sum 1 ...         */
+  float routed_scaling_factor;   /* ... then multiplied by this (K2: 2.827)                */
+  int32_t dtype;                 /* moe_dtype of x, y, router and expert weights           */
+} moe_config;
+
+/* Bytes of workspace the call `op` needs.
+ *   MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_COMBINE, MOE_OP_FORWARD, MOE_OP_FORWARD_ROUTED:
+ *       rows = T (tokens), n_groups ignored.
+ *   MOE_OP_GROUPED_SWIGLU: rows = max_rows, n_groups = number of groups.
+ * Returns 0 for an invalid config (see moe_last_error()). */
+size_t moe_workspace_size(const moe_config* cfg, int32_t op, int64_t rows, int32_t n_groups);
+
+/* Router: [DEEP] §10.2 Steps 1-4, §4.2; n_group = 1 per [ZH-INFRA] §2.4; scale 2.827 per
+ * [ZH-PRETRAIN] and [QA] Q2.3.
+ *   x            [T, H]  dtype
+ *   w_router     [E, H]  dtype
+ *   score_bias   [E] fp32 or NULL: e_score_correction_bias ([QA] Q7.2), added to the
+ *                scores for the top-K choice only; the weights use the unbiased scores.
+ *   logit_offset [E] fp32 or NULL: added to the logits before the sigmoid (synthetic skew).
+ *   topk_ids     [T, K] int32 out: the K experts with the largest key, key descending,
+ *                ties to the smaller id.
+ *   topk_weights [T, K] fp32 out: rsf * s / sum(s) over the selected experts.
+ * Workspace: moe_workspace_size(cfg, MOE_OP_ROUTE, T, 0). */
+int moe_route(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+              const float* score_bias, const float* logit_offset, int32_t* topk_ids,
+              float* topk_weights, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Dispatch permutation: [DEEP] §10.2 Step 6 (tokens of each expert gathered together).
+ * Pairs (t, k) are grouped into per-expert contiguous segments of a row space
+ * [0, T*K); inside a segment they keep (t, k) order.
+ *   topk_ids       [T, K] int32 in, each in [0, E)
+ *   expert_offsets [E + 1] int32 out: segment e is rows [off[e], off[e+1]); off[E] = T*K
+ *   row_token      [T * K] int32 out: token of row r
+ *   pair_row       [T * K] int32 out: row of pair (t, k) at index t*K + k
+ *   x, x_perm      both NULL, or x [T, H] dtype in and x_perm [T*K, H] out (x_perm[r] = x[row_token[r]])
+ * Workspace: moe_workspace_size(cfg, MOE_OP_PERMUTE, T, 0). */
+int moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_ids, int32_t* expert_offsets,
+                int32_t* row_token, int32_t* pair_row, const void* x, void* x_perm, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* Grouped SwiGLU experts: [DEEP] §4.3 and §10.2 Steps 5-6 (gate+up -> SiLU -> x -> down),
+ * batched over groups as the grouped GEMM of [QA] Q8.3.
+ * For every group g and row r in [group_offsets[g], group_offsets[g+1]):
+ *     a = x[row_index ? row_index[r] : r]
+ *     y_rows[r] = row_scale[r] (or 1) * W_down[g] (SiLU(W_gate[g] a) * (W_up[g] a))
+ *   n_groups       G >= 1 (host)
+ *   group_offsets  [G + 1] int32, non-decreasing, group_offsets[0] = 0, last <= max_rows
+ *   max_rows       host upper bound on group_offsets[G]; rows at or beyond it are not computed
+ *   x              [*, H] dtype; row_index [max_rows] int32 or NULL
+ *   w_gate, w_up   [G, I, H] dtype; w_down [G, H, I] dtype
+ *   row_scale      [max_rows] fp32 or NULL
+ *   y_rows         [max_rows, H] of y_dtype (MOE_F32 or MOE_BF16; MOE_F32 when dtype is MOE_F32)
+ * Workspace: moe_workspace_size(cfg, MOE_OP_GROUPED_SWIGLU, max_rows, G). */
+int moe_grouped_swiglu(const moe_config* cfg, int32_t n_groups, const int32_t* group_offsets,
+                       int64_t max_rows, const void* x, const int32_t* row_index, const void* w_gate,
+                       const void* w_up, const void* w_down, const float* row_scale, void* y_rows,
+                       int32_t y_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Weighted combine: [DEEP] §10.2 Steps 6-7; [QA] Q8.3 (index_add_ accumulation).
+ *     y[t] = sum_k topk_weights[t,k] * y_rows[pair_row[t,k]]  (+ y_shared[t])
+ * summed in fp32 in k order, the shared row last, rounded once to dtype.
+ *   y_rows   [*, H] of y_dtype;  pair_row [T, K] int32;  topk_weights [T, K] fp32
+ *   y_shared [T, H] of y_dtype or NULL;  y [T, H] dtype out
+ * No workspace. */
+int moe_combine(const moe_config* cfg, int64_t T, const void* y_rows, int32_t y_dtype,
+                const int32_t* pair_row, const float* topk_weights, const void* y_shared, void* y,
+                void* stream);
+
+/* The whole layer: [DEEP] §10.2 Steps 1-7.
+ *   x [T, H]; w_router [E, H]; score_bias, logit_offset as in moe_route
+ *   w_gate, w_up [E, I, H]; w_down [E, H, I]            routed experts
+ *   ws_gate, ws_up [I, H]; ws_down [H, I]                shared expert (required iff n_shared_experts = 1)
+ *   y [T, H] dtype out
+ *   topk_ids_out [T, K] int32, topk_weights_out [T, K] fp32: optional copies of the routing (or NULL)
+ * Workspace: moe_workspace_size(cfg, MOE_OP_FORWARD, T, 0). */
+int moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                const float* score_bias, const float* logit_offset, const void* w_gate, const void* w_up,
+                const void* w_down, const void* ws_gate, const void* ws_up, const void* ws_down, void* y,
+                int32_t* topk_ids_out, float* topk_weights_out, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* The layer for tokens that arrive already routed (one expert-parallel rank's share:
+ * [ZH-INFRA] §2.1 places 3 routed + 1 shared expert per rank at EP = 128): Steps 5-7 of
+ * [DEEP] §10.2 with topk_ids [T, K] int32 and topk_weights [T, K] fp32 given.
+ * Workspace: moe_workspace_size(cfg, MOE_OP_FORWARD_ROUTED, T, 0). */
+int moe_forward_routed(const moe_config* cfg, int64_t T, const void* x, const int32_t* topk_ids,
+                       const float* topk_weights, const void* w_gate, const void* w_up,
+                       const void* w_down, const void* ws_gate, const void* ws_up, const void* ws_down,
+                       void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message of the last failed call on this thread ("" if none); valid until the next call. */
+const char* moe_last_error(void);
+
+/* Per-kernel timing for profilers and benchmarks (not needed for normal use).
+ *   events    host array of n_events hipEvent_t handles (as void*), created by the caller; the
+ *             library only records them.  NULL / 0 switches timing off.
+ * While set (per thread), each later call on this thread records events[2i] and events[2i+1] on
+ * its stream right before and right after its i-th kernel launch, for up to min(n_events/2, 32)
+ * launches.  moe_profile_count() and moe_profile_kernel(i) report what the last call on this
+ * thread launched ("router_logits", "topk", "permute", "plan", "gateup_stream", "down_stream",
+ * "gateup_tile", "down_tile", "combine", ...). */
+int moe_profile_events(void* const* events, int32_t n_events);
+int32_t moe_profile_count(void);
+const char* moe_profile_kernel(int32_t i);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,111 @@
+// Internal interface between the C-ABI host layer (moe_api.cpp) and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ----------------------------------------------------------------------------- element helpers
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Logistic function in fp32 with IEEE division.
+__device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+// SwiGLU activation of one (gate, up) pair: SiLU(g) * u.
+__device__ __forceinline__ float swiglu_f32(float g, float u) { return g * sigmoid_f32(g) * u; }
+
+constexpr int kXcds = 8;  // MI355X: 8 XCDs, work-groups dealt round-robin by blockIdx
+
+// ----------------------------------------------------------------------------- launch descriptors
+// Row groups of a grouped GEMM.  Rows of group g are [group_offsets[g], group_offsets[g+1]),
+// clamped to max_rows; the A row of row r is row_index ? row_index[r] : r.
+struct Groups {
+  int32_t n_groups = 0;
+  const int32_t* group_offsets = nullptr;  // [G+1] device
+  int64_t max_rows = 0;
+  const int32_t* row_index = nullptr;      // [max_rows] device or null
+  // Plan (workspace), written by launch_plan.
+  int32_t* active = nullptr;               // [G] ids of groups with rows
+  int32_t* counters = nullptr;             // [0] n_active, [1] n_tiles
+  int32_t* tiles = nullptr;                // [2 * max_tiles] (group, first row in group)
+  int32_t max_tiles = 0;
+  int32_t tile_m = 0;                      // rows per tile in the tile list
+};
+
+// Expert weights by group: group g < shared_group uses the stacked tensors at index g; the group
+// equal to shared_group uses the s_* tensors.
+struct Weights {
+  const void* gate = nullptr;  // [*, I, H]
+  const void* up = nullptr;    // [*, I, H]
+  const void* down = nullptr;  // [*, H, I]
+  const void* s_gate = nullptr;
+  const void* s_up = nullptr;
+  const void* s_down = nullptr;
+  int32_t shared_group = -1;
+};
+
+// ----------------------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.
+
+// routing ---------------------------------------------------------------------
+// K splits of the router GEMM (its partial sums are [nsplit, T, E] fp32); 1 for fp32 inputs.
+int router_nsplit(int64_t T, int H, int E, bool bf16);
+// part[s, T, E] (fp32) = x[T, H] . w_router[E, H]^T restricted to the s-th K range
+hipError_t launch_router_logits_bf16(const uint16_t* x, const uint16_t* w_router, float* part, int64_t T,
+                                     int H, int E, hipStream_t s);
+hipError_t launch_router_logits_f32(const float* x, const float* w_router, float* logits, int64_t T, int H,
+                                    int E, hipStream_t s);
+// sum of the partials, sigmoid, bias, top-K, normalise, scale: one wave per token.
+hipError_t launch_topk(const float* part, int nsplit, const float* logit_offset, const float* score_bias,
+                       int64_t T, int E, int K, float rsf, int32_t* ids, float* weights, hipStream_t s);
+
+// permutation -----------------------------------------------------------------
+int64_t permute_blocks(int64_t pairs);
+// Scratch ints the permutation needs (block counts).
+int64_t permute_scratch_ints(int64_t pairs, int E);
+// group_offsets gets E+1 entries, plus a final T*K + T entry when shared_rows (the shared
+// expert's rows follow the routed rows; row_token of those rows is filled with t).
+hipError_t launch_permute(const int32_t* ids, int64_t T, int K, int E, int32_t* group_offsets,
+                          int32_t* row_token, int32_t* pair_row, int32_t* scratch, bool shared_rows,
+                          hipStream_t s);
+hipError_t launch_gather_rows(const void* x, const int32_t* row_token, void* x_perm, int64_t rows, int H,
+                              int elem_bytes, hipStream_t s);
+
+// plan --------------------------------------------------------------------------
+hipError_t launch_plan(const Groups& g, hipStream_t s);
+
+// grouped SwiGLU, bf16 ------------------------------------------------------------
+// h[r, I] (bf16) = SiLU(a Wg^T) * (a Wu^T) for every row of every active group.
+hipError_t launch_gateup_stream_bf16(const Groups& g, const Weights& w, const uint16_t* x, uint16_t* h, int H,
+                                     int I, hipStream_t s);
+hipError_t launch_gateup_tile_bf16(const Groups& g, const Weights& w, const uint16_t* x, uint16_t* h, int H,
+                                   int I, hipStream_t s);
+// y_rows[r, H] = row_scale[r] * h[r] Wd^T   (y fp32 when y_bf16 == false)
+hipError_t launch_down_stream_bf16(const Groups& g, const Weights& w, const uint16_t* h, void* y_rows,
+                                   bool y_bf16, const float* row_scale, int H, int I, hipStream_t s);
+hipError_t launch_down_tile_bf16(const Groups& g, const Weights& w, const uint16_t* h, void* y_rows,
+                                 bool y_bf16, const float* row_scale, int H, int I, hipStream_t s);
+// Rows per tile used by the tile kernels' plan.
+constexpr int kTileM = 128;
+
+// grouped SwiGLU, fp32 (plain kernels) ---------------------------------------------
+hipError_t launch_gateup_f32(const Groups& g, const Weights& w, const float* x, float* h, int H, int I,
+                             hipStream_t s);
+hipError_t launch_down_f32(const Groups& g, const Weights& w, const float* h, float* y_rows,
+                           const float* row_scale, int H, int I, hipStream_t s);
+
+// combine -------------------------------------------------------------------------
+hipError_t launch_combine(const void* y_rows, bool rows_bf16, const int32_t* pair_row, const float* weights,
+                          const void* y_shared, void* y, bool y_bf16, int64_t T, int K, int H, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,480 @@
+// C-ABI host layer of libmoe: argument checks, workspace layout, kernel choice, launches.
+// The operations are those of include/moe.h (see the citations there); nothing here touches data:
+// every step of the layer runs in the kernels of this directory.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kernels.h"
+#include "moe.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+int device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MOE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Optional per-kernel timing (moe_profile_events): events[2i] / events[2i+1] are recorded on the
+// call's stream before / after its i-th kernel launch.
+constexpr int kMaxProfiled = 32;
+struct Profile {
+  void* const* events = nullptr;
+  int n_events = 0;
+  int count = 0;
+  const char* names[kMaxProfiled] = {};
+};
+thread_local Profile g_prof;
+
+void prof_reset() { g_prof.count = 0; }
+
+template <class F>
+hipError_t timed(const char* name, hipStream_t s, F&& launch) {
+  Profile& p = g_prof;
+  const int i = p.count;
+  const bool on = p.events != nullptr && i < kMaxProfiled && 2 * i + 1 < p.n_events;
+  if (on) {
+    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(p.events[2 * i]), s);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch();
+  if (on) {
+    if (e == hipSuccess) e = hipEventRecord(static_cast<hipEvent_t>(p.events[2 * i + 1]), s);
+    p.names[i] = name;
+    p.count = i + 1;
+  }
+  return e;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Carves aligned sub-buffers out of the caller's workspace (or just measures when base is null).
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(int64_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+    used += align_up((size_t)(count > 0 ? count : 0) * sizeof(T));
+    return p;
+  }
+};
+
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 64;
+constexpr int kMaxGroups = 4096;
+
+int check_config(const moe_config* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "config is NULL");
+  if (c->hidden_size <= 0 || c->moe_intermediate_size <= 0 || c->n_routed_experts <= 0 || c->top_k <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "sizes must be positive (H=%d I=%d E=%d K=%d)", c->hidden_size,
+                c->moe_intermediate_size, c->n_routed_experts, c->top_k);
+  if (c->top_k > c->n_routed_experts)
+    return fail(MOE_ERR_INVALID_ARG, "top_k (%d) > n_routed_experts (%d)", c->top_k, c->n_routed_experts);
+  if (c->n_shared_experts < 0) return fail(MOE_ERR_INVALID_ARG, "n_shared_experts < 0");
+  if (c->n_group != 1 || c->topk_group != 1)
+    return fail(MOE_ERR_UNSUPPORTED, "only n_group = topk_group = 1 (router without expert groups) is supported");
+  if (c->norm_topk_prob != 1) return fail(MOE_ERR_UNSUPPORTED, "only norm_topk_prob = 1 is supported");
+  if (c->n_shared_experts > 1) return fail(MOE_ERR_UNSUPPORTED, "at most one shared expert is supported");
+  if (c->hidden_size % 128 || c->moe_intermediate_size % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "hidden_size and moe_intermediate_size must be multiples of 128");
+  if (c->n_routed_experts > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "n_routed_experts > %d", kMaxExperts);
+  if (c->top_k > kMaxTopK) return fail(MOE_ERR_UNSUPPORTED, "top_k > %d", kMaxTopK);
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "dtype %d", c->dtype);
+  if (!(c->routed_scaling_factor == c->routed_scaling_factor)) return fail(MOE_ERR_INVALID_ARG, "scale is NaN");
+  return MOE_OK;
+}
+
+int check_tokens(int64_t T, const moe_config* c) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "negative token count");
+  const int64_t rows = T * (c->top_k + 1);
+  if (rows > 0x7fffffffLL) return fail(MOE_ERR_UNSUPPORTED, "T*(K+1) exceeds 2^31-1");
+  return MOE_OK;
+}
+
+size_t elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+bool use_stream_kernels(int64_t max_rows, int G) { return max_rows <= 4LL * G; }
+
+// Grouped SwiGLU scratch: h, then the plan.
+struct SwigluWs {
+  void* h;
+  moe::Groups g;
+};
+
+SwigluWs carve_swiglu(Carver& cv, const moe_config* c, int G, int64_t max_rows) {
+  SwigluWs w{};
+  w.h = cv.take<char>(max_rows * c->moe_intermediate_size * (int64_t)elem_bytes(c->dtype));
+  w.g.n_groups = G;
+  w.g.max_rows = max_rows;
+  w.g.tile_m = moe::kTileM;
+  w.g.max_tiles = (int32_t)((max_rows + moe::kTileM - 1) / moe::kTileM + G);
+  w.g.active = cv.take<int32_t>(G);
+  w.g.counters = cv.take<int32_t>(2);
+  w.g.tiles = cv.take<int32_t>(2LL * w.g.max_tiles);
+  return w;
+}
+
+// Launch plan + both grouped GEMMs over prepared groups.
+hipError_t run_swiglu(const moe_config* c, const moe::Groups& g, const moe::Weights& w, const void* x, void* h,
+                      const float* row_scale, void* y_rows, bool y_bf16, hipStream_t s) {
+  const int H = c->hidden_size, I = c->moe_intermediate_size;
+  hipError_t e = timed("plan", s, [&] { return moe::launch_plan(g, s); });
+  if (e != hipSuccess) return e;
+  if (c->dtype == MOE_F32) {
+    e = timed("gateup_f32", s, [&] {
+      return moe::launch_gateup_f32(g, w, static_cast<const float*>(x), static_cast<float*>(h), H, I, s);
+    });
+    if (e != hipSuccess) return e;
+    return timed("down_f32", s, [&] {
+      return moe::launch_down_f32(g, w, static_cast<const float*>(h), static_cast<float*>(y_rows), row_scale, H, I, s);
+    });
+  }
+  if (use_stream_kernels(g.max_rows, g.n_groups)) {
+    e = timed("gateup_stream", s, [&] {
+      return moe::launch_gateup_stream_bf16(g, w, static_cast<const uint16_t*>(x), static_cast<uint16_t*>(h), H, I, s);
+    });
+    if (e != hipSuccess) return e;
+    return timed("down_stream", s, [&] {
+      return moe::launch_down_stream_bf16(g, w, static_cast<const uint16_t*>(h), y_rows, y_bf16, row_scale, H, I, s);
+    });
+  }
+  e = timed("gateup_tile", s, [&] {
+    return moe::launch_gateup_tile_bf16(g, w, static_cast<const uint16_t*>(x), static_cast<uint16_t*>(h), H, I, s);
+  });
+  if (e != hipSuccess) return e;
+  return timed("down_tile", s, [&] {
+    return moe::launch_down_tile_bf16(g, w, static_cast<const uint16_t*>(h), y_rows, y_bf16, row_scale, H, I, s);
+  });
+}
+
+// Workspace of the full forward (router optional).
+struct ForwardWs {
+  int32_t* ids;
+  float* weights;
+  float* router_part;
+  int32_t* offsets;
+  int32_t* row_token;
+  int32_t* pair_row;
+  int32_t* perm_scratch;
+  SwigluWs sw;
+  void* y_rows;
+};
+
+ForwardWs carve_forward(Carver& cv, const moe_config* c, int64_t T, bool with_router) {
+  const int H = c->hidden_size, E = c->n_routed_experts, K = c->top_k;
+  const bool shared = c->n_shared_experts == 1;
+  const int64_t P = T * K;
+  const int64_t rows = P + (shared ? T : 0);
+  const int G = E + (shared ? 1 : 0);
+  ForwardWs w{};
+  w.ids = cv.take<int32_t>(P);
+  w.weights = cv.take<float>(P);
+  w.router_part = with_router ? cv.take<float>((int64_t)moe::router_nsplit(T, H, E, c->dtype == MOE_BF16) * T * E)
+                              : nullptr;
+  w.offsets = cv.take<int32_t>(E + 2);
+  w.row_token = cv.take<int32_t>(rows);
+  w.pair_row = cv.take<int32_t>(P);
+  w.perm_scratch = cv.take<int32_t>(moe::permute_scratch_ints(P, E));
+  w.sw = carve_swiglu(cv, c, G, rows);
+  w.y_rows = cv.take<char>(rows * H * (int64_t)elem_bytes(c->dtype));
+  return w;
+}
+
+int run_after_routing(const moe_config* c, int64_t T, const void* x, const int32_t* ids, const float* weights,
+                      const void* w_gate, const void* w_up, const void* w_down, const void* ws_gate,
+                      const void* ws_up, const void* ws_down, void* y, ForwardWs& w, hipStream_t s) {
+  const int H = c->hidden_size, E = c->n_routed_experts, K = c->top_k;
+  const bool shared = c->n_shared_experts == 1;
+  const int64_t P = T * K;
+  hipError_t e = timed("permute", s, [&] {
+    return moe::launch_permute(ids, T, K, E, w.offsets, w.row_token, w.pair_row, w.perm_scratch, shared, s);
+  });
+  if (e != hipSuccess) return device_status(e, "permute");
+  moe::Groups g = w.sw.g;
+  g.group_offsets = w.offsets;
+  g.row_index = w.row_token;
+  moe::Weights wt;
+  wt.gate = w_gate;
+  wt.up = w_up;
+  wt.down = w_down;
+  if (shared) {
+    wt.s_gate = ws_gate;
+    wt.s_up = ws_up;
+    wt.s_down = ws_down;
+    wt.shared_group = E;
+  }
+  const bool rows_bf16 = c->dtype == MOE_BF16;
+  e = run_swiglu(c, g, wt, x, w.sw.h, nullptr, w.y_rows, rows_bf16, s);
+  if (e != hipSuccess) return device_status(e, "grouped swiglu");
+  const char* yr = static_cast<const char*>(w.y_rows);
+  const void* ysh = shared ? yr + P * H * (int64_t)elem_bytes(c->dtype) : nullptr;
+  e = timed("combine", s, [&] {
+    return moe::launch_combine(w.y_rows, rows_bf16, w.pair_row, weights, ysh, y, c->dtype == MOE_BF16, T, K, H, s);
+  });
+  if (e != hipSuccess) return device_status(e, "combine");
+  return ok();
+}
+
+hipError_t run_router(const moe_config* c, int64_t T, const void* x, const void* w_router, float* part,
+                      hipStream_t s) {
+  const int H = c->hidden_size, E = c->n_routed_experts;
+  if (c->dtype == MOE_BF16)
+    return timed("router_logits", s, [&] {
+      return moe::launch_router_logits_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
+                                            part, T, H, E, s);
+    });
+  return timed("router_logits_f32", s, [&] {
+    return moe::launch_router_logits_f32(static_cast<const float*>(x), static_cast<const float*>(w_router), part, T,
+                                         H, E, s);
+  });
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return MOE_OK;
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (have < need) return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", have, need);
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+    return fail(MOE_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_config* cfg, int32_t op, int64_t rows, int32_t n_groups) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  if (rows < 0) {
+    fail(MOE_ERR_INVALID_ARG, "negative rows");
+    return 0;
+  }
+  Carver cv(nullptr);
+  switch (op) {
+    case MOE_OP_ROUTE:
+      cv.take<float>((int64_t)moe::router_nsplit(rows, cfg->hidden_size, cfg->n_routed_experts,
+                                                 cfg->dtype == MOE_BF16) * rows * cfg->n_routed_experts);
+      break;
+    case MOE_OP_PERMUTE:
+      cv.take<int32_t>(moe::permute_scratch_ints(rows * cfg->top_k, cfg->n_routed_experts));
+      break;
+    case MOE_OP_GROUPED_SWIGLU:
+      if (n_groups < 1 || n_groups > kMaxGroups) {
+        fail(MOE_ERR_INVALID_ARG, "n_groups must be in [1, %d]", kMaxGroups);
+        return 0;
+      }
+      carve_swiglu(cv, cfg, n_groups, rows);
+      break;
+    case MOE_OP_COMBINE:
+      break;
+    case MOE_OP_FORWARD:
+      if (check_tokens(rows, cfg) != MOE_OK) return 0;
+      carve_forward(cv, cfg, rows, true);
+      break;
+    case MOE_OP_FORWARD_ROUTED:
+      if (check_tokens(rows, cfg) != MOE_OK) return 0;
+      carve_forward(cv, cfg, rows, false);
+      break;
+    default:
+      fail(MOE_ERR_INVALID_ARG, "unknown op %d", op);
+      return 0;
+  }
+  ok();
+  return cv.used;
+}
+
+int moe_route(const moe_config* cfg, int64_t T, const void* x, const void* w_router, const float* score_bias,
+              const float* logit_offset, int32_t* topk_ids, float* topk_weights, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  prof_reset();
+  int st = check_config(cfg);
+  if (st) return st;
+  if ((st = check_tokens(T, cfg))) return st;
+  if (T == 0) return ok();
+  if (!x || !w_router || !topk_ids || !topk_weights)
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: x, w_router, topk_ids and topk_weights are required");
+  const int H = cfg->hidden_size, E = cfg->n_routed_experts, K = cfg->top_k;
+  const bool bf16 = cfg->dtype == MOE_BF16;
+  Carver cv(workspace);
+  const int nsplit = moe::router_nsplit(T, H, E, bf16);
+  float* part = cv.take<float>((int64_t)nsplit * T * E);
+  if ((st = check_ws(workspace, workspace_bytes, cv.used))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = run_router(cfg, T, x, w_router, part, s);
+  if (e != hipSuccess) return device_status(e, "router logits");
+  e = timed("topk", s, [&] {
+    return moe::launch_topk(part, nsplit, logit_offset, score_bias, T, E, K, cfg->routed_scaling_factor, topk_ids,
+                            topk_weights, s);
+  });
+  return device_status(e, "top-k");
+}
+
+int moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_ids, int32_t* expert_offsets,
+                int32_t* row_token, int32_t* pair_row, const void* x, void* x_perm, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  prof_reset();
+  int st = check_config(cfg);
+  if (st) return st;
+  if ((st = check_tokens(T, cfg))) return st;
+  if (T == 0) return ok();
+  if (!topk_ids || !expert_offsets || !row_token || !pair_row)
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: topk_ids, expert_offsets, row_token and pair_row are required");
+  if ((x == nullptr) != (x_perm == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: x and x_perm must both be given or both be NULL");
+  const int E = cfg->n_routed_experts, K = cfg->top_k;
+  Carver cv(workspace);
+  int32_t* scratch = cv.take<int32_t>(moe::permute_scratch_ints(T * K, E));
+  if ((st = check_ws(workspace, workspace_bytes, cv.used))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("permute", s, [&] {
+    return moe::launch_permute(topk_ids, T, K, E, expert_offsets, row_token, pair_row, scratch, false, s);
+  });
+  if (e != hipSuccess) return device_status(e, "permute");
+  if (x) {
+    e = timed("gather", s, [&] {
+      return moe::launch_gather_rows(x, row_token, x_perm, T * K, cfg->hidden_size, (int)elem_bytes(cfg->dtype), s);
+    });
+    if (e != hipSuccess) return device_status(e, "gather");
+  }
+  return ok();
+}
+
+int moe_grouped_swiglu(const moe_config* cfg, int32_t n_groups, const int32_t* group_offsets, int64_t max_rows,
+                       const void* x, const int32_t* row_index, const void* w_gate, const void* w_up,
+                       const void* w_down, const float* row_scale, void* y_rows, int32_t y_dtype, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  prof_reset();
+  int st = check_config(cfg);
+  if (st) return st;
+  if (n_groups < 1 || n_groups > kMaxGroups) return fail(MOE_ERR_INVALID_ARG, "n_groups must be in [1, %d]", kMaxGroups);
+  if (max_rows < 0) return fail(MOE_ERR_INVALID_ARG, "negative max_rows");
+  if (max_rows > 0x7fffffffLL) return fail(MOE_ERR_UNSUPPORTED, "max_rows exceeds 2^31-1");
+  if (max_rows == 0) return ok();
+  if (!group_offsets || !x || !w_gate || !w_up || !w_down || !y_rows)
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_swiglu: group_offsets, x, weights and y_rows are required");
+  if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "y_dtype %d", y_dtype);
+  if (cfg->dtype == MOE_F32 && y_dtype != MOE_F32)
+    return fail(MOE_ERR_UNSUPPORTED, "fp32 layers produce fp32 y_rows");
+  Carver cv(workspace);
+  SwigluWs w = carve_swiglu(cv, cfg, n_groups, max_rows);
+  if ((st = check_ws(workspace, workspace_bytes, cv.used))) return st;
+  w.g.group_offsets = group_offsets;
+  w.g.row_index = row_index;
+  moe::Weights wt;
+  wt.gate = w_gate;
+  wt.up = w_up;
+  wt.down = w_down;
+  hipError_t e = run_swiglu(cfg, w.g, wt, x, w.h, row_scale, y_rows, y_dtype == MOE_BF16,
+                            static_cast<hipStream_t>(stream));
+  return device_status(e, "grouped swiglu");
+}
+
+int moe_combine(const moe_config* cfg, int64_t T, const void* y_rows, int32_t y_dtype, const int32_t* pair_row,
+                const float* topk_weights, const void* y_shared, void* y, void* stream) {
+  prof_reset();
+  int st = check_config(cfg);
+  if (st) return st;
+  if ((st = check_tokens(T, cfg))) return st;
+  if (T == 0) return ok();
+  if (!y_rows || !pair_row || !topk_weights || !y)
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine: y_rows, pair_row, topk_weights and y are required");
+  if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "y_dtype %d", y_dtype);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("combine", s, [&] {
+    return moe::launch_combine(y_rows, y_dtype == MOE_BF16, pair_row, topk_weights, y_shared, y,
+                               cfg->dtype == MOE_BF16, T, cfg->top_k, cfg->hidden_size, s);
+  });
+  return device_status(e, "combine");
+}
+
+int moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_router, const float* score_bias,
+                const float* logit_offset, const void* w_gate, const void* w_up, const void* w_down,
+                const void* ws_gate, const void* ws_up, const void* ws_down, void* y, int32_t* topk_ids_out,
+                float* topk_weights_out, void* workspace, size_t workspace_bytes, void* stream) {
+  prof_reset();
+  int st = check_config(cfg);
+  if (st) return st;
+  if ((st = check_tokens(T, cfg))) return st;
+  if (T == 0) return ok();
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !y)
+    return fail(MOE_ERR_INVALID_ARG, "moe_forward: x, w_router, expert weights and y are required");
+  if (cfg->n_shared_experts == 1 && (!ws_gate || !ws_up || !ws_down))
+    return fail(MOE_ERR_INVALID_ARG, "moe_forward: shared expert weights are required");
+  const int H = cfg->hidden_size, E = cfg->n_routed_experts, K = cfg->top_k;
+  const bool bf16 = cfg->dtype == MOE_BF16;
+  Carver cv(workspace);
+  ForwardWs w = carve_forward(cv, cfg, T, true);
+  if ((st = check_ws(workspace, workspace_bytes, cv.used))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* ids = topk_ids_out ? topk_ids_out : w.ids;
+  float* weights = topk_weights_out ? topk_weights_out : w.weights;
+  hipError_t e = run_router(cfg, T, x, w_router, w.router_part, s);
+  if (e != hipSuccess) return device_status(e, "router logits");
+  e = timed("topk", s, [&] {
+    return moe::launch_topk(w.router_part, moe::router_nsplit(T, H, E, bf16), logit_offset, score_bias, T, E, K,
+                            cfg->routed_scaling_factor, ids, weights, s);
+  });
+  if (e != hipSuccess) return device_status(e, "top-k");
+  return run_after_routing(cfg, T, x, ids, weights, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y, w, s);
+}
+
+int moe_forward_routed(const moe_config* cfg, int64_t T, const void* x, const int32_t* topk_ids,
+                       const float* topk_weights, const void* w_gate, const void* w_up, const void* w_down,
+                       const void* ws_gate, const void* ws_up, const void* ws_down, void* y, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  prof_reset();
+  int st = check_config(cfg);
+  if (st) return st;
+  if ((st = check_tokens(T, cfg))) return st;
+  if (T == 0) return ok();
+  if (!x || !topk_ids || !topk_weights || !w_gate || !w_up || !w_down || !y)
+    return fail(MOE_ERR_INVALID_ARG, "moe_forward_routed: x, routing, expert weights and y are required");
+  if (cfg->n_shared_experts == 1 && (!ws_gate || !ws_up || !ws_down))
+    return fail(MOE_ERR_INVALID_ARG, "moe_forward_routed: shared expert weights are required");
+  Carver cv(workspace);
+  ForwardWs w = carve_forward(cv, cfg, T, false);
+  if ((st = check_ws(workspace, workspace_bytes, cv.used))) return st;
+  return run_after_routing(cfg, T, x, topk_ids, topk_weights, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y, w,
+                           static_cast<hipStream_t>(stream));
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int moe_profile_events(void* const* events, int32_t n_events) {
+  if (n_events < 0 || (n_events > 0 && events == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "moe_profile_events: need events for n_events > 0");
+  g_prof.events = n_events > 0 ? events : nullptr;
+  g_prof.n_events = n_events;
+  g_prof.count = 0;
+  return ok();
+}
+
+int32_t moe_profile_count(void) { return g_prof.count; }
+
+const char* moe_profile_kernel(int32_t i) {
+  return (i >= 0 && i < g_prof.count && i < kMaxProfiled && g_prof.names[i]) ? g_prof.names[i] : "";
+}
+
+}  // extern "C"

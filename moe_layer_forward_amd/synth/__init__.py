@@ -63,6 +63,8 @@ def _host_lib():
 def _dev_lib():
     global _dev
     if _dev is None:
+        import torch  # noqa: F401  (bind to the HIP runtime torch has loaded)
+
         if not os.path.exists(DEV_LIB):
             raise RuntimeError(f"{DEV_LIB} is missing: run __graft_entry__.build() first")
         lib = ctypes.CDLL(DEV_LIB)

@@ -152,14 +152,12 @@ def host_shared(w: Workload):
 
 
 # --------------------------------------------------------------------------- device side
-def device_inputs(w: Workload, device="cuda"):
-    """All inputs of the workload, resident in HBM (torch tensors)."""
+def device_weights(w: Workload, device="cuda"):
+    """Router, routed-expert and shared-expert weights of the workload, generated in HBM."""
     import torch
 
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     t = {}
-    t["x"] = synth.device_fill(torch.empty((w.T, w.H), dtype=dt, device=device), w.x_seed, S_X, 0, 1,
-                               w.T * w.H, w.sigma_x)
     if w.routing != "preassigned":
         t["w_router"] = synth.device_fill(torch.empty((w.E, w.H), dtype=dt, device=device), w.w_seed, S_ROUTER,
                                           0, 1, w.E * w.H, w.sigma_router)
@@ -176,6 +174,16 @@ def device_inputs(w: Workload, device="cuda"):
                                        w.I * w.H, w.sigma_gate_up)
         t["ws_down"] = synth.device_fill(torch.empty((w.H, w.I), dtype=dt, device=device), w.w_seed, S_SDOWN, 0,
                                          1, w.H * w.I, w.sigma_down)
+    return t
+
+
+def device_activations(w: Workload, device="cuda"):
+    """Token rows (and skew offsets / pre-assigned routing) of the workload, in HBM."""
+    import torch
+
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    t = {"x": synth.device_fill(torch.empty((w.T, w.H), dtype=dt, device=device), w.x_seed, S_X, 0, 1,
+                                w.T * w.H, w.sigma_x)}
     off = logit_offsets(w)
     if off is not None:
         t["logit_offset"] = torch.from_numpy(off).to(device)
@@ -183,4 +191,11 @@ def device_inputs(w: Workload, device="cuda"):
         ids, wts = preassigned(w)
         t["topk_ids"] = torch.from_numpy(ids).to(device)
         t["topk_weights"] = torch.from_numpy(wts).to(device)
+    return t
+
+
+def device_inputs(w: Workload, device="cuda"):
+    """All inputs of the workload, resident in HBM (torch tensors)."""
+    t = device_weights(w, device)
+    t.update(device_activations(w, device))
     return t

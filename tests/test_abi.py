@@ -1,0 +1,116 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol, sizes workspaces and
+rejects bad arguments before anything is launched (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_layer_forward_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|int32_t|size_t|const char\*)\s+(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.load_library()
+    names = _declared_functions()
+    assert set(names) == set(moe.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_config_struct_layout():
+    assert ctypes.sizeof(moe.MoeConfig) == 40
+    assert moe.MoeConfig.routed_scaling_factor.offset == 32
+
+
+def test_workspace_sizes():
+    cfg = moe.make_config()
+    fwd = moe.moe_workspace_size(cfg, moe.MOE_OP_FORWARD, 8192)
+    # h (73728 x 2048 bf16) + y_rows (73728 x 7168 bf16) dominate
+    assert fwd > 73728 * (2048 + 7168) * 2
+    assert moe.moe_workspace_size(cfg, moe.MOE_OP_FORWARD, 64) < fwd
+    assert moe.moe_workspace_size(cfg, moe.MOE_OP_COMBINE, 64) == 0
+    assert moe.moe_workspace_size(cfg, moe.MOE_OP_GROUPED_SWIGLU, 1000, 3) > 1000 * 2048 * 2
+    assert moe.moe_workspace_size(cfg, moe.MOE_OP_ROUTE, 64) > 0
+    assert moe.moe_workspace_size(cfg, moe.MOE_OP_PERMUTE, 64) > 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_group", 8, moe.MOE_ERR_UNSUPPORTED),
+    ("topk_group", 4, moe.MOE_ERR_UNSUPPORTED),
+    ("norm_topk_prob", 0, moe.MOE_ERR_UNSUPPORTED),
+    ("hidden_size", 7000, moe.MOE_ERR_UNSUPPORTED),
+    ("moe_intermediate_size", 2000, moe.MOE_ERR_UNSUPPORTED),
+    ("top_k", 400, moe.MOE_ERR_INVALID_ARG),
+    ("top_k", 0, moe.MOE_ERR_INVALID_ARG),
+    ("n_routed_experts", 600, moe.MOE_ERR_UNSUPPORTED),
+    ("n_shared_experts", 2, moe.MOE_ERR_UNSUPPORTED),
+    ("dtype", 7, moe.MOE_ERR_UNSUPPORTED),
+])
+def test_bad_config_is_rejected(field, value, status):
+    cfg = moe.make_config()
+    setattr(cfg, field, value)
+    lib = moe.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    rc = lib.moe_forward(ctypes.byref(cfg), 64, fake, fake, None, None, fake, fake, fake, fake, fake, fake, fake,
+                         None, None, fake, 1 << 40, None)
+    assert rc == status
+    assert moe.moe_last_error()
+    assert lib.moe_workspace_size(ctypes.byref(cfg), moe.MOE_OP_FORWARD, 64, 0) == 0
+
+
+def test_null_pointers_and_small_workspace_are_rejected():
+    cfg = moe.make_config()
+    lib = moe.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    rc = lib.moe_forward(ctypes.byref(cfg), 64, None, fake, None, None, fake, fake, fake, fake, fake, fake, fake,
+                         None, None, fake, 1 << 40, None)
+    assert rc == moe.MOE_ERR_INVALID_ARG
+    rc = lib.moe_forward(ctypes.byref(cfg), 64, fake, fake, None, None, fake, fake, fake, None, fake, fake, fake,
+                         None, None, fake, 1 << 40, None)
+    assert rc == moe.MOE_ERR_INVALID_ARG and "shared" in moe.moe_last_error()
+    rc = lib.moe_forward(ctypes.byref(cfg), 64, fake, fake, None, None, fake, fake, fake, fake, fake, fake, fake,
+                         None, None, fake, 1024, None)
+    assert rc == moe.MOE_ERR_WORKSPACE
+    rc = lib.moe_forward(ctypes.byref(cfg), 64, fake, fake, None, None, fake, fake, fake, fake, fake, fake, fake,
+                         None, None, None, 0, None)
+    assert rc == moe.MOE_ERR_WORKSPACE
+    rc = lib.moe_forward(ctypes.byref(cfg), -1, fake, fake, None, None, fake, fake, fake, fake, fake, fake, fake,
+                         None, None, fake, 1 << 40, None)
+    assert rc == moe.MOE_ERR_INVALID_ARG
+    rc = lib.moe_route(ctypes.byref(cfg), 64, fake, None, None, None, fake, fake, fake, 1 << 40, None)
+    assert rc == moe.MOE_ERR_INVALID_ARG
+    rc = lib.moe_permute(ctypes.byref(cfg), 64, fake, fake, fake, fake, fake, None, fake, 1 << 40, None)
+    assert rc == moe.MOE_ERR_INVALID_ARG
+    rc = lib.moe_grouped_swiglu(ctypes.byref(cfg), 0, fake, 10, fake, None, fake, fake, fake, None, fake,
+                                moe.MOE_BF16, fake, 1 << 40, None)
+    assert rc == moe.MOE_ERR_INVALID_ARG
+    rc = lib.moe_combine(ctypes.byref(cfg), 64, fake, 9, fake, fake, None, fake, None)
+    assert rc == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_zero_tokens_is_a_no_op():
+    cfg = moe.make_config()
+    lib = moe.load_library()
+    rc = lib.moe_forward(ctypes.byref(cfg), 0, None, None, None, None, None, None, None, None, None, None, None,
+                         None, None, None, 0, None)
+    assert rc == moe.MOE_OK
+    assert lib.moe_route(ctypes.byref(cfg), 0, None, None, None, None, None, None, None, 0, None) == moe.MOE_OK
+    assert lib.moe_combine(ctypes.byref(cfg), 0, None, 1, None, None, None, None, None) == moe.MOE_OK
+
+
+def test_python_binding_refuses_host_tensors():
+    import torch
+
+    cfg = moe.make_config(hidden_size=256, moe_intermediate_size=128, n_routed_experts=4, top_k=2)
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        moe.moe_route(cfg, x, torch.zeros((4, 256), dtype=torch.bfloat16))
