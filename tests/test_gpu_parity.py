@@ -219,7 +219,8 @@ def test_grouped_swiglu_and_combine_calls(y_bf16):
     pair_row = np.stack([r.choice(rows, size=K, replace=False) for _ in range(T)]).astype(np.int32)
     wts = r.uniform(0.1, 1.0, size=(T, K)).astype(np.float32)
     y_sh = y_rows[:T].contiguous()
-    y = moe.moe_combine(cfg, y_rows, torch.from_numpy(pair_row).cuda(), torch.from_numpy(wts).cuda(), y_sh)
+    ccfg = moe.make_config(hidden_size=w.H, moe_intermediate_size=w.I, n_routed_experts=w.E, top_k=K)
+    y = moe.moe_combine(ccfg, y_rows, torch.from_numpy(pair_row).cuda(), torch.from_numpy(wts).cuda(), y_sh)
     torch.cuda.synchronize()
     y_ref = oracle.combine(to_np(y_rows), pair_row, wts, to_np(y_sh))
     assert rel_l2(to_np(y), y_ref).max() <= Y_TOL["bf16"]
