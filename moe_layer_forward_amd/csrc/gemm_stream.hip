@@ -7,10 +7,13 @@
 // along as the A operand from L2.
 //
 // A wave owns 16 output columns of one group: 16 gate rows + the 16 matching up rows (gate/up) or 16
-// rows of W_down (down).  Per 128-wide K step a lane loads 64 contiguous bytes of its weight row
-// (lanes 16q..16q+15 take K quarter q), i.e. four 16x16x32 MFMA operands.  Because the K sum is
-// order-free, the same K permutation is used for the token rows, so no shuffle is needed.  The next
-// step's loads are issued before the current step's MFMAs (register double buffer).
+// rows of W_down (down).  A 128-wide K step of a weight row is 256 bytes; load j (j = 0..3) of lane l
+// takes bytes 64*j + 16*(l/16) .. +16 of row l%16, so each load covers 64 contiguous bytes of each of
+// 16 rows, and load j is the B operand of the j-th 16x16x32 MFMA.  Because the K sum is order-free,
+// the token rows (A operand) are read with the same K permutation, so no shuffle is needed.  The next
+// step's loads are issued before the current step's MFMAs (register double buffer).  Plain loads:
+// measured on MI355X, this row-strided shape streams at ~6.2 TB/s with ordinary loads and far
+// slower with non-temporal ones.
 // Work-groups = 4 waves = 64 columns of one group; groups come from the plan's active list, largest
 // first, so the long-running many-row groups start early.
 #include "kernels.h"
@@ -38,17 +41,10 @@ struct Frag {
   u32x4 v[4];
 };
 
+// Four 16-byte loads at p, p + 32, p + 64, p + 96 elements (64-byte stride): one K step of one row.
 __device__ __forceinline__ void load_frag(Frag& f, const uint16_t* p) {
-  const u32x4* q = reinterpret_cast<const u32x4*>(p);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.v[j] = q[j];
-}
-
-// Weights are read once: non-temporal loads keep them from displacing the token rows in L2.
-__device__ __forceinline__ void load_frag_stream(Frag& f, const uint16_t* p) {
-  const u32x4* q = reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) f.v[j] = __builtin_nontemporal_load(q + j);
+  for (int j = 0; j < 4; ++j) f.v[j] = *reinterpret_cast<const u32x4*>(p + 32 * j);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
@@ -65,7 +61,7 @@ __global__ __launch_bounds__(256) void stream_kernel(StreamArgs p) {
   const int K = SWIGLU ? H : I;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = nb * 64 + wave * 16;       // first output column of this wave
-  const int kq = (lane >> 4) * 32;          // this lane's K quarter inside a 128-wide step
+  const int kq = (lane >> 4) * 8;           // this lane's 16-byte slot inside each 64-byte quarter
   const bool sh = g == p.w.shared_group;
 
   const uint16_t* w0;
@@ -96,8 +92,8 @@ __global__ __launch_bounds__(256) void stream_kernel(StreamArgs p) {
       load_frag(a[buf], arow + off);
 #pragma unroll
       for (int j = 0; j < 4; ++j) a[buf].v[j] &= keep;
-      load_frag_stream(b0[buf], w0 + off);
-      if (SWIGLU) load_frag_stream(b1[buf], w1 + off);
+      load_frag(b0[buf], w0 + off);
+      if (SWIGLU) load_frag(b1[buf], w1 + off);
     };
     auto mma = [&](int buf) {
 #pragma unroll

@@ -5,13 +5,15 @@
 // "Kimi K2.5 架构 QA" Q8.3 names in place of the per-expert loop.
 //
 // Work item = (row tile of one group, column tile).  The row tiles come from the device-side plan
-// (largest groups first); a work-group stages 128 rows of its group -- gathered straight from the
-// token rows through row_index, so no permuted copy of x is ever written -- and a 128-row slice of
-// the weights through LDS, and runs the MFMA main loop of tile_core.h.
-//   gate/up: the 128 weight rows are 64 gate rows and the 64 matching up rows, interleaved in
-//            16-row blocks so each wave ends with gate and up accumulators of the same h columns in
-//            the same lanes; the epilogue writes h = SiLU(g) * u as bf16.
-//   down:    128 rows of W_down; the epilogue writes y_rows (fp32 or bf16), times row_scale if given.
+// (largest groups first, 256 rows each, so a K2 expert's ~170 prefill rows are one tile and every
+// weight byte is read once); a work-group stages the tile's rows -- gathered straight from the token
+// rows through row_index, so no permuted copy of x is ever written -- and a 256-row slice of the
+// weights through LDS, and runs the MFMA main loop of tile_core.h, which skips the 32-row
+// sub-tiles past the group's end.
+//   gate/up: the 256 weight rows are 128 gate rows and the 128 matching up rows, interleaved in
+//            32-row blocks, so column sub-tiles 2p and 2p+1 of a wave are the gate and up columns of
+//            the same 32 h columns, in the same lanes; the epilogue writes h = SiLU(g) * u as bf16.
+//   down:    256 rows of W_down; the epilogue writes y_rows (fp32 or bf16), times row_scale if given.
 // Work items are dealt XCD-major (tile_core.h) so the column tiles of one row tile run on the same
 // XCD at the same time and share its rows of A in that XCD's L2 while each weight byte is read once.
 #include "tile_core.h"
@@ -19,7 +21,8 @@
 namespace moe {
 namespace {
 
-using S = TileShape<kTileM, 128, 64>;
+using S = TileShape<kTileM, 256, 64, 2>;
+static_assert(S::kRowsPerLoad * S::kBLoads == 32, "wave w loads B rows [32w, 32w+32): one gate or up block");
 
 struct TileArgs {
   const int32_t* group_offsets;
@@ -35,116 +38,134 @@ struct TileArgs {
   int H, I, n_ntiles;
 };
 
-__device__ __forceinline__ void group_rows(const int32_t* off, int64_t max_rows, int g, int64_t& r0, int64_t& r1) {
-  r0 = off[g];
-  r1 = off[g + 1];
-  if (r0 > max_rows) r0 = max_rows;
-  if (r1 > max_rows) r1 = max_rows;
+struct TileRows {
+  int g;
+  int64_t rbeg, rend;
+};
+
+__device__ __forceinline__ bool tile_of(const TileArgs& p, int& nt, TileRows& t) {
+  int64_t L;
+  if (!xcd_work_item((int64_t)p.counters[1] * p.n_ntiles, L)) return false;
+  const int tile = (int)(L / p.n_ntiles);
+  nt = (int)(L % p.n_ntiles);
+  t.g = p.tiles[2 * tile];
+  const int m0 = p.tiles[2 * tile + 1];
+  int64_t r0 = p.group_offsets[t.g], r1 = p.group_offsets[t.g + 1];
+  if (r0 > p.max_rows) r0 = p.max_rows;
+  if (r1 > p.max_rows) r1 = p.max_rows;
   if (r1 < r0) r1 = r0;
+  t.rbeg = r0 + m0;
+  t.rend = t.rbeg + S::BM < r1 ? t.rbeg + S::BM : r1;
+  return t.rbeg < t.rend;
 }
 
-__global__ __launch_bounds__(256) void gateup_tile_kernel(TileArgs p) {
-  __shared__ __align__(16) uint16_t smem[S::kSmemBytes / 2];
-  int64_t L;
-  if (!xcd_work_item((int64_t)p.counters[1] * p.n_ntiles, L)) return;
-  const int tile = (int)(L / p.n_ntiles), nt = (int)(L % p.n_ntiles);
-  const int g = p.tiles[2 * tile], m0 = p.tiles[2 * tile + 1];
-  int64_t r0, r1;
-  group_rows(p.group_offsets, p.max_rows, g, r0, r1);
-  const int64_t rbeg = r0 + m0;
-  const int64_t rend = rbeg + S::BM < r1 ? rbeg + S::BM : r1;
+__global__ __launch_bounds__(512) void gateup_tile_kernel(TileArgs p) {
+  __shared__ __align__(16) char smem[S::kSmemBytes];
+  int nt;
+  TileRows t;
+  if (!tile_of(p, nt, t)) return;
   const int H = p.H, I = p.I;
-  const bool sh = g == p.w.shared_group;
-  const uint16_t* wg = sh ? (const uint16_t*)p.w.s_gate : (const uint16_t*)p.w.gate + (int64_t)g * I * H;
-  const uint16_t* wu = sh ? (const uint16_t*)p.w.s_up : (const uint16_t*)p.w.up + (int64_t)g * I * H;
-  const int n0 = nt * 64;  // first h column of this tile
+  const bool sh = t.g == p.w.shared_group;
+  const uint16_t* wg = sh ? (const uint16_t*)p.w.s_gate : (const uint16_t*)p.w.gate + (int64_t)t.g * I * H;
+  const uint16_t* wu = sh ? (const uint16_t*)p.w.s_up : (const uint16_t*)p.w.up + (int64_t)t.g * I * H;
+  const int n0 = nt * (S::BN / 2);  // first h column of this tile (128 per tile)
 
-  const int tid = threadIdx.x;
-  const uint16_t* aptr[S::kALoads];
-  const uint16_t* bptr[S::kBLoads];
-  uint32_t amask = 0;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  Operands<S> o;
+  o.a_base = reinterpret_cast<const char*>(p.a);
+  // B rows (virtual columns) are 32-row blocks alternating gate / up; wave w loads block w, so its
+  // rows are gate rows when w is even and up rows when w is odd.  With the 2x4 wave grid every
+  // wave's two 32-column sub-tiles are then a gate block and the matching up block.  Virtual column
+  // vc holds h column n0 + 32*(vc/64) + vc%32.
+  const bool up_rows = __builtin_amdgcn_readfirstlane(w & 1) != 0;
+  o.b_base = reinterpret_cast<const char*>((up_rows ? wu : wg) + (int64_t)n0 * H);
 #pragma unroll
   for (int j = 0; j < S::kALoads; ++j) {
-    const int64_t r = rbeg + S::stage_row(tid, j);
-    const bool ok = r < rend;
-    const int64_t src = ok ? (p.row_index ? (int64_t)p.row_index[r] : r) : 0;
-    amask |= (ok ? 1u : 0u) << j;
-    aptr[j] = p.a + src * H + S::stage_col(tid, j);
+    const int rl = S::load_row(w, j, lane, S::kALoads);
+    const int64_t r = t.rbeg + rl;
+    const int64_t rr = r < t.rend ? r : t.rbeg;  // rows past the group end re-read its first row
+    const int64_t src = p.row_index ? (int64_t)p.row_index[rr] : rr;
+    o.a_off[j] = (uint32_t)((src * H + 8 * S::load_chunk(rl, lane)) * 2);
   }
 #pragma unroll
   for (int j = 0; j < S::kBLoads; ++j) {
-    const int vc = S::stage_row(tid, j);  // virtual column: 16 gate rows, 16 up rows, ...
-    const int n = n0 + (vc >> 5) * 16 + (vc & 15);
-    bptr[j] = ((vc >> 4) & 1 ? wu : wg) + (int64_t)n * H + S::stage_col(tid, j);
+    const int vc = S::load_row(w, j, lane, S::kBLoads);
+    const int n = (vc >> 6) * 32 + (vc & 31);
+    o.b_off[j] = (uint32_t)(((int64_t)n * H + 8 * S::load_chunk(vc, lane)) * 2);
   }
-  f32x4 acc[S::kMI][S::kNI];
-  tile_mainloop<S>(aptr, bptr, amask, 0xffffffffu, H, smem, acc);
+  f32x16 acc[S::kMSub][S::kNSub];
+  const int m_valid = (int)(t.rend - t.rbeg);
+  tile_mainloop<S>(o, m_valid, H, smem, acc);
 
-  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int wave = w, wm = wave >> 2, wn = wave & 3;
   uint16_t* h = static_cast<uint16_t*>(p.out);
+  const int nsv = (m_valid + 31) / 32;
 #pragma unroll
-  for (int mi = 0; mi < S::kMI; ++mi)
+  for (int i = 0; i < S::kMSub; ++i) {
+    if (2 * i + wm >= nsv) continue;
 #pragma unroll
-    for (int pr = 0; pr < S::kNI / 2; ++pr) {
-      const int col = n0 + (2 * wn + pr) * 16 + (lane & 15);
+    for (int pr = 0; pr < S::kNSub / 2; ++pr) {
+      const int col = n0 + wn * (S::kWaveN / 2) + pr * 32 + (lane & 31);  // kWaveN/2 = 32 h columns
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t r = rbeg + wm * S::kWaveM + mi * 16 + 4 * (lane >> 4) + i;
-        if (r < rend) h[r * I + col] = f32_to_bf16(swiglu_f32(acc[mi][2 * pr][i], acc[mi][2 * pr + 1][i]));
+      for (int q = 0; q < 16; ++q) {
+        const int64_t r = t.rbeg + S::sub_row(wm, i) + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        if (r < t.rend) h[r * I + col] = f32_to_bf16(swiglu_f32(acc[i][2 * pr][q], acc[i][2 * pr + 1][q]));
       }
     }
+  }
 }
 
-__global__ __launch_bounds__(256) void down_tile_kernel(TileArgs p) {
-  __shared__ __align__(16) uint16_t smem[S::kSmemBytes / 2];
-  int64_t L;
-  if (!xcd_work_item((int64_t)p.counters[1] * p.n_ntiles, L)) return;
-  const int tile = (int)(L / p.n_ntiles), nt = (int)(L % p.n_ntiles);
-  const int g = p.tiles[2 * tile], m0 = p.tiles[2 * tile + 1];
-  int64_t r0, r1;
-  group_rows(p.group_offsets, p.max_rows, g, r0, r1);
-  const int64_t rbeg = r0 + m0;
-  const int64_t rend = rbeg + S::BM < r1 ? rbeg + S::BM : r1;
+__global__ __launch_bounds__(512) void down_tile_kernel(TileArgs p) {
+  __shared__ __align__(16) char smem[S::kSmemBytes];
+  int nt;
+  TileRows t;
+  if (!tile_of(p, nt, t)) return;
   const int H = p.H, I = p.I;
-  const uint16_t* wd = g == p.w.shared_group ? (const uint16_t*)p.w.s_down
-                                              : (const uint16_t*)p.w.down + (int64_t)g * H * I;
+  const uint16_t* wd = t.g == p.w.shared_group ? (const uint16_t*)p.w.s_down
+                                                : (const uint16_t*)p.w.down + (int64_t)t.g * H * I;
   const int n0 = nt * S::BN;
 
-  const int tid = threadIdx.x;
-  const uint16_t* aptr[S::kALoads];
-  const uint16_t* bptr[S::kBLoads];
-  uint32_t amask = 0;
+  const int tid = threadIdx.x, w = tid >> 6;
+  Operands<S> o;
+  o.a_base = reinterpret_cast<const char*>(p.a);
+  o.b_base = reinterpret_cast<const char*>(wd);
 #pragma unroll
   for (int j = 0; j < S::kALoads; ++j) {
-    const int64_t r = rbeg + S::stage_row(tid, j);
-    const bool ok = r < rend;
-    amask |= (ok ? 1u : 0u) << j;
-    aptr[j] = p.a + (ok ? r : rbeg) * I + S::stage_col(tid, j);
+    const int rl = S::load_row(w, j, tid & 63, S::kALoads);
+    const int64_t r = t.rbeg + rl;
+    o.a_off[j] = (uint32_t)(((r < t.rend ? r : t.rbeg) * I + 8 * S::load_chunk(rl, tid & 63)) * 2);
   }
 #pragma unroll
-  for (int j = 0; j < S::kBLoads; ++j)
-    bptr[j] = wd + (int64_t)(n0 + S::stage_row(tid, j)) * I + S::stage_col(tid, j);
-  f32x4 acc[S::kMI][S::kNI];
-  tile_mainloop<S>(aptr, bptr, amask, 0xffffffffu, I, smem, acc);
+  for (int j = 0; j < S::kBLoads; ++j) {
+    const int vc = S::load_row(w, j, tid & 63, S::kBLoads);
+    const int n = n0 + vc;  // columns past H (last tile) read row 0, never stored
+    o.b_off[j] = (uint32_t)(((int64_t)(n < H ? n : 0) * I + 8 * S::load_chunk(vc, tid & 63)) * 2);
+  }
+  f32x16 acc[S::kMSub][S::kNSub];
+  const int m_valid = (int)(t.rend - t.rbeg);
+  tile_mainloop<S>(o, m_valid, I, smem, acc);
 
-  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int lane = tid & 63, wave = w, wm = wave >> 2, wn = wave & 3;
 #pragma unroll
-  for (int mi = 0; mi < S::kMI; ++mi)
+  for (int i = 0; i < S::kMSub; ++i) {
+    if (2 * i + wm >= (m_valid + 31) / 32) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t r = rbeg + wm * S::kWaveM + mi * 16 + 4 * (lane >> 4) + i;
-      if (r >= rend) continue;
+    for (int q = 0; q < 16; ++q) {
+      const int64_t r = t.rbeg + S::sub_row(wm, i) + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+      if (r >= t.rend) continue;
       const float sc = p.row_scale ? p.row_scale[r] : 1.f;
 #pragma unroll
-      for (int ni = 0; ni < S::kNI; ++ni) {
-        const int col = n0 + wn * S::kWaveN + ni * 16 + (lane & 15);
-        const float v = acc[mi][ni][i] * sc;
+      for (int u = 0; u < S::kNSub; ++u) {
+        const int col = n0 + wn * S::kWaveN + 32 * u + (lane & 31);
+        if (col >= H) continue;
+        const float v = acc[i][u][q] * sc;
         if (p.out_bf16)
           static_cast<uint16_t*>(p.out)[r * H + col] = f32_to_bf16(v);
         else
           static_cast<float*>(p.out)[r * H + col] = v;
       }
     }
+  }
 }
 
 unsigned grid_for(int64_t max_tiles, int n_ntiles) {
@@ -157,7 +178,8 @@ unsigned grid_for(int64_t max_tiles, int n_ntiles) {
 
 hipError_t launch_gateup_tile_bf16(const Groups& g, const Weights& w, const uint16_t* x, uint16_t* h, int H, int I,
                                    hipStream_t s) {
-  TileArgs p{g.group_offsets, g.row_index, g.tiles, g.counters, g.max_rows, w, x, h, 1, nullptr, H, I, I / 64};
+  TileArgs p{g.group_offsets, g.row_index, g.tiles, g.counters, g.max_rows, w, x, h, 1, nullptr, H, I,
+             I / (S::BN / 2)};
   gateup_tile_kernel<<<grid_for(g.max_tiles, p.n_ntiles), S::kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
@@ -165,7 +187,7 @@ hipError_t launch_gateup_tile_bf16(const Groups& g, const Weights& w, const uint
 hipError_t launch_down_tile_bf16(const Groups& g, const Weights& w, const uint16_t* h, void* y_rows, bool y_bf16,
                                  const float* row_scale, int H, int I, hipStream_t s) {
   TileArgs p{g.group_offsets, nullptr, g.tiles, g.counters, g.max_rows, w, h, y_rows, y_bf16 ? 1 : 0, row_scale,
-             H, I, H / S::BN};
+             H, I, (H + S::BN - 1) / S::BN};
   down_tile_kernel<<<grid_for(g.max_tiles, p.n_ntiles), S::kThreads, 0, s>>>(p);
   return hipGetLastError();
 }

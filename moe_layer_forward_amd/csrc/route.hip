@@ -14,14 +14,15 @@
 namespace moe {
 namespace {
 
-using RS = TileShape<128, 128, 64>;
+using RS = TileShape<128, 128, 64, 2>;
 
 // Number of K splits for the router GEMM: enough work-groups to cover the chip, partial sums no
 // larger than the router weight itself, and each split a whole number of 64-wide K steps.
 int router_splits(int64_t T, int H, int E) {
   const int64_t tiles = ((T + RS::BM - 1) / RS::BM) * ((E + RS::BN - 1) / RS::BN);
   const int ksteps = H / RS::BK;
-  const int64_t cap = H / (2 * T) > 1 ? H / (2 * T) : 1;  // partials [S,T,E] fp32 <= router weight bytes
+  // partials [S, T, E] fp32: no more than the router weight or two copies of the logits
+  const int64_t cap = H / (2 * T) > 2 ? H / (2 * T) : 2;
   int best = 1;
   for (int s = 1; s <= ksteps; ++s) {
     if (ksteps % s) continue;
@@ -32,44 +33,45 @@ int router_splits(int64_t T, int H, int E) {
   return best;
 }
 
-__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
-                                                            const uint16_t* __restrict__ w, float* __restrict__ part,
+__global__ __launch_bounds__(512) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ wr, float* __restrict__ part,
                                                             int64_t T, int H, int E, int ksplit) {
-  __shared__ __align__(16) uint16_t smem[RS::kSmemBytes / 2];
+  __shared__ __align__(16) char smem[RS::kSmemBytes];
   const int tid = threadIdx.x;
   const int64_t m0 = (int64_t)blockIdx.x * RS::BM;
   const int n0 = blockIdx.y * RS::BN;
   const int split = blockIdx.z;
   const int k0 = split * ksplit;
-  const uint16_t* aptr[RS::kALoads];
-  const uint16_t* bptr[RS::kBLoads];
-  uint32_t amask = 0, bmask = 0;
+  Operands<RS> o;
+  const int w = tid >> 6, lane = tid & 63;
+  o.a_base = reinterpret_cast<const char*>(x + k0);
+  o.b_base = reinterpret_cast<const char*>(wr + k0);
 #pragma unroll
   for (int j = 0; j < RS::kALoads; ++j) {
-    const int64_t t = m0 + RS::stage_row(tid, j);
-    amask |= (t < T ? 1u : 0u) << j;
-    aptr[j] = x + (t < T ? t : 0) * H + k0 + RS::stage_col(tid, j);
+    const int rl = RS::load_row(w, j, lane, RS::kALoads);
+    const int64_t t = m0 + rl;
+    o.a_off[j] = (uint32_t)(((t < T ? t : 0) * H + 8 * RS::load_chunk(rl, lane)) * 2);
   }
 #pragma unroll
   for (int j = 0; j < RS::kBLoads; ++j) {
-    const int e = n0 + RS::stage_row(tid, j);
-    bmask |= (e < E ? 1u : 0u) << j;
-    bptr[j] = w + (int64_t)(e < E ? e : 0) * H + k0 + RS::stage_col(tid, j);
+    const int rl = RS::load_row(w, j, lane, RS::kBLoads);
+    const int e = n0 + rl;  // experts past E read row 0, never stored
+    o.b_off[j] = (uint32_t)(((int64_t)(e < E ? e : 0) * H + 8 * RS::load_chunk(rl, lane)) * 2);
   }
-  f32x4 acc[RS::kMI][RS::kNI];
-  tile_mainloop<RS>(aptr, bptr, amask, bmask, ksplit, smem, acc);
+  f32x16 acc[RS::kMSub][RS::kNSub];
+  tile_mainloop<RS>(o, T - m0 < RS::BM ? (int)(T - m0) : RS::BM, ksplit, smem, acc);
 
-  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int wm = w >> 2, wn = w & 3;
   float* out = part + (int64_t)split * T * E;
 #pragma unroll
-  for (int mi = 0; mi < RS::kMI; ++mi)
+  for (int i = 0; i < RS::kMSub; ++i)
 #pragma unroll
-    for (int ni = 0; ni < RS::kNI; ++ni) {
-      const int e = n0 + wn * RS::kWaveN + ni * 16 + (lane & 15);
+    for (int u = 0; u < RS::kNSub; ++u) {
+      const int e = n0 + wn * RS::kWaveN + 32 * u + (lane & 31);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t t = m0 + wm * RS::kWaveM + mi * 16 + 4 * (lane >> 4) + i;
-        if (t < T && e < E) out[t * E + e] = acc[mi][ni][i];
+      for (int q = 0; q < 16; ++q) {
+        const int64_t t = m0 + RS::sub_row(wm, i) + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        if (t < T && e < E) out[t * E + e] = acc[i][u][q];
       }
     }
 }
@@ -123,6 +125,32 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave leaves together
 
+  // logits: the K-split partial sums added in split order (4 splits' loads in flight per round)
+  float lg[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) lg[j] = 0.f;
+  const float* pt = part + t * E;
+  const int64_t sstride = T * E;
+  int sp = 0;
+  for (; sp + 4 <= nsplit; sp += 4) {
+    float v[4][J];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int e = lane + 64 * j;
+        v[u][j] = e < E ? pt[(sp + u) * sstride + e] : 0.f;
+      }
+#pragma unroll
+    for (int j = 0; j < J; ++j) lg[j] = (((lg[j] + v[0][j]) + v[1][j]) + v[2][j]) + v[3][j];
+  }
+  for (; sp < nsplit; ++sp)
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E) lg[j] += pt[sp * sstride + e];
+    }
+
   uint64_t key[J];
   float sc[J];
 #pragma unroll
@@ -131,8 +159,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
     key[j] = 0;
     sc[j] = 0.f;
     if (e < E) {
-      float l = 0.f;
-      for (int sp = 0; sp < nsplit; ++sp) l += part[((int64_t)sp * T + t) * E + e];
+      float l = lg[j];
       if (logit_offset) l += logit_offset[e];
       const float score = sigmoid_f32(l);
       const float kv = score_bias ? score + score_bias[e] : score;
