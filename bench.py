@@ -8,11 +8,24 @@ prefill workload (T=8192) is measured in the same run and reported beside it.  P
 come from HIP events recorded around every kernel launch inside the timed steps.
 
     python bench.py [--steps K] [--warmup W] [--workload decode|prefill|skew|ep_share|tiny]
+
+Profiling helpers (rocprofv3 runs the bench; this file turns its CSV output into the summaries kept
+under profiles/):
+
+    rocprofv3 --kernel-trace --stats -d DIR -o run --output-format csv -- python bench.py ...
+    python bench.py --profile-summary DIR            # markdown table of the kernel statistics
+    rocprofv3 --pmc FETCH_SIZE -d FDIR -o run --output-format csv -- python bench.py --pmc-calibrate ...
+    rocprofv3 --pmc WRITE_SIZE -d WDIR -o run --output-format csv -- python bench.py --pmc-calibrate ...
+    python bench.py --traffic-summary WORKLOAD FDIR WDIR   # HBM bytes per dispatch, copy-calibrated
 """
 import argparse
+import csv
 import ctypes
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -23,6 +36,43 @@ METRIC = "K2 MoE layer tokens/s at T=64 decode & T=8192 prefill; % HBM / % MFMA 
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 BF16_PEAK = 2.5e15         # dense bf16 MFMA FLOP/s
 F32_PEAK = 157.3e12        # fp32 vector FLOP/s
+
+# Library kernel names (as the library reports them) -> a substring of the kernel symbol rocprofv3
+# prints, and the source files that make the kernel (its measured traffic is only reported while
+# their digest is unchanged).
+KERNEL_SYMBOLS = {
+    "gateup_stream": ("stream_kernel<true>", ["gemm_stream.hip", "kernels.h"]),
+    "down_stream": ("stream_kernel<false>", ["gemm_stream.hip", "kernels.h"]),
+    "gateup_tile": ("gateup_tile_kernel", ["gemm_tile.hip", "tile_core.h", "kernels.h"]),
+    "down_tile": ("down_tile_kernel", ["gemm_tile.hip", "tile_core.h", "kernels.h"]),
+    "router_logits": ("router_logits_kernel", ["route.hip", "tile_core.h", "kernels.h"]),
+    "combine": ("combine_kernel", ["combine.hip", "kernels.h"]),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+CALIB_BYTES = 1 << 30      # the calibration copy reads and writes this many bytes
+CALIB_SYMBOL = "neg_kernel"
+
+
+def sources_digest(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SYMBOLS[kernel][1]:
+        with open(os.path.join(ROOT, "moe_layer_forward_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, kernel):
+    """Counter-measured HBM bytes per launch of `kernel` on `workload`, from the committed PMC
+    summary, or None when there is none or the kernel's sources changed since it was taken."""
+    if kernel not in KERNEL_SYMBOLS or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as fh:
+        text = fh.read()
+    for block in re.findall(r"```json\n(.*?)\n```", text, re.S):
+        for rec in json.loads(block):
+            if rec["workload"] == workload and rec["kernel"] == kernel:
+                return rec["traffic_bytes"] if rec["sources"] == sources_digest(kernel) else None
+    return None
 
 
 def log(msg):
@@ -160,11 +210,11 @@ def run(w, weights, steps, warmup):
     peak_flops = BF16_PEAK if w.dtype == "bf16" else F32_PEAK
     if kb is not None and kf / kb < peak_flops / HBM_PEAK:
         roof = {"bound": "hbm", "achieved": kb / dom_s / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                "frac": kb / dom_s / HBM_PEAK, "traffic": None, "kernel": dom,
+                "frac": kb / dom_s / HBM_PEAK, "traffic": load_traffic(w.name, dom), "kernel": dom,
                 "bytes_per_launch": kb, "flops_per_launch": kf, "avg_launch_us": kern[dom] * 1e3}
     elif kb is not None:
         roof = {"bound": "mfma", "achieved": kf / dom_s / 1e12, "peak": peak_flops / 1e12, "unit": "TFLOP/s",
-                "frac": kf / dom_s / peak_flops, "traffic": None, "kernel": dom,
+                "frac": kf / dom_s / peak_flops, "traffic": load_traffic(w.name, dom), "kernel": dom,
                 "bytes_per_launch": kb, "flops_per_launch": kf, "avg_launch_us": kern[dom] * 1e3}
     else:
         roof = None
@@ -209,13 +259,81 @@ def cpu_baseline(w, n_tokens):
                       f"each, float64 numpy; {el:.2f} s of oracle arithmetic, weight regeneration not timed"}
 
 
+def _csv_rows(d, suffix):
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return rows
+
+
+def profile_summary(d):
+    """Markdown table of a rocprofv3 --kernel-trace --stats run (its *kernel_stats.csv)."""
+    rows = _csv_rows(d, "kernel_stats.csv")
+    print("| kernel | calls | average µs | min µs | max µs | total ms | % of GPU time |")
+    print("|---|---|---|---|---|---|---|")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"].split("(")[0] if "(" in r["Name"] else r["Name"]
+        print(f"| `{name[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+              f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |")
+
+
+def _counter_means(d, counter):
+    """Mean counter value per dispatch, keyed by kernel symbol."""
+    acc = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def traffic_summary(workload, fdir, wdir):
+    """HBM bytes per dispatch of the library's kernels from a FETCH_SIZE run and a WRITE_SIZE run,
+    each scaled by what the same counter reads for a copy of CALIB_BYTES (read and written)."""
+    fetch, write = _counter_means(fdir, "FETCH_SIZE"), _counter_means(wdir, "WRITE_SIZE")
+
+    def pick(means, sym):
+        hits = [v for k, v in means.items() if sym in k]
+        return sum(hits) / len(hits) if hits else None
+
+    cf, cw = pick(fetch, CALIB_SYMBOL), pick(write, CALIB_SYMBOL)
+    if not cf or not cw:
+        raise SystemExit("the calibration copy is missing (run the bench with --pmc-calibrate)")
+    kf, kw = CALIB_BYTES / (cf * 1024), CALIB_BYTES / (cw * 1024)
+    print(f"Calibration: a copy of {CALIB_BYTES} bytes (torch.neg, bf16) reads FETCH_SIZE = {cf:.0f} KiB and "
+          f"WRITE_SIZE = {cw:.0f} KiB per dispatch, so the counters are scaled by {kf:.4f} (fetch) and "
+          f"{kw:.4f} (write).\n")
+    print("| kernel | FETCH_SIZE KiB / dispatch | WRITE_SIZE KiB / dispatch | HBM bytes / launch (scaled) |")
+    print("|---|---|---|---|")
+    recs = []
+    for name, (sym, _) in KERNEL_SYMBOLS.items():
+        f, w_ = pick(fetch, sym), pick(write, sym)
+        if f is None or w_ is None:
+            continue
+        fb, wb = f * 1024 * kf, w_ * 1024 * kw
+        print(f"| {name} | {f:.0f} | {w_:.0f} | {fb + wb:.4g} |")
+        recs.append({"workload": workload, "kernel": name, "sources": sources_digest(name), "fetch_kib": f,
+                     "write_kib": w_, "fetch_bytes": fb, "write_bytes": wb, "traffic_bytes": fb + wb})
+    print("\n```json\n" + json.dumps(recs, indent=1) + "\n```")
+
+
 def main():
+    if len(sys.argv) >= 2 and sys.argv[1] == "--profile-summary":
+        return profile_summary(sys.argv[2])
+    if len(sys.argv) >= 2 and sys.argv[1] == "--traffic-summary":
+        return traffic_summary(*sys.argv[2:5])
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skew", "ep_share", "tiny"])
-    ap.add_argument("--also", default="prefill", help="second workload measured in the same run ('none' to skip)")
+    ap.add_argument("--also", default="prefill,skew,ep_share",
+                    help="comma-separated workloads measured in the same run and reported beside it ('none')")
+    ap.add_argument("--pmc-calibrate", action="store_true",
+                    help="first run one copy of known size (the traffic summary's counter calibration)")
     ap.add_argument("--cpu-tokens", type=int, default=6, help="tokens in the oracle's CPU-baseline sample (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -231,6 +349,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     main_w = wl.WORKLOADS[args.workload]
+    if args.pmc_calibrate:
+        a = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+        b = torch.empty_like(a)
+        torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        del a, b
     weights_cache = {}
 
     def weights_for(w):
@@ -253,8 +377,8 @@ def main():
                    "parallelism": "1 GPU"},
         "roofline": res["roofline"], "layer": res["layer"], "kernels_us": res["kernels_us"],
     }
-    if args.also != "none" and args.also != args.workload:
-        w2 = wl.WORKLOADS[args.also]
+    for name in [n for n in args.also.split(",") if n and n not in ("none", args.workload)]:
+        w2 = wl.WORKLOADS[name]
         log(f"running {w2.name} ...")
         r2 = run(w2, weights_for(w2), args.steps, args.warmup)
         out[w2.name] = {"value": r2["tokens_per_s"], "unit": "tokens/s", "ms_per_step": r2["ms_per_step"],

@@ -41,7 +41,10 @@
  *     be ordered on one stream.
  *   - Supported shapes: hidden_size and moe_intermediate_size multiples of 128;
  *     1 <= top_k <= min(64, n_routed_experts); n_routed_experts <= 512; n_group == topk_group == 1;
- *     n_shared_experts 0 or 1; norm_topk_prob == 1.
+ *     n_shared_experts 0 or 1; norm_topk_prob == 1.  For MOE_BF16 every operand matrix the
+ *     MFMA kernels read (x, the intermediate h of T*(top_k+n_shared) rows x I, one expert's
+ *     weight, the router weight) must span less than 4 GiB (at H = 7168: T <= 299,593 for x and
+ *     T*(K+1) <= 524,287 rows for h); larger calls return MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_H
 #define MOE_H

@@ -116,6 +116,27 @@ int check_tokens(int64_t T, const moe_config* c) {
 
 size_t elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 
+// The bf16 MFMA kernels address each operand matrix as a uniform base plus a 32-bit per-lane byte
+// offset, so every matrix they read must span less than 4 GiB.
+int check_span(const char* what, int64_t bytes) {
+  if (bytes >= (int64_t(1) << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "%s spans %lld bytes; bf16 operands must stay below 4 GiB", what,
+                (long long)bytes);
+  return MOE_OK;
+}
+
+// Operand spans of a bf16 forward over T tokens (x, the intermediate h, one expert's weights).
+int check_forward_spans(const moe_config* c, int64_t T) {
+  if (c->dtype != MOE_BF16) return MOE_OK;
+  const int64_t H = c->hidden_size, I = c->moe_intermediate_size;
+  const int64_t rows = T * (c->top_k + c->n_shared_experts);
+  int st;
+  if ((st = check_span("x [T, H]", T * H * 2))) return st;
+  if ((st = check_span("h [rows, I]", rows * I * 2))) return st;
+  if ((st = check_span("an expert weight [I, H]", I * H * 2))) return st;
+  return check_span("w_router [E, H]", (int64_t)c->n_routed_experts * H * 2);
+}
+
 bool use_stream_kernels(int64_t max_rows, int G) { return max_rows <= 4LL * G; }
 
 // Grouped SwiGLU scratch: h, then the plan.
@@ -317,6 +338,8 @@ int moe_route(const moe_config* cfg, int64_t T, const void* x, const void* w_rou
     return fail(MOE_ERR_INVALID_ARG, "moe_route: x, w_router, topk_ids and topk_weights are required");
   const int H = cfg->hidden_size, E = cfg->n_routed_experts, K = cfg->top_k;
   const bool bf16 = cfg->dtype == MOE_BF16;
+  if (bf16 && ((st = check_span("x [T, H]", T * H * 2)) || (st = check_span("w_router [E, H]", (int64_t)E * H * 2))))
+    return st;
   Carver cv(workspace);
   const int nsplit = moe::router_nsplit(T, H, E, bf16);
   float* part = cv.take<float>((int64_t)nsplit * T * E);
@@ -377,6 +400,12 @@ int moe_grouped_swiglu(const moe_config* cfg, int32_t n_groups, const int32_t* g
   if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "y_dtype %d", y_dtype);
   if (cfg->dtype == MOE_F32 && y_dtype != MOE_F32)
     return fail(MOE_ERR_UNSUPPORTED, "fp32 layers produce fp32 y_rows");
+  if (cfg->dtype == MOE_BF16) {
+    const int64_t H = cfg->hidden_size, I = cfg->moe_intermediate_size;
+    if ((!row_index && (st = check_span("x [max_rows, H]", max_rows * H * 2))) ||
+        (st = check_span("h [max_rows, I]", max_rows * I * 2)) || (st = check_span("an expert weight [I, H]", I * H * 2)))
+      return st;
+  }
   Carver cv(workspace);
   SwigluWs w = carve_swiglu(cv, cfg, n_groups, max_rows);
   if ((st = check_ws(workspace, workspace_bytes, cv.used))) return st;
@@ -422,6 +451,7 @@ int moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_r
     return fail(MOE_ERR_INVALID_ARG, "moe_forward: x, w_router, expert weights and y are required");
   if (cfg->n_shared_experts == 1 && (!ws_gate || !ws_up || !ws_down))
     return fail(MOE_ERR_INVALID_ARG, "moe_forward: shared expert weights are required");
+  if ((st = check_forward_spans(cfg, T))) return st;
   const int H = cfg->hidden_size, E = cfg->n_routed_experts, K = cfg->top_k;
   const bool bf16 = cfg->dtype == MOE_BF16;
   Carver cv(workspace);
@@ -453,6 +483,7 @@ int moe_forward_routed(const moe_config* cfg, int64_t T, const void* x, const in
     return fail(MOE_ERR_INVALID_ARG, "moe_forward_routed: x, routing, expert weights and y are required");
   if (cfg->n_shared_experts == 1 && (!ws_gate || !ws_up || !ws_down))
     return fail(MOE_ERR_INVALID_ARG, "moe_forward_routed: shared expert weights are required");
+  if ((st = check_forward_spans(cfg, T))) return st;
   Carver cv(workspace);
   ForwardWs w = carve_forward(cv, cfg, T, false);
   if ((st = check_ws(workspace, workspace_bytes, cv.used))) return st;

@@ -10,7 +10,7 @@
 //             last peer advances the wave's running cursor for that expert (LDS), so the order
 //             inside a segment is exactly (t, k) order without atomics on the output.
 // The plan kernel turns group offsets into (a) the list of groups with rows, largest first, for
-// the weight-streaming kernels and (b) the list of 128-row tiles for the tile kernels.  Group
+// the weight-streaming kernels and (b) the list of kTileM-row tiles for the tile kernels.  Group
 // sizes never leave the device.
 #include "kernels.h"
 
