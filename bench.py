@@ -256,7 +256,8 @@ def cpu_baseline(w, n_tokens):
     el = time.perf_counter() - t0 - gen[0]
     return {"value": n_tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n_tokens} tokens of the {w.name} workload (T={w.T}), all {w.K}+{w.n_shared} experts "
-                      f"each, float64 numpy; {el:.2f} s of oracle arithmetic, weight regeneration not timed"}
+                      f"each, float64 numpy; {el:.2f} s of oracle arithmetic timed, plus {gen[0]:.1f} s of "
+                      f"input (expert weight) regeneration not timed"}
 
 
 def _csv_rows(d, suffix):
@@ -275,7 +276,7 @@ def profile_summary(d):
     print("| kernel | calls | average µs | min µs | max µs | total ms | % of GPU time |")
     print("|---|---|---|---|---|---|---|")
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        name = r["Name"].split("(")[0] if "(" in r["Name"] else r["Name"]
+        name = r["Name"].replace("(anonymous namespace)::", "").split("(")[0]
         print(f"| `{name[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
               f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |")
 
@@ -334,7 +335,7 @@ def main():
                     help="comma-separated workloads measured in the same run and reported beside it ('none')")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="first run one copy of known size (the traffic summary's counter calibration)")
-    ap.add_argument("--cpu-tokens", type=int, default=6, help="tokens in the oracle's CPU-baseline sample (0: skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens in the oracle's CPU-baseline sample (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this implementation runs on one GPU; --gpus must be 1 (sharding across GPUs is "
