@@ -4,25 +4,63 @@
 // (gate + up -> SiLU -> multiply -> down), batched over experts as the grouped GEMM that
 // "Kimi K2.5 架构 QA" Q8.3 names in place of the per-expert loop.
 //
-// Work item = (row tile of one group, column tile).  The row tiles come from the device-side plan
-// (largest groups first, 256 rows each, so a K2 expert's ~170 prefill rows are one tile and every
-// weight byte is read once); a work-group stages the tile's rows -- gathered straight from the token
-// rows through row_index, so no permuted copy of x is ever written -- and a 256-row slice of the
-// weights through LDS, and runs the MFMA main loop of tile_core.h, which skips the 32-row
-// sub-tiles past the group's end.
-//   gate/up: the 256 weight rows are 128 gate rows and the 128 matching up rows, interleaved in
-//            32-row blocks, so column sub-tiles 2p and 2p+1 of a wave are the gate and up columns of
-//            the same 32 h columns, in the same lanes; the epilogue writes h = SiLU(g) * u as bf16.
-//   down:    256 rows of W_down; the epilogue writes y_rows (fp32 or bf16), times row_scale if given.
-// Work items are dealt XCD-major (tile_core.h) so the column tiles of one row tile run on the same
-// XCD at the same time and share its rows of A in that XCD's L2 while each weight byte is read once.
+// Work item = (row tile of one group, column slab).  Row tiles come from the device-side plan
+// (largest groups first, kTileM = 256 rows each, so a K2 expert's ~170 prefill rows are one tile
+// and every weight byte is read from HBM once).  With ~170 rows per expert the layer moves ~170
+// FLOP per weight byte, below the MI355X ridge (~310), so these kernels are weight streams first
+// and matrix-core loops second:
+//
+//   * B (weights) never touches LDS.  Each wave owns 32 weight rows (output columns) and loads them
+//     straight into v_mfma_f32_16x16x32_bf16 B-operand registers: one load instruction covers 64
+//     contiguous bytes of each of 16 rows, and kDepth K steps of it are in flight per wave (a
+//     register ring), which is what keeps HBM busy.  8 waves, two per SIMD (up to 128 accumulators
+//     and the 64-register ring fit a wave's 256 registers), so one wave's MFMAs cover the other's
+//     waits.
+//   * A (token rows) is shared by the 8 waves and staged through a kStages-deep LDS ring with
+//     gfx950's direct global -> LDS loads (no register round trip).  Each stage is its own
+//     __shared__ array and every access names its stage statically (the K loop is unrolled by
+//     kStages), so the compiler can tell which LDS reads depend on which direct loads; with a
+//     single array it would make every LDS read wait for the newest direct load, i.e. for all
+//     loads in flight, weights included.  Rows are gathered straight
+//     from x through row_index, so no permuted copy of x is written.  LDS rows are unpadded;
+//     16-byte chunk c of row r sits at c ^ swz(r), so the 16 rows one 16-lane group reads land in
+//     16 different bank groups.
+//   * Every wave multiplies all rows of the tile, in 32-row steps up to the group's end: the K loop
+//     is instantiated per row count (chosen outside the loop), so padding rows cost no MFMA and
+//     the A rows past the last 32-row step are not even loaded.
+//   * One barrier per K step (LDS traffic only; the loads in flight stay in flight).
+//
+//   gate/up: wave w owns h columns n0 + 16w .. +16 of the tile's 128: column sub-tile 0 is their
+//            gate rows, sub-tile 1 their up rows, so h = SiLU(g) * u is formed in registers.
+//   down:    wave w owns 32 rows of W_down; y_rows (fp32 or bf16), times row_scale if given.
+// Work items are dealt XCD-major, so the column slabs of one row tile run on the same XCD at the
+// same time and share its rows of A in that XCD's L2.
 #include "tile_core.h"
 
 namespace moe {
 namespace {
 
-using S = TileShape<kTileM, 256, 64, 2>;
-static_assert(S::kRowsPerLoad * S::kBLoads == 32, "wave w loads B rows [32w, 32w+32): one gate or up block");
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 512, kWaves = 8;
+constexpr int kBK = 64;                                // k per step
+constexpr int kRowBytes = kBK * 2;                     // one A row of one step in LDS
+constexpr int kStages = 4;                             // LDS ring of A (one __shared__ array per stage)
+constexpr int kDepth = kStages;                        // K steps of weights in flight per wave
+constexpr int kADist = kStages - 1;                    // A is loaded this many steps ahead
+constexpr int kStageBytes = kTileM * kRowBytes;        // 32 KiB
+constexpr int kSmemBytes = kStages * kStageBytes;      // 128 KiB
+constexpr int kALoads = kStageBytes / 1024 / kWaves;   // direct-to-LDS loads per wave per step (at most)
+constexpr int kNSub = 2;                               // 16-column sub-tiles per wave
+constexpr int kBLoads = 2 * kNSub;                     // 2 k-substeps x 2 column sub-tiles
+constexpr int kLoads = kALoads + kBLoads;              // vector-memory ops per wave per step
+constexpr int kSub = kTileM / 16;                      // 16-row sub-tiles of a tile
+static_assert(kALoads * kWaves * 1024 == kStageBytes && kRowBytes == 128 && kTileM % 32 == 0, "A staging");
+static_assert(kSmemBytes <= 160 * 1024, "LDS");
+static_assert(3 * kBLoads + 2 * kALoads <= 63, "vmcnt");
+
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 struct TileArgs {
   const int32_t* group_offsets;
@@ -55,117 +93,287 @@ __device__ __forceinline__ bool tile_of(const TileArgs& p, int& nt, TileRows& t)
   if (r1 > p.max_rows) r1 = p.max_rows;
   if (r1 < r0) r1 = r0;
   t.rbeg = r0 + m0;
-  t.rend = t.rbeg + S::BM < r1 ? t.rbeg + S::BM : r1;
+  t.rend = t.rbeg + kTileM < r1 ? t.rbeg + kTileM : r1;
   return t.rbeg < t.rend;
 }
 
-__global__ __launch_bounds__(512) void gateup_tile_kernel(TileArgs p) {
-  __shared__ __align__(16) char smem[S::kSmemBytes];
-  int nt;
-  TileRows t;
-  if (!tile_of(p, nt, t)) return;
-  const int H = p.H, I = p.I;
-  const bool sh = t.g == p.w.shared_group;
-  const uint16_t* wg = sh ? (const uint16_t*)p.w.s_gate : (const uint16_t*)p.w.gate + (int64_t)t.g * I * H;
-  const uint16_t* wu = sh ? (const uint16_t*)p.w.s_up : (const uint16_t*)p.w.up + (int64_t)t.g * I * H;
-  const int n0 = nt * (S::BN / 2);  // first h column of this tile (128 per tile)
+// Operand addressing: uniform bases plus 32-bit per-lane byte offsets (operands stay below 4 GiB).
+struct Operands {
+  const char* a_base;          // A rows; lane offsets a_off[j] include the row and the LDS chunk
+  uint32_t a_off[kALoads];
+  const char* b[kNSub];        // first weight row of each 16-column sub-tile of this wave
+  uint32_t b_off;              // row (lane % 16) and 16-byte quarter (lane / 16) of a 64-byte piece
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  Operands<S> o;
-  o.a_base = reinterpret_cast<const char*>(p.a);
-  // B rows (virtual columns) are 32-row blocks alternating gate / up; wave w loads block w, so its
-  // rows are gate rows when w is even and up rows when w is odd.  With the 2x4 wave grid every
-  // wave's two 32-column sub-tiles are then a gate block and the matching up block.  Virtual column
-  // vc holds h column n0 + 32*(vc/64) + vc%32.
-  const bool up_rows = __builtin_amdgcn_readfirstlane(w & 1) != 0;
-  o.b_base = reinterpret_cast<const char*>((up_rows ? wu : wg) + (int64_t)n0 * H);
-#pragma unroll
-  for (int j = 0; j < S::kALoads; ++j) {
-    const int rl = S::load_row(w, j, lane, S::kALoads);
-    const int64_t r = t.rbeg + rl;
-    const int64_t rr = r < t.rend ? r : t.rbeg;  // rows past the group end re-read its first row
-    const int64_t src = p.row_index ? (int64_t)p.row_index[rr] : rr;
-    o.a_off[j] = (uint32_t)((src * H + 8 * S::load_chunk(rl, lane)) * 2);
-  }
-#pragma unroll
-  for (int j = 0; j < S::kBLoads; ++j) {
-    const int vc = S::load_row(w, j, lane, S::kBLoads);
-    const int n = (vc >> 6) * 32 + (vc & 31);
-    o.b_off[j] = (uint32_t)(((int64_t)n * H + 8 * S::load_chunk(vc, lane)) * 2);
-  }
-  f32x16 acc[S::kMSub][S::kNSub];
-  const int m_valid = (int)(t.rend - t.rbeg);
-  tile_mainloop<S>(o, m_valid, H, smem, acc);
+// B fragments of one K step: [k-substep][column sub-tile].
+struct BFrag {
+  u32x4 v[2][kNSub];
+};
 
-  const int wave = w, wm = wave >> 2, wn = wave & 3;
-  uint16_t* h = static_cast<uint16_t*>(p.out);
-  const int nsv = (m_valid + 31) / 32;
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ void load_b(BFrag& f, const Operands& o, uint32_t kb) {
+  const uint32_t off = o.b_off + kb;
 #pragma unroll
-  for (int i = 0; i < S::kMSub; ++i) {
-    if (2 * i + wm >= nsv) continue;
-#pragma unroll
-    for (int pr = 0; pr < S::kNSub / 2; ++pr) {
-      const int col = n0 + wn * (S::kWaveN / 2) + pr * 32 + (lane & 31);  // kWaveN/2 = 32 h columns
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int64_t r = t.rbeg + S::sub_row(wm, i) + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        if (r < t.rend) h[r * I + col] = f32_to_bf16(swiglu_f32(acc[i][2 * pr][q], acc[i][2 * pr + 1][q]));
-      }
-    }
+  for (int s = 0; s < kNSub; ++s) {
+    f.v[0][s] = *reinterpret_cast<const u32x4*>(o.b[s] + off);
+    f.v[1][s] = *reinterpret_cast<const u32x4*>(o.b[s] + off + 64);
   }
 }
 
-__global__ __launch_bounds__(512) void down_tile_kernel(TileArgs p) {
-  __shared__ __align__(16) char smem[S::kSmemBytes];
+// A loads per wave per step when only the first 32*NP rows are multiplied.
+template <int NP>
+constexpr int a_loads() { return (4 * NP + kWaves - 1) / kWaves; }
+
+// Direct global -> LDS loads of step kt's A block: 1 KiB piece g (rows 8g .. 8g+7) is loaded by
+// wave g % kWaves; only the pieces under the first 32*NP rows are loaded.
+template <int NP>
+__device__ __forceinline__ void issue_a(const Operands& o, uint32_t kb, char* stage) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int j = 0; j < a_loads<NP>(); ++j)
+    __builtin_amdgcn_global_load_lds(o.a_base + (o.a_off[j] + kb), stage + (j * kWaves + w) * 1024, 16, 0, 0);
+}
+
+// MFMAs of one K step over the first 2*NP 16-row sub-tiles.  acc[i][s]: rows 16i.., column
+// sub-tile s; lane l, element e holds row 16i + 4*(l/16) + e, column 16s + l%16 of this wave.
+// The A fragments of the step (2 k-substeps x 2*NP sub-tiles) are read from LDS two ahead of the
+// MFMAs that use them, in a fixed order (a scheduling barrier after each fragment's MFMAs), so
+// only three are live at a time and each read has 8 MFMAs to land behind.
+template <int NP>
+__device__ __forceinline__ void compute_step(const char* stage, const BFrag& b, f32x4 (&acc)[2 * NP][kNSub]) {
+  constexpr int kFrags = 2 * (2 * NP);
+  const int lane = threadIdx.x & 63, r16 = lane & 15, q = lane >> 4;
+  // swz(16i + r16) == swz(r16): the lane's chunk position is the same in every sub-tile
+  const char* ap0 = stage + r16 * kRowBytes + ((q ^ swz(r16)) << 4);
+  const char* ap1 = stage + r16 * kRowBytes + (((4 + q) ^ swz(r16)) << 4);
+  auto read = [&](int f) {
+    const int kk = f / (2 * NP), i = f % (2 * NP);
+    return *reinterpret_cast<const bf16x8*>((kk ? ap1 : ap0) + i * 16 * kRowBytes);
+  };
+  bf16x8 a[kFrags];
+  a[0] = read(0);
+  a[1] = read(1);
+#pragma unroll
+  for (int f = 0; f < kFrags; ++f) {
+    if (f + 2 < kFrags) a[f + 2] = read(f + 2);
+    const int kk = f / (2 * NP), i = f % (2 * NP);
+#pragma unroll
+    for (int s = 0; s < kNSub; ++s)
+      acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[f], as_bf16x8(b.v[kk][s]), acc[i][s], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The A ring: stage d of step kt is array kt % kStages.
+struct Ring {
+  char* st[kStages];
+};
+
+// One K step (kt % kStages == D): wait for this wave's A block of step kt, then for every wave's
+// (barrier, which also frees the stage of step kt-1), refill that stage with step kt+kADist,
+// multiply, and refill this step's register slot with the weights of step kt+kDepth.
+// Vector-memory order per wave: ..., A(j), B(j+1), A(j+1), B(j+2), ...  so when step kt starts,
+// the operations issued after A(kt) are B(kt+1), A(kt+1), B(kt+2), A(kt+2), B(kt+3) (those that
+// exist), kBLoads or a_loads<NP>() each.
+template <int NP, int D, bool kTail>
+__device__ __forceinline__ void kstep(const Operands& o, int kt, int nk, const Ring& ring, BFrag (&b)[kDepth],
+                                      f32x4 (&acc)[2 * NP][kNSub]) {
+  constexpr int kA = a_loads<NP>();
+  const int ahead = kTail ? nk - 1 - kt : 3;
+  if (ahead >= 3)
+    wait_vmcnt<3 * kBLoads + 2 * kA>();
+  else if (ahead == 2)
+    wait_vmcnt<2 * kBLoads + 2 * kA>();
+  else if (ahead == 1)
+    wait_vmcnt<kBLoads + kA>();
+  else
+    wait_vmcnt<0>();
+  block_sync_lds();
+  if (!kTail || kt + kADist < nk) issue_a<NP>(o, (uint32_t)(kt + kADist) * kRowBytes, ring.st[(D + kADist) % kStages]);
+  compute_step<NP>(ring.st[D], b[D], acc);
+  if (!kTail || kt + kDepth < nk) load_b(b[D], o, (uint32_t)(kt + kDepth) * kRowBytes);
+}
+
+template <int NP>
+__device__ __forceinline__ void kloop(const Operands& o, int nk, const Ring& ring, f32x4 (&acc)[2 * NP][kNSub]) {
+  static_assert(kStages == 4 && kDepth == 4 && kADist == 3, "the unrolling below");
+  BFrag b[kDepth];
+  int kt = 0;
+  if (nk >= 8) {
+    // prologue in the steady-state order B(0), A(0), B(1), A(1), B(2), A(2), B(3); unconditional,
+    // so the compiler's own wait for B(kt) at the loop head sees the full count of later loads
+#pragma unroll
+    for (int s = 0; s < kDepth; ++s) {
+      load_b(b[s], o, (uint32_t)s * kRowBytes);
+      if (s < kADist) issue_a<NP>(o, (uint32_t)s * kRowBytes, ring.st[s]);
+    }
+    // steady state: every refill of these four steps exists (kt + 7 < nk), no conditions
+    for (; kt + 8 <= nk; kt += 4) {
+      kstep<NP, 0, false>(o, kt, nk, ring, b, acc);
+      kstep<NP, 1, false>(o, kt + 1, nk, ring, b, acc);
+      kstep<NP, 2, false>(o, kt + 2, nk, ring, b, acc);
+      kstep<NP, 3, false>(o, kt + 3, nk, ring, b, acc);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < kDepth; ++s) {
+      if (s < nk) load_b(b[s], o, (uint32_t)s * kRowBytes);
+      if (s < kADist && s < nk) issue_a<NP>(o, (uint32_t)s * kRowBytes, ring.st[s]);
+    }
+  }
+  // the last 2 to 6 steps (K is a multiple of 128, so nk is even)
+  if (kt + 4 <= nk) {
+    kstep<NP, 0, true>(o, kt, nk, ring, b, acc);
+    kstep<NP, 1, true>(o, kt + 1, nk, ring, b, acc);
+    kstep<NP, 2, true>(o, kt + 2, nk, ring, b, acc);
+    kstep<NP, 3, true>(o, kt + 3, nk, ring, b, acc);
+    kt += 4;
+  }
+  if (kt < nk) kstep<NP, 0, true>(o, kt, nk, ring, b, acc);
+  if (kt + 1 < nk) kstep<NP, 1, true>(o, kt + 1, nk, ring, b, acc);
+}
+
+// The tile's product over the full K (a multiple of kBK) for its first 2*NP 16-row sub-tiles,
+// then the epilogue on the accumulators.
+template <int NP, class Epilogue>
+__device__ __forceinline__ void tile_body(const Operands& o, int K, const Ring& smem, const Epilogue& epilogue) {
+  f32x4 acc[2 * NP][kNSub];
+#pragma unroll
+  for (int i = 0; i < 2 * NP; ++i)
+#pragma unroll
+    for (int s = 0; s < kNSub; ++s) acc[i][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  kloop<NP>(o, K / kBK, smem, acc);
+  epilogue(acc);
+}
+
+// One instance of the whole tile body per 32-row count of the tile (1..8): the accumulators of
+// each instance are sized to its rows, and nothing is merged across instances.  Device pass
+// only: these instances are device code.
+template <class Epilogue>
+__device__ __forceinline__ void run_tile(const Operands& o, int m_valid, int K, const Ring& smem, const Epilogue& epilogue) {
+  static_assert(kSub == 16, "dispatch below covers 1..8 row pairs");
+  const int np = (m_valid + 31) / 32;
+#if defined(__HIP_DEVICE_COMPILE__)
+  switch (np) {
+    case 8: tile_body<8>(o, K, smem, epilogue); break;
+    case 7: tile_body<7>(o, K, smem, epilogue); break;
+    case 6: tile_body<6>(o, K, smem, epilogue); break;
+    case 5: tile_body<5>(o, K, smem, epilogue); break;
+    case 4: tile_body<4>(o, K, smem, epilogue); break;
+    case 3: tile_body<3>(o, K, smem, epilogue); break;
+    case 2: tile_body<2>(o, K, smem, epilogue); break;
+    default: tile_body<1>(o, K, smem, epilogue); break;
+  }
+#else
+  (void)np;
+  (void)o;
+  (void)K;
+  (void)smem;
+  (void)epilogue;
+#endif
+}
+
+// Lane offsets of the A loads: row rl of the tile is source row src(rl) of a [*, K] matrix.
+template <class RowOf>
+__device__ __forceinline__ void a_offsets(Operands& o, int K, RowOf row_of) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < kALoads; ++j) {
+    const int rl = (j * kWaves + w) * 8 + (lane >> 3);  // 8 rows of 128 bytes per 1 KiB load
+    const int chunk = (lane & 7) ^ swz(rl);              // the chunk that belongs in this lane's slot
+    o.a_off[j] = (uint32_t)((row_of(rl) * K + 8 * chunk) * 2);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gateup_tile_kernel(TileArgs p) {
+  __shared__ __align__(16) char a0[kStageBytes], a1[kStageBytes], a2[kStageBytes], a3[kStageBytes];
+  const Ring smem{{a0, a1, a2, a3}};
   int nt;
   TileRows t;
   if (!tile_of(p, nt, t)) return;
   const int H = p.H, I = p.I;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool sh = t.g == p.w.shared_group;
+  const uint16_t* wg = sh ? (const uint16_t*)p.w.s_gate : (const uint16_t*)p.w.gate + (int64_t)t.g * I * H;
+  const uint16_t* wu = sh ? (const uint16_t*)p.w.s_up : (const uint16_t*)p.w.up + (int64_t)t.g * I * H;
+  const int c0 = nt * 128 + 16 * w;  // first h column of this wave
+
+  Operands o;
+  o.a_base = reinterpret_cast<const char*>(p.a);
+  a_offsets(o, H, [&](int rl) -> int64_t {
+    const int64_t r = t.rbeg + rl;
+    const int64_t rr = r < t.rend ? r : t.rbeg;  // rows past the group end re-read its first row
+    return p.row_index ? (int64_t)p.row_index[rr] : rr;
+  });
+  o.b[0] = reinterpret_cast<const char*>(wg + (int64_t)c0 * H);  // gate rows of the wave's 16 columns
+  o.b[1] = reinterpret_cast<const char*>(wu + (int64_t)c0 * H);  // their up rows
+  o.b_off = (uint32_t)((lane & 15) * H * 2 + 16 * (lane >> 4));
+
+  uint16_t* h = static_cast<uint16_t*>(p.out);
+  const int64_t rbeg = t.rbeg, rend = t.rend;
+  run_tile(o, (int)(rend - rbeg), H, smem, [&](const auto& acc) {
+    constexpr int n16 = sizeof(acc) / sizeof(acc[0]);
+#pragma unroll
+    for (int i = 0; i < n16; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t r = rbeg + 16 * i + 4 * (lane >> 4) + e;
+        if (r >= rend) continue;
+        h[r * I + c0 + (lane & 15)] = f32_to_bf16(swiglu_f32(acc[i][0][e], acc[i][1][e]));
+      }
+  });
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void down_tile_kernel(TileArgs p) {
+  __shared__ __align__(16) char a0[kStageBytes], a1[kStageBytes], a2[kStageBytes], a3[kStageBytes];
+  const Ring smem{{a0, a1, a2, a3}};
+  int nt;
+  TileRows t;
+  if (!tile_of(p, nt, t)) return;
+  const int H = p.H, I = p.I;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint16_t* wd = t.g == p.w.shared_group ? (const uint16_t*)p.w.s_down
                                                 : (const uint16_t*)p.w.down + (int64_t)t.g * H * I;
-  const int n0 = nt * S::BN;
+  const int c0 = nt * 256 + 32 * w;  // first output column of this wave (H is a multiple of 32)
+  const bool cols_ok = c0 < H;       // the last slab of an H that is not a multiple of 256
 
-  const int tid = threadIdx.x, w = tid >> 6;
-  Operands<S> o;
+  Operands o;
   o.a_base = reinterpret_cast<const char*>(p.a);
-  o.b_base = reinterpret_cast<const char*>(wd);
-#pragma unroll
-  for (int j = 0; j < S::kALoads; ++j) {
-    const int rl = S::load_row(w, j, tid & 63, S::kALoads);
+  a_offsets(o, I, [&](int rl) -> int64_t {
     const int64_t r = t.rbeg + rl;
-    o.a_off[j] = (uint32_t)(((r < t.rend ? r : t.rbeg) * I + 8 * S::load_chunk(rl, tid & 63)) * 2);
-  }
+    return r < t.rend ? r : t.rbeg;
+  });
 #pragma unroll
-  for (int j = 0; j < S::kBLoads; ++j) {
-    const int vc = S::load_row(w, j, tid & 63, S::kBLoads);
-    const int n = n0 + vc;  // columns past H (last tile) read row 0, never stored
-    o.b_off[j] = (uint32_t)(((int64_t)(n < H ? n : 0) * I + 8 * S::load_chunk(vc, tid & 63)) * 2);
-  }
-  f32x16 acc[S::kMSub][S::kNSub];
-  const int m_valid = (int)(t.rend - t.rbeg);
-  tile_mainloop<S>(o, m_valid, I, smem, acc);
+  for (int s = 0; s < kNSub; ++s)  // idle waves re-read the first rows
+    o.b[s] = reinterpret_cast<const char*>(wd + (int64_t)((cols_ok ? c0 : 0) + 16 * s) * I);
+  o.b_off = (uint32_t)((lane & 15) * I * 2 + 16 * (lane >> 4));
 
-  const int lane = tid & 63, wave = w, wm = wave >> 2, wn = wave & 3;
+  const int64_t rbeg = t.rbeg, rend = t.rend;
+  const float* row_scale = p.row_scale;
+  void* out = p.out;
+  const bool out_bf16 = p.out_bf16 != 0;
+  run_tile(o, (int)(rend - rbeg), I, smem, [&](const auto& acc) {
+    if (!cols_ok) return;
+    constexpr int n16 = sizeof(acc) / sizeof(acc[0]);
 #pragma unroll
-  for (int i = 0; i < S::kMSub; ++i) {
-    if (2 * i + wm >= (m_valid + 31) / 32) continue;
+    for (int i = 0; i < n16; ++i)
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int64_t r = t.rbeg + S::sub_row(wm, i) + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-      if (r >= t.rend) continue;
-      const float sc = p.row_scale ? p.row_scale[r] : 1.f;
+      for (int e = 0; e < 4; ++e) {
+        const int64_t r = rbeg + 16 * i + 4 * (lane >> 4) + e;
+        if (r >= rend) continue;
+        const float sc = row_scale ? row_scale[r] : 1.f;
 #pragma unroll
-      for (int u = 0; u < S::kNSub; ++u) {
-        const int col = n0 + wn * S::kWaveN + 32 * u + (lane & 31);
-        if (col >= H) continue;
-        const float v = acc[i][u][q] * sc;
-        if (p.out_bf16)
-          static_cast<uint16_t*>(p.out)[r * H + col] = f32_to_bf16(v);
-        else
-          static_cast<float*>(p.out)[r * H + col] = v;
+        for (int s = 0; s < kNSub; ++s) {
+          const int col = c0 + 16 * s + (lane & 15);
+          const float v = acc[i][s][e] * sc;
+          if (out_bf16)
+            static_cast<uint16_t*>(out)[r * H + col] = f32_to_bf16(v);
+          else
+            static_cast<float*>(out)[r * H + col] = v;
+        }
       }
-    }
-  }
+  });
 }
 
 unsigned grid_for(int64_t max_tiles, int n_ntiles) {
@@ -178,17 +386,16 @@ unsigned grid_for(int64_t max_tiles, int n_ntiles) {
 
 hipError_t launch_gateup_tile_bf16(const Groups& g, const Weights& w, const uint16_t* x, uint16_t* h, int H, int I,
                                    hipStream_t s) {
-  TileArgs p{g.group_offsets, g.row_index, g.tiles, g.counters, g.max_rows, w, x, h, 1, nullptr, H, I,
-             I / (S::BN / 2)};
-  gateup_tile_kernel<<<grid_for(g.max_tiles, p.n_ntiles), S::kThreads, 0, s>>>(p);
+  TileArgs p{g.group_offsets, g.row_index, g.tiles, g.counters, g.max_rows, w, x, h, 1, nullptr, H, I, I / 128};
+  gateup_tile_kernel<<<grid_for(g.max_tiles, p.n_ntiles), kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 
 hipError_t launch_down_tile_bf16(const Groups& g, const Weights& w, const uint16_t* h, void* y_rows, bool y_bf16,
                                  const float* row_scale, int H, int I, hipStream_t s) {
   TileArgs p{g.group_offsets, nullptr, g.tiles, g.counters, g.max_rows, w, h, y_rows, y_bf16 ? 1 : 0, row_scale,
-             H, I, (H + S::BN - 1) / S::BN};
-  down_tile_kernel<<<grid_for(g.max_tiles, p.n_ntiles), S::kThreads, 0, s>>>(p);
+             H, I, (H + 255) / 256};
+  down_tile_kernel<<<grid_for(g.max_tiles, p.n_ntiles), kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -96,7 +96,7 @@ hipError_t launch_down_stream_bf16(const Groups& g, const Weights& w, const uint
 hipError_t launch_down_tile_bf16(const Groups& g, const Weights& w, const uint16_t* h, void* y_rows,
                                  bool y_bf16, const float* row_scale, int H, int I, hipStream_t s);
 // Rows per tile used by the tile kernels' plan.
-constexpr int kTileM = 256;
+constexpr int kTileM = 256;  // rows per tile of the tile GEMMs
 
 // grouped SwiGLU, fp32 (plain kernels) ---------------------------------------------
 hipError_t launch_gateup_f32(const Groups& g, const Weights& w, const float* x, float* h, int H, int I,
