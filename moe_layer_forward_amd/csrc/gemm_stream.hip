@@ -2,21 +2,27 @@
 //
 // Experts as in "Kimi K2.5 模型架构深度拆解" §4.3 / §10.2 Steps 5-6, batched over the experts present
 // (the grouped GEMM of "Kimi K2.5 架构 QA" Q8.3).  With ~1-2 tokens per expert every weight byte is
-// used once or twice, so the kernel is a weight stream: each weight row is read exactly once per
-// 16-row pass, straight from HBM into the MFMA B operand (no LDS), and the handful of token rows ride
-// along as the A operand from L2.
+// used once or twice, so the kernel is a weight stream: each weight byte crosses HBM once per pass
+// over the group's rows (one pass covers up to 32 rows).
 //
 // A wave owns 16 output columns of one group: 16 gate rows + the 16 matching up rows (gate/up) or 16
-// rows of W_down (down).  A 128-wide K step of a weight row is 256 bytes; load j (j = 0..3) of lane l
-// takes bytes 64*j + 16*(l/16) .. +16 of row l%16, so each load covers 64 contiguous bytes of each of
-// 16 rows, and load j is the B operand of the j-th 16x16x32 MFMA.  Because the K sum is order-free,
-// the token rows (A operand) are read with the same K permutation, so no shuffle is needed.  The next
-// step's loads are issued before the current step's MFMAs (register double buffer).  Plain loads:
-// measured on MI355X, this row-strided shape streams at ~6.2 TB/s with ordinary loads and far
-// slower with non-temporal ones.
+// rows of W_down (down).  Its weight rows stream through a wave-private LDS ring with gfx950's direct
+// global -> LDS loads: one load instruction moves 4 rows x 256 contiguous bytes (whole cache lines)
+// with the streaming (non-temporal) policy -- measured on MI355X at ~7.0 TB/s, against ~6.2 TB/s for
+// 16-row x 64-byte register loads -- and kDepth K steps are in flight.  The 16 x 256-byte rows of a
+// step sit in LDS with 16-byte chunk c of row r at position c ^ r, so the v_mfma_f32_16x16x32_bf16
+// B-operand reads (16 rows, one chunk each per 16-lane group) hit 16 different bank groups.  The
+// token rows (A operand, from L2) are loaded into registers in the same step as their weights, so the
+// wave's in-order load counter never makes a weight load wait for a younger token-row load.
+// The ring is private to the wave: no barriers.  Each ring stage is its own __shared__ array and the
+// K loop is unrolled by the stage count, so the compiler can tell which LDS reads depend on which
+// direct loads.
 // Work-groups = 4 waves = 64 columns of one group; groups come from the plan's active list, largest
 // first, so the long-running many-row groups start early.
+#include <type_traits>
+
 #include "kernels.h"
+#include "tile_core.h"
 
 namespace moe {
 namespace {
@@ -35,22 +41,206 @@ struct StreamArgs {
   int H, I, n_nblk;
 };
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-struct Frag {
-  u32x4 v[4];
-};
-
-// Four 16-byte loads at p, p + 32, p + 64, p + 96 elements (64-byte stride): one K step of one row.
-__device__ __forceinline__ void load_frag(Frag& f, const uint16_t* p) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) f.v[j] = *reinterpret_cast<const u32x4*>(p + 32 * j);
-}
+constexpr int kWaves = 4;
+constexpr int kStepK = 128;                 // k per step: 256 bytes of each weight row
+constexpr int kSetBytes = 16 * 256;         // one 16-row set of one step
+constexpr int kMaxPasses = 2;               // 16-row passes per stream of the weights
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
-template <bool SWIGLU>
+// R weight-row sets per wave (2: gate + up, 1: down), D ring stages, NP 16-row passes.
+template <int R, int D>
+struct Ring {
+  static constexpr int kWaveBytes = R * kSetBytes;           // one wave's part of one stage
+  static constexpr int kStageBytes = kWaves * kWaveBytes;
+  char* st[D];
+};
+
+// Token-row fragments of one step for NP passes: 4 x 16 bytes per lane per pass.
+template <int NP>
+struct AFrag {
+  u32x4 v[NP][4];
+};
+
+template <int R, int D, int NP>
+struct Stream {
+  static constexpr int kLoads = 4 * R + 4 * NP;  // vector-memory ops per step per wave
+  static_assert((D - 1) * kLoads <= 63, "vmcnt");
+
+  const char* wb[R];        // weight-row sets: first row of this wave's 16 (uniform)
+  uint32_t w_off[4];        // lane offsets of the 4 direct loads of a set (row, swizzled chunk)
+  const uint16_t* arow[NP]; // token row of each pass for this lane (row lane % 16), at k = 8*(lane/16)
+  int wave_off;             // this wave's part of a stage
+
+  __device__ __forceinline__ void issue(const Ring<R, D>& ring, int d, int st, AFrag<NP>& a) const {
+    char* dst = ring.st[d] + wave_off;
+    const uint32_t kb = (uint32_t)st * (kStepK * 2);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(wb[r] + (w_off[i] + kb), dst + r * kSetBytes + i * 1024, 16, 0, 2);
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a.v[p][j] = *reinterpret_cast<const u32x4*>(arow[p] + st * kStepK + 32 * j);
+  }
+
+  // MFMAs of one step: B fragments from this wave's ring part, A fragments from registers.
+  __device__ __forceinline__ void compute(const Ring<R, D>& ring, int d, const AFrag<NP>& a,
+                                          f32x4 (&acc)[NP][R]) const {
+    const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
+    const char* src = ring.st[d] + wave_off + c * 256;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(src + r * kSetBytes + (((4 * j + q) ^ c) << 4));
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+          acc[p][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a.v[p][j]), b, acc[p][r], 0, 0, 0);
+      }
+    }
+  }
+
+  // One step (st % D == DS): wait for its loads, refill its stage and A slot with step st + D - 1
+  // (issued first: the loads of a step are its weights then its token rows, and step st's are the
+  // oldest D-1 steps back), multiply.
+  template <int DS, bool kTail>
+  __device__ __forceinline__ void step(const Ring<R, D>& ring, int st, int nsteps, AFrag<NP> (&a)[D],
+                                       f32x4 (&acc)[NP][R]) const {
+    const int ahead = kTail ? nsteps - 1 - st : D - 1;  // later steps already issued
+    if constexpr (D == 2) {
+      if (ahead >= 1) wait_vmcnt<kLoads>(); else wait_vmcnt<0>();
+    } else {
+      static_assert(D == 4, "waits below");
+      if (ahead >= 3) wait_vmcnt<3 * kLoads>();
+      else if (ahead == 2) wait_vmcnt<2 * kLoads>();
+      else if (ahead == 1) wait_vmcnt<kLoads>();
+      else wait_vmcnt<0>();
+    }
+    // nothing of this step moves above the wait (the compiler would then wait for every load itself)
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ring, DS, a[DS], acc);
+    // every LDS read of this stage is done before it is refilled
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (!kTail || st + D < nsteps) issue(ring, DS, st + D, a[DS]);
+  }
+
+  // The whole K stream (nsteps steps) into acc.
+  __device__ __forceinline__ void run(const Ring<R, D>& ring, int nsteps, f32x4 (&acc)[NP][R]) const {
+    AFrag<NP> a[D];
+    int st = 0;
+    if (nsteps >= 2 * D) {
+      // unconditional prologue and steady state: every refill of an unrolled block exists
+#pragma unroll
+      for (int s = 0; s < D; ++s) issue(ring, s, s, a[s]);
+      for (; st + 2 * D <= nsteps; st += D) unrolled<false>(ring, st, nsteps, a, acc);
+    } else {
+#pragma unroll
+      for (int s = 0; s < D; ++s)
+        if (s < nsteps) issue(ring, s, s, a[s]);
+    }
+    // the last D .. 2D-1 steps (or all of a short stream), refills checked
+    for (; st + D <= nsteps; st += D) unrolled<true>(ring, st, nsteps, a, acc);
+    tail_steps(ring, st, nsteps, a, acc);
+  }
+
+  template <bool kTail>
+  __device__ __forceinline__ void unrolled(const Ring<R, D>& ring, int st, int nsteps, AFrag<NP> (&a)[D],
+                                           f32x4 (&acc)[NP][R]) const {
+    step<0, kTail>(ring, st, nsteps, a, acc);
+    step<1, kTail>(ring, st + 1, nsteps, a, acc);
+    if constexpr (D == 4) {
+      step<2, kTail>(ring, st + 2, nsteps, a, acc);
+      step<3, kTail>(ring, st + 3, nsteps, a, acc);
+    }
+  }
+
+  __device__ __forceinline__ void tail_steps(const Ring<R, D>& ring, int st, int nsteps, AFrag<NP> (&a)[D],
+                                             f32x4 (&acc)[NP][R]) const {
+    if (st < nsteps) step<0, true>(ring, st, nsteps, a, acc);
+    if constexpr (D == 4) {
+      if (st + 1 < nsteps) step<1, true>(ring, st + 1, nsteps, a, acc);
+      if (st + 2 < nsteps) step<2, true>(ring, st + 2, nsteps, a, acc);
+    }
+  }
+};
+
+// One pass over the weights for rows [mb, mb + 16*NP) of the group (rows past r1 are computed from a
+// copy of row mb and never stored), then the epilogue.
+template <bool SWIGLU, int D, int NP>
+__device__ __forceinline__ void stream_pass(const StreamArgs& p, const Ring<SWIGLU ? 2 : 1, D>& ring,
+                                            const char* const (&wb)[SWIGLU ? 2 : 1], int n0, int64_t mb,
+                                            int64_t r1) {
+  constexpr int R = SWIGLU ? 2 : 1;
+  const int H = p.H, I = p.I, K = SWIGLU ? H : I;
+  const int lane = threadIdx.x & 63;
+  // wave-uniform, so the LDS destinations of the direct loads stay visibly inside their stage array
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  Stream<R, D, NP> s;
+#pragma unroll
+  for (int r = 0; r < R; ++r) s.wb[r] = wb[r];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * i + (lane >> 4);  // lane's row in the 16-row set, its slot = chunk position
+    s.w_off[i] = (uint32_t)(row * K * 2 + (((lane & 15) ^ row) << 4));
+  }
+#pragma unroll
+  for (int q = 0; q < NP; ++q) {
+    const int64_t r = mb + 16 * q + (lane & 15);
+    const int64_t rr = r < r1 ? r : mb;
+    const int64_t src = SWIGLU ? (p.row_index ? (int64_t)p.row_index[rr] : rr) : rr;
+    s.arow[q] = p.a + src * K + (lane >> 4) * 8;
+  }
+  s.wave_off = wave * Ring<R, D>::kWaveBytes;
+
+  f32x4 acc[NP][R];
+#pragma unroll
+  for (int q = 0; q < NP; ++q)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[q][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  s.run(ring, K / kStepK, acc);
+
+  // lane holds rows mb + 16q + 4*(lane/16) + e, column n0 + lane%16
+  const int col = n0 + (lane & 15);
+#pragma unroll
+  for (int q = 0; q < NP; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t row = mb + 16 * q + 4 * (lane >> 4) + e;
+      if (row >= r1) continue;
+      if (SWIGLU) {
+        static_cast<uint16_t*>(p.out)[row * I + col] = f32_to_bf16(swiglu_f32(acc[q][0][e], acc[q][1][e]));
+      } else {
+        const float v = acc[q][0][e] * (p.row_scale ? p.row_scale[row] : 1.f);
+        if (p.out_bf16)
+          static_cast<uint16_t*>(p.out)[row * H + col] = f32_to_bf16(v);
+        else
+          static_cast<float*>(p.out)[row * H + col] = v;
+      }
+    }
+}
+
+template <bool SWIGLU, int D>
 __global__ __launch_bounds__(256) void stream_kernel(StreamArgs p) {
+  constexpr int R = SWIGLU ? 2 : 1;
+  constexpr int kStage = Ring<R, D>::kStageBytes;
+  __shared__ __align__(16) char s0[kStage], s1[kStage], s2[D == 4 ? kStage : 16], s3[D == 4 ? kStage : 16];
+  Ring<R, D> ring;
+  ring.st[0] = s0;
+  ring.st[1] = s1;
+  if constexpr (D == 4) {
+    ring.st[2] = s2;
+    ring.st[3] = s3;
+  } else {
+    (void)s2;
+    (void)s3;
+  }
+
   const int slot = blockIdx.x / p.n_nblk, nb = blockIdx.x % p.n_nblk;
   if (slot >= p.counters[0]) return;
   const int g = p.active[slot];
@@ -58,79 +248,35 @@ __global__ __launch_bounds__(256) void stream_kernel(StreamArgs p) {
   if (r0 > p.max_rows) r0 = p.max_rows;
   if (r1 > p.max_rows) r1 = p.max_rows;
   const int H = p.H, I = p.I;
-  const int K = SWIGLU ? H : I;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = nb * 64 + wave * 16;       // first output column of this wave
-  const int kq = (lane >> 4) * 8;           // this lane's 16-byte slot inside each 64-byte quarter
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = nb * 64 + wave * 16;  // first output column of this wave
   const bool sh = g == p.w.shared_group;
 
-  const uint16_t* w0;
-  const uint16_t* w1 = nullptr;
-  if (SWIGLU) {
+  const char* wb[R];
+  if constexpr (SWIGLU) {
     const uint16_t* wg = sh ? (const uint16_t*)p.w.s_gate : (const uint16_t*)p.w.gate + (int64_t)g * I * H;
     const uint16_t* wu = sh ? (const uint16_t*)p.w.s_up : (const uint16_t*)p.w.up + (int64_t)g * I * H;
-    w0 = wg + (int64_t)(n0 + (lane & 15)) * H + kq;
-    w1 = wu + (int64_t)(n0 + (lane & 15)) * H + kq;
+    wb[0] = reinterpret_cast<const char*>(wg + (int64_t)n0 * H);
+    wb[1] = reinterpret_cast<const char*>(wu + (int64_t)n0 * H);
   } else {
     const uint16_t* wd = sh ? (const uint16_t*)p.w.s_down : (const uint16_t*)p.w.down + (int64_t)g * H * I;
-    w0 = wd + (int64_t)(n0 + (lane & 15)) * I + kq;
+    wb[0] = reinterpret_cast<const char*>(wd + (int64_t)n0 * I);
   }
-  const int nsteps = K / 128;
-
-  for (int64_t mb = r0; mb < r1; mb += 16) {
-    // Rows past the group end read the group's first row and are zeroed (no branch around loads).
-    const int64_t r = mb + (lane & 15);
-    const bool rok = r < r1;
-    const int64_t rr = rok ? r : mb;
-    const int64_t src = SWIGLU ? (p.row_index ? (int64_t)p.row_index[rr] : rr) : rr;
-    const uint16_t* arow = p.a + src * K + kq;
-    const uint32_t keep = rok ? 0xffffffffu : 0u;
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    Frag a[2], b0[2], b1[2];
-    auto load = [&](int buf, int st) {
-      const int64_t off = (int64_t)st * 128;
-      load_frag(a[buf], arow + off);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) a[buf].v[j] &= keep;
-      load_frag(b0[buf], w0 + off);
-      if (SWIGLU) load_frag(b1[buf], w1 + off);
-    };
-    auto mma = [&](int buf) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8 av = as_bf16x8(a[buf].v[j]);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, as_bf16x8(b0[buf].v[j]), acc0, 0, 0, 0);
-        if (SWIGLU) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, as_bf16x8(b1[buf].v[j]), acc1, 0, 0, 0);
-      }
-    };
-    load(0, 0);
-    int st = 0;
-    for (; st + 2 <= nsteps; st += 2) {
-      load(1, st + 1);
-      mma(0);
-      if (st + 2 < nsteps) load(0, st + 2);
-      mma(1);
-    }
-    if (st < nsteps) mma(0);  // odd step count: the last step sits in buffer 0
-
-    // lane holds rows mb + 4*(lane/16) + i, column n0 + lane%16
-    const int col = n0 + (lane & 15);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t row = mb + 4 * (lane >> 4) + i;
-      if (row >= r1) continue;
-      if (SWIGLU) {
-        static_cast<uint16_t*>(p.out)[row * I + col] = f32_to_bf16(swiglu_f32(acc0[i], acc1[i]));
-      } else {
-        const float v = acc0[i] * (p.row_scale ? p.row_scale[row] : 1.f);
-        if (p.out_bf16)
-          static_cast<uint16_t*>(p.out)[row * H + col] = f32_to_bf16(v);
-        else
-          static_cast<float*>(p.out)[row * H + col] = v;
-      }
-    }
-  }
+  // Passes of 32 rows (two 16-row MFMA row blocks).  A single-block variant for groups of at most
+  // 16 rows would save the second block's token-row loads and MFMAs, but its K loop gets a full
+  // drain of the load counter at every loop head from the compiler, which costs far more than the
+  // redundant row loads (they hit L1/L2: the rows past the group's end repeat its first row).
+  // Device pass only: the pass is device code.
+#if defined(__HIP_DEVICE_COMPILE__)
+  for (int64_t mb = r0; mb < r1; mb += 16 * kMaxPasses) stream_pass<SWIGLU, D, kMaxPasses>(p, ring, wb, n0, mb, r1);
+#else
+  (void)wb;
+  (void)n0;
+#endif
 }
+
+constexpr int kDepthGateUp = 4;  // 4 x 32 KiB of LDS: one work-group per CU
+constexpr int kDepthDown = 4;    // 4 x 16 KiB: two work-groups per CU
 
 }  // namespace
 
@@ -138,7 +284,7 @@ hipError_t launch_gateup_stream_bf16(const Groups& g, const Weights& w, const ui
                                      hipStream_t s) {
   StreamArgs p{g.group_offsets, g.row_index, g.active, g.counters, g.max_rows, w, x, h, 1, nullptr, H, I, I / 64};
   const int64_t blocks = (int64_t)g.n_groups * p.n_nblk;
-  stream_kernel<true><<<(unsigned)blocks, 256, 0, s>>>(p);
+  stream_kernel<true, kDepthGateUp><<<(unsigned)blocks, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -147,7 +293,7 @@ hipError_t launch_down_stream_bf16(const Groups& g, const Weights& w, const uint
   StreamArgs p{g.group_offsets, nullptr, g.active, g.counters, g.max_rows, w, h, y_rows, y_bf16 ? 1 : 0, row_scale,
                H, I, H / 64};
   const int64_t blocks = (int64_t)g.n_groups * p.n_nblk;
-  stream_kernel<false><<<(unsigned)blocks, 256, 0, s>>>(p);
+  stream_kernel<false, kDepthDown><<<(unsigned)blocks, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 

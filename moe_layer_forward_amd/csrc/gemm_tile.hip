@@ -35,6 +35,8 @@
 //   down:    wave w owns 32 rows of W_down; y_rows (fp32 or bf16), times row_scale if given.
 // Work items are dealt XCD-major, so the column slabs of one row tile run on the same XCD at the
 // same time and share its rows of A in that XCD's L2.
+#include <type_traits>
+
 #include "tile_core.h"
 
 namespace moe {
@@ -274,6 +276,61 @@ __device__ __forceinline__ void run_tile(const Operands& o, int m_valid, int K, 
 #endif
 }
 
+// Output tiles leave through LDS so that global stores are whole 16-byte chunks of contiguous rows
+// (the MFMA layout would give 2-byte stores, 32 bytes per row per instruction).  After the K loop
+// the A ring is free; a bf16 tile of kCols columns is staged there, row r in stage r / kRowsPerStage,
+// and 16-byte chunk c of row r at position c ^ out_swz(r) (the four row groups one MFMA result
+// register spans land in different banks).
+__device__ __forceinline__ int out_swz(int r) { return ((r >> 2) & 3) << 1; }
+
+template <int kCols>
+struct OutTile {
+  static constexpr int kRowB = kCols * 2;                 // bytes per staged row
+  static constexpr int kRowsPerStage = kStageBytes / kRowB;
+  static constexpr int kChunks = kRowB / 16;              // 16-byte chunks per row
+  static_assert(kRowsPerStage % 16 == 0 && kRowsPerStage * kStages >= kTileM, "staging");
+
+  // Write one bf16 value of row r (tile-relative), column col (tile-relative).  i is the 16-row
+  // sub-tile of r, so the stage index is a compile-time constant.
+  template <int I>
+  __device__ static __forceinline__ void put(const Ring& ring, int r, int col, float v) {
+    char* st = ring.st[(16 * I) / kRowsPerStage];
+    *reinterpret_cast<uint16_t*>(st + (r % kRowsPerStage) * kRowB + (((col >> 3) ^ out_swz(r)) << 4) +
+                                 (col & 7) * 2) = f32_to_bf16(v);
+  }
+
+  // Store rows [0, m_valid) of the staged tile to out[(rbeg + r) * ld + col0 + c], columns below
+  // col_end only; every thread of the work-group takes part.
+  __device__ static __forceinline__ void store(const Ring& ring, int m_valid, uint16_t* out, int64_t ld,
+                                               int64_t rbeg, int col0, int col_end) {
+    constexpr int kPerThread = kRowsPerStage * kChunks / kThreads;
+    static_assert(kPerThread * kThreads == kRowsPerStage * kChunks, "chunks per thread");
+#pragma unroll
+    for (int st = 0; st < kStages; ++st) {
+      if (st * kRowsPerStage >= m_valid) break;
+#pragma unroll
+      for (int j = 0; j < kPerThread; ++j) {
+        const int ch = j * kThreads + threadIdx.x;
+        const int rl = ch / kChunks, c = ch % kChunks;
+        const int r = st * kRowsPerStage + rl;
+        if (r < m_valid && col0 + 8 * c < col_end) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(ring.st[st] + rl * kRowB + ((c ^ out_swz(r)) << 4));
+          *reinterpret_cast<u32x4*>(out + (rbeg + r) * ld + col0 + 8 * c) = v;
+        }
+      }
+    }
+  }
+};
+
+// Compile-time loop helper: f(integral_constant<int, I>) for I = 0 .. N-1.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(const F& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 // Lane offsets of the A loads: row rl of the tile is source row src(rl) of a [*, K] matrix.
 template <class RowOf>
 __device__ __forceinline__ void a_offsets(Operands& o, int K, RowOf row_of) {
@@ -311,17 +368,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   o.b_off = (uint32_t)((lane & 15) * H * 2 + 16 * (lane >> 4));
 
   uint16_t* h = static_cast<uint16_t*>(p.out);
-  const int64_t rbeg = t.rbeg, rend = t.rend;
-  run_tile(o, (int)(rend - rbeg), H, smem, [&](const auto& acc) {
+  const int64_t rbeg = t.rbeg;
+  const int m_valid = (int)(t.rend - t.rbeg);
+  run_tile(o, m_valid, H, smem, [&](const auto& acc) {
     constexpr int n16 = sizeof(acc) / sizeof(acc[0]);
+    using Out = OutTile<128>;
+    block_sync_lds();  // every wave is done reading the A ring
+    static_for<n16>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
 #pragma unroll
-    for (int i = 0; i < n16; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t r = rbeg + 16 * i + 4 * (lane >> 4) + e;
-        if (r >= rend) continue;
-        h[r * I + c0 + (lane & 15)] = f32_to_bf16(swiglu_f32(acc[i][0][e], acc[i][1][e]));
-      }
+      for (int e = 0; e < 4; ++e)
+        Out::put<i>(smem, 16 * i + 4 * (lane >> 4) + e, 16 * w + (lane & 15),
+                    swiglu_f32(acc[i][0][e], acc[i][1][e]));
+    });
+    block_sync_lds();
+    Out::store(smem, m_valid, h, I, rbeg, nt * 128, I);
   });
 }
 
@@ -350,12 +411,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   o.b_off = (uint32_t)((lane & 15) * I * 2 + 16 * (lane >> 4));
 
   const int64_t rbeg = t.rbeg, rend = t.rend;
+  const int m_valid = (int)(rend - rbeg);
   const float* row_scale = p.row_scale;
   void* out = p.out;
-  const bool out_bf16 = p.out_bf16 != 0;
-  run_tile(o, (int)(rend - rbeg), I, smem, [&](const auto& acc) {
-    if (!cols_ok) return;
+  run_tile(o, m_valid, I, smem, [&](const auto& acc) {
     constexpr int n16 = sizeof(acc) / sizeof(acc[0]);
+    if (p.out_bf16) {
+      using Out = OutTile<256>;
+      block_sync_lds();  // every wave is done reading the A ring
+      static_for<n16>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * i + 4 * (lane >> 4) + e;
+          const float sc = row_scale && r < m_valid ? row_scale[rbeg + r] : 1.f;
+#pragma unroll
+          for (int s = 0; s < kNSub; ++s) Out::put<i>(smem, r, 32 * w + 16 * s + (lane & 15), acc[i][s][e] * sc);
+        }
+      });
+      block_sync_lds();
+      Out::store(smem, m_valid, static_cast<uint16_t*>(out), H, rbeg, nt * 256, H);
+      return;
+    }
+    // fp32 rows (a caller's choice in moe_grouped_swiglu): direct stores
+    if (!cols_ok) return;
 #pragma unroll
     for (int i = 0; i < n16; ++i)
 #pragma unroll
@@ -364,14 +443,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         if (r >= rend) continue;
         const float sc = row_scale ? row_scale[r] : 1.f;
 #pragma unroll
-        for (int s = 0; s < kNSub; ++s) {
-          const int col = c0 + 16 * s + (lane & 15);
-          const float v = acc[i][s][e] * sc;
-          if (out_bf16)
-            static_cast<uint16_t*>(out)[r * H + col] = f32_to_bf16(v);
-          else
-            static_cast<float*>(out)[r * H + col] = v;
-        }
+        for (int s = 0; s < kNSub; ++s)
+          static_cast<float*>(out)[r * H + c0 + 16 * s + (lane & 15)] = acc[i][s][e] * sc;
       }
   });
 }
