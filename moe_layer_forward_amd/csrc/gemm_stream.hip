@@ -5,8 +5,9 @@
 // used once or twice, so the kernel is a weight stream: each weight byte crosses HBM once per pass
 // over the group's rows (one pass covers up to 32 rows).
 //
-// A wave owns 16 output columns of one group: 16 gate rows + the 16 matching up rows (gate/up) or 16
-// rows of W_down (down).  Its weight rows stream through a wave-private LDS ring with gfx950's direct
+// A wave streams two 16-row sets of weight rows of one group: the 16 gate rows and the 16 matching
+// up rows of 16 h columns (gate/up), or 32 rows of W_down, i.e. 32 output columns (down), so both
+// kernels issue the same mix of weight and token-row loads.  Its weight rows stream through a wave-private LDS ring with gfx950's direct
 // global -> LDS loads: one load instruction moves 4 rows x 256 contiguous bytes (whole cache lines)
 // with the streaming (non-temporal) policy -- measured on MI355X at ~7.0 TB/s, against ~6.2 TB/s for
 // 16-row x 64-byte register loads -- and kDepth K steps are in flight.  The 16 x 256-byte rows of a
@@ -17,8 +18,8 @@
 // The ring is private to the wave: no barriers.  Each ring stage is its own __shared__ array and the
 // K loop is unrolled by the stage count, so the compiler can tell which LDS reads depend on which
 // direct loads.
-// Work-groups = 4 waves = 64 columns of one group; groups come from the plan's active list, largest
-// first, so the long-running many-row groups start early.
+// Work-groups = 4 waves (64 h columns, or 128 output columns of down) of one group; groups come from
+// the plan's active list, largest first, so the long-running many-row groups start early.
 #include <type_traits>
 
 #include "kernels.h"
@@ -173,10 +174,9 @@ struct Stream {
 // One pass over the weights for rows [mb, mb + 16*NP) of the group (rows past r1 are computed from a
 // copy of row mb and never stored), then the epilogue.
 template <bool SWIGLU, int D, int NP>
-__device__ __forceinline__ void stream_pass(const StreamArgs& p, const Ring<SWIGLU ? 2 : 1, D>& ring,
-                                            const char* const (&wb)[SWIGLU ? 2 : 1], int n0, int64_t mb,
-                                            int64_t r1) {
-  constexpr int R = SWIGLU ? 2 : 1;
+__device__ __forceinline__ void stream_pass(const StreamArgs& p, const Ring<2, D>& ring, const char* const (&wb)[2],
+                                            int n0, int64_t mb, int64_t r1) {
+  constexpr int R = 2;
   const int H = p.H, I = p.I, K = SWIGLU ? H : I;
   const int lane = threadIdx.x & 63;
   // wave-uniform, so the LDS destinations of the direct loads stay visibly inside their stage array
@@ -216,18 +216,22 @@ __device__ __forceinline__ void stream_pass(const StreamArgs& p, const Ring<SWIG
       if (SWIGLU) {
         static_cast<uint16_t*>(p.out)[row * I + col] = f32_to_bf16(swiglu_f32(acc[q][0][e], acc[q][1][e]));
       } else {
-        const float v = acc[q][0][e] * (p.row_scale ? p.row_scale[row] : 1.f);
-        if (p.out_bf16)
-          static_cast<uint16_t*>(p.out)[row * H + col] = f32_to_bf16(v);
-        else
-          static_cast<float*>(p.out)[row * H + col] = v;
+        const float sc = p.row_scale ? p.row_scale[row] : 1.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {  // set r covers output columns n0 + 16r ..
+          const float v = acc[q][r][e] * sc;
+          if (p.out_bf16)
+            static_cast<uint16_t*>(p.out)[row * H + col + 16 * r] = f32_to_bf16(v);
+          else
+            static_cast<float*>(p.out)[row * H + col + 16 * r] = v;
+        }
       }
     }
 }
 
 template <bool SWIGLU, int D>
 __global__ __launch_bounds__(256) void stream_kernel(StreamArgs p) {
-  constexpr int R = SWIGLU ? 2 : 1;
+  constexpr int R = 2;
   constexpr int kStage = Ring<R, D>::kStageBytes;
   __shared__ __align__(16) char s0[kStage], s1[kStage], s2[D == 4 ? kStage : 16], s3[D == 4 ? kStage : 16];
   Ring<R, D> ring;
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(256) void stream_kernel(StreamArgs p) {
   if (r1 > p.max_rows) r1 = p.max_rows;
   const int H = p.H, I = p.I;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = nb * 64 + wave * 16;  // first output column of this wave
+  const int n0 = nb * (SWIGLU ? 64 : 128) + wave * (SWIGLU ? 16 : 32);  // first output column of this wave
   const bool sh = g == p.w.shared_group;
 
   const char* wb[R];
@@ -261,6 +265,7 @@ __global__ __launch_bounds__(256) void stream_kernel(StreamArgs p) {
   } else {
     const uint16_t* wd = sh ? (const uint16_t*)p.w.s_down : (const uint16_t*)p.w.down + (int64_t)g * H * I;
     wb[0] = reinterpret_cast<const char*>(wd + (int64_t)n0 * I);
+    wb[1] = reinterpret_cast<const char*>(wd + (int64_t)(n0 + 16) * I);
   }
   // Passes of 32 rows (two 16-row MFMA row blocks).  A single-block variant for groups of at most
   // 16 rows would save the second block's token-row loads and MFMAs, but its K loop gets a full
@@ -276,7 +281,7 @@ __global__ __launch_bounds__(256) void stream_kernel(StreamArgs p) {
 }
 
 constexpr int kDepthGateUp = 4;  // 4 x 32 KiB of LDS: one work-group per CU
-constexpr int kDepthDown = 4;    // 4 x 16 KiB: two work-groups per CU
+constexpr int kDepthDown = 4;    // 4 x 32 KiB: one work-group per CU
 
 }  // namespace
 
@@ -291,7 +296,7 @@ hipError_t launch_gateup_stream_bf16(const Groups& g, const Weights& w, const ui
 hipError_t launch_down_stream_bf16(const Groups& g, const Weights& w, const uint16_t* h, void* y_rows, bool y_bf16,
                                    const float* row_scale, int H, int I, hipStream_t s) {
   StreamArgs p{g.group_offsets, nullptr, g.active, g.counters, g.max_rows, w, h, y_rows, y_bf16 ? 1 : 0, row_scale,
-               H, I, H / 64};
+               H, I, H / 128};
   const int64_t blocks = (int64_t)g.n_groups * p.n_nblk;
   stream_kernel<false, kDepthDown><<<(unsigned)blocks, 256, 0, s>>>(p);
   return hipGetLastError();
