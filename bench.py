@@ -133,7 +133,7 @@ def layer_work(w, n_touched):
     n_exp = n_touched + w.n_shared
     bytes_ = n_exp * 3 * w.H * w.I * eb + 2 * w.T * w.H * eb
     flops = (w.T * w.K + w.T * w.n_shared) * 2 * 3 * w.H * w.I
-    if w.routing != "preassigned":
+    if w.routing not in ("preassigned", "dense"):
         bytes_ += w.E * w.H * eb
         flops += 2 * w.T * w.E * w.H
     return bytes_, flops
@@ -150,7 +150,15 @@ def run(w, weights, steps, warmup):
     cfg = moe.config_for(w)
     T = w.T
     y = torch.empty((T, w.H), dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32, device="cuda")
-    if w.routing == "preassigned":
+    if w.routing == "dense":
+        # the dense first-layer FFN: one group of all T rows on the grouped-SwiGLU kernels
+        ws = moe.alloc_workspace(cfg, moe.MOE_OP_GROUPED_SWIGLU, T, 1)
+        offs = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+
+        def step():
+            moe.moe_grouped_swiglu(cfg, offs, T, acts["x"], weights["w_gate"], weights["w_up"], weights["w_down"],
+                                   y_dtype=moe.MOE_BF16, workspace=ws, out=y)
+    elif w.routing == "preassigned":
         ws = moe.alloc_workspace(cfg, moe.MOE_OP_FORWARD_ROUTED, T)
         wg, wu, wd = (weights[k][:w.E] for k in ("w_gate", "w_up", "w_down"))
 
@@ -196,11 +204,14 @@ def run(w, weights, steps, warmup):
     ms = (t1 - t0) * 1e3 / steps
 
     # routing actually realised (counts touched experts for the byte accounting)
-    if w.routing == "preassigned":
-        ids = acts["topk_ids"]
+    if w.routing == "dense":
+        counts = np.array([T])
     else:
-        ids, _ = moe.moe_route(cfg, acts["x"], weights["w_router"], logit_offset=acts.get("logit_offset"))
-    counts = np.bincount(ids.cpu().numpy().ravel(), minlength=w.E)
+        if w.routing == "preassigned":
+            ids = acts["topk_ids"]
+        else:
+            ids, _ = moe.moe_route(cfg, acts["x"], weights["w_router"], logit_offset=acts.get("logit_offset"))
+        counts = np.bincount(ids.cpu().numpy().ravel(), minlength=w.E)
     n_touched = int((counts > 0).sum())
     rows = T * w.K + T * w.n_shared
     lb, lf = layer_work(w, n_touched)
@@ -326,12 +337,13 @@ def main():
         return profile_summary(sys.argv[2])
     if len(sys.argv) >= 2 and sys.argv[1] == "--traffic-summary":
         return traffic_summary(*sys.argv[2:5])
+    from moe_layer_forward_amd import workloads as wl
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skew", "ep_share", "tiny"])
-    ap.add_argument("--also", default="prefill,skew,ep_share",
+    ap.add_argument("--workload", default="decode", choices=list(wl.WORKLOADS))
+    ap.add_argument("--also", default="prefill,skew,ep_share,dense_decode,dense_prefill",
                     help="comma-separated workloads measured in the same run and reported beside it ('none')")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="first run one copy of known size (the traffic summary's counter calibration)")
@@ -343,8 +355,6 @@ def main():
         sys.exit(2)
 
     import torch
-
-    from moe_layer_forward_amd import workloads as wl
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -359,9 +369,11 @@ def main():
     weights_cache = {}
 
     def weights_for(w):
-        key = (w.w_seed, w.dtype, w.H, w.I, w.E if w.w_seed != 100 else 384)
+        # the four full-size MoE workloads share one weight set; the dense workloads share another
+        shared_moe = w.w_seed == 100 and w.routing != "dense"
+        key = (w.w_seed, w.routing == "dense", w.dtype, w.H, w.I, 384 if shared_moe else w.E)
         if key not in weights_cache:
-            src = wl.WORKLOADS["decode"] if w.w_seed == 100 else w
+            src = wl.WORKLOADS["decode"] if shared_moe else w
             log(f"generating weights for {src.name} ...")
             weights_cache[key] = wl.device_weights(src)
             torch.cuda.synchronize()

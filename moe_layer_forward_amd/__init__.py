@@ -198,6 +198,10 @@ def moe_combine(cfg, y_rows, pair_row, topk_weights, y_shared=None, out=None):
     import torch
 
     T = pair_row.shape[0]
+    if y_shared is not None and (y_shared.shape[0] < T or y_shared.shape[-1] != cfg.hidden_size):
+        raise ValueError(f"y_shared must be [T={T}, H={cfg.hidden_size}], got {tuple(y_shared.shape)}")
+    if y_rows.shape[-1] != cfg.hidden_size:
+        raise ValueError(f"y_rows must have H={cfg.hidden_size} columns, got {tuple(y_rows.shape)}")
     ydt = MOE_BF16 if y_rows.dtype == torch.bfloat16 else MOE_F32
     dev, stream = _dev(y_rows, pair_row, topk_weights, y_shared)
     y = out if out is not None else torch.empty((T, cfg.hidden_size), dtype=_elem(cfg), device=dev)

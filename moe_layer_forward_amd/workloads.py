@@ -10,10 +10,15 @@ decode         64  7168  2048  384   8  bf16    sigmoid router
 prefill      8192  7168  2048  384   8  bf16    sigmoid router (near-uniform)
 skew         4096  7168  2048  384   8  bf16    router + Zipf-shaped logit offsets
 ep_share    16384  7168  2048    3   1  bf16    pre-dispatched ids/weights, no router
+dense_*     64 /   7168 18432    1   1  bf16    none: the dense SwiGLU FFN of the
+            8192                                 model's first layer, all tokens
 ==========  =====  ====  ====  ===  ==  ======  ==================================
 
-Each has one always-on shared expert of the routed experts' shape and the
-routed scaling factor 2.827.
+
+Each MoE workload has one always-on shared expert of the routed experts'
+shape and the routed scaling factor 2.827.  The dense workloads are the
+7168 -> 18432 -> 7168 SwiGLU FFN of layer 0 (no router, no experts): one
+group of all T rows on the grouped-SwiGLU kernels, weight 1.
 
 Distributions: activations N(0, 1); router weight N(0, 0.02); gate/up
 N(0, 1/sqrt(H)); down N(0, 1/sqrt(I)) -- "N(0, a)" reads a as a standard
@@ -22,8 +27,9 @@ deviation.  Draws are Irwin-Hall(8) approximately-normal variates (see
 their activations use the workload number (2..5) as seed; tiny uses seed 1.
 
 Synthetic streams: 0 activations, 1 router, 2 gate, 3 up, 4 down, 5/6/7 shared
-gate/up/down (Philox, index = expert id); 8 skew permutation, 9 EP-share ids,
-10 EP-share weights (numpy PCG64 from SeedSequence([seed, stream])).
+gate/up/down, 11/12/13 dense gate/up/down (Philox, index = expert id); 8 skew
+permutation, 9 EP-share ids, 10 EP-share weights (numpy PCG64 from
+SeedSequence([seed, stream])).
 
 Skew offsets: o_e = -1.1 * ln(r_e) added to expert e's logit before the
 sigmoid, r a seeded permutation of 1..E -- a Zipf(s = 1.1)-shaped popularity
@@ -44,6 +50,8 @@ RSF_K2 = 2.827
 
 S_X, S_ROUTER, S_GATE, S_UP, S_DOWN, S_SGATE, S_SUP, S_SDOWN = range(8)
 S_SKEW, S_EP_IDS, S_EP_W = 8, 9, 10
+S_DGATE, S_DUP, S_DDOWN = 11, 12, 13
+DENSE_I = 18432  # intermediate size of the dense first-layer FFN
 
 
 @dataclass(frozen=True)
@@ -57,7 +65,7 @@ class Workload:
     dtype: str                    # 'bf16' | 'f32'
     x_seed: int
     w_seed: int
-    routing: str = "router"       # 'router' | 'skew' | 'preassigned'
+    routing: str = "router"       # 'router' | 'skew' | 'preassigned' | 'dense'
     n_shared: int = 1
     rsf: float = RSF_K2
     sigma_x: float = 1.0
@@ -88,6 +96,10 @@ WORKLOADS = {
     "skew": Workload("skew", 4096, 7168, 2048, 384, 8, "bf16", x_seed=4, w_seed=100, routing="skew"),
     "ep_share": Workload("ep_share", 16384, 7168, 2048, 3, 1, "bf16", x_seed=5, w_seed=100,
                          routing="preassigned"),
+    "dense_decode": Workload("dense_decode", 64, 7168, DENSE_I, 1, 1, "bf16", x_seed=6, w_seed=100,
+                             routing="dense", n_shared=0),
+    "dense_prefill": Workload("dense_prefill", 8192, 7168, DENSE_I, 1, 1, "bf16", x_seed=7, w_seed=100,
+                              routing="dense", n_shared=0),
 }
 
 
@@ -134,11 +146,16 @@ def host_router(w: Workload) -> np.ndarray:
     return _to_f64(synth.host_tensor(w.w_seed, S_ROUTER, 0, (w.E, w.H), w.sigma_router, w.dtype), w.dtype)
 
 
+def _expert_streams(w: Workload):
+    return (S_DGATE, S_DUP, S_DDOWN) if w.routing == "dense" else (S_GATE, S_UP, S_DOWN)
+
+
 def host_expert(w: Workload, e: int):
-    """(W_gate [I,H], W_up [I,H], W_down [H,I]) of routed expert e, float64."""
-    g = synth.host_tensor(w.w_seed, S_GATE, e, (w.I, w.H), w.sigma_gate_up, w.dtype)
-    u = synth.host_tensor(w.w_seed, S_UP, e, (w.I, w.H), w.sigma_gate_up, w.dtype)
-    d = synth.host_tensor(w.w_seed, S_DOWN, e, (w.H, w.I), w.sigma_down, w.dtype)
+    """(W_gate [I,H], W_up [I,H], W_down [H,I]) of routed expert e (the dense FFN for 'dense'), float64."""
+    sg, su, sd = _expert_streams(w)
+    g = synth.host_tensor(w.w_seed, sg, e, (w.I, w.H), w.sigma_gate_up, w.dtype)
+    u = synth.host_tensor(w.w_seed, su, e, (w.I, w.H), w.sigma_gate_up, w.dtype)
+    d = synth.host_tensor(w.w_seed, sd, e, (w.H, w.I), w.sigma_down, w.dtype)
     return _to_f64(g, w.dtype), _to_f64(u, w.dtype), _to_f64(d, w.dtype)
 
 
@@ -153,19 +170,21 @@ def host_shared(w: Workload):
 
 # --------------------------------------------------------------------------- device side
 def device_weights(w: Workload, device="cuda"):
-    """Router, routed-expert and shared-expert weights of the workload, generated in HBM."""
+    """Router, routed-expert and shared-expert weights of the workload (the dense FFN as expert 0 for
+    'dense'), generated in HBM."""
     import torch
 
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     t = {}
-    if w.routing != "preassigned":
+    if w.routing not in ("preassigned", "dense"):
         t["w_router"] = synth.device_fill(torch.empty((w.E, w.H), dtype=dt, device=device), w.w_seed, S_ROUTER,
                                           0, 1, w.E * w.H, w.sigma_router)
-    t["w_gate"] = synth.device_fill(torch.empty((w.E, w.I, w.H), dtype=dt, device=device), w.w_seed, S_GATE, 0,
+    sg, su, sd = _expert_streams(w)
+    t["w_gate"] = synth.device_fill(torch.empty((w.E, w.I, w.H), dtype=dt, device=device), w.w_seed, sg, 0,
                                     w.E, w.I * w.H, w.sigma_gate_up)
-    t["w_up"] = synth.device_fill(torch.empty((w.E, w.I, w.H), dtype=dt, device=device), w.w_seed, S_UP, 0,
+    t["w_up"] = synth.device_fill(torch.empty((w.E, w.I, w.H), dtype=dt, device=device), w.w_seed, su, 0,
                                   w.E, w.I * w.H, w.sigma_gate_up)
-    t["w_down"] = synth.device_fill(torch.empty((w.E, w.H, w.I), dtype=dt, device=device), w.w_seed, S_DOWN, 0,
+    t["w_down"] = synth.device_fill(torch.empty((w.E, w.H, w.I), dtype=dt, device=device), w.w_seed, sd, 0,
                                     w.E, w.H * w.I, w.sigma_down)
     if w.n_shared:
         t["ws_gate"] = synth.device_fill(torch.empty((w.I, w.H), dtype=dt, device=device), w.w_seed, S_SGATE, 0,

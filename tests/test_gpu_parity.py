@@ -152,6 +152,41 @@ def test_ep_share_full_size(k2_weights):
     assert err.max() <= Y_TOL["bf16"]
 
 
+# ----------------------------------------------------------------- the dense first-layer FFN
+def _dense(w, t):
+    """The dense SwiGLU FFN on the grouped kernels: one group of all T rows, weight 1."""
+    torch = _torch()
+    offs = torch.tensor([0, w.T], dtype=torch.int32, device="cuda")
+    y = moe.moe_grouped_swiglu(moe.config_for(w), offs, w.T, t["x"], t["w_gate"], t["w_up"], t["w_down"],
+                               y_dtype=moe.MOE_BF16)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("T", [3, 200], ids=["stream_kernels", "tile_kernels"])
+def test_dense_ffn_every_token(T):
+    _torch()
+    w = wl.custom("dense_small", T=T, H=512, I=1152, E=1, K=1, routing="dense", n_shared=0)
+    t = wl.device_inputs(w)
+    y = _dense(w, t)
+    err = rel_l2(to_np(y), oracle.swiglu_expert(wl.host_x(w), *wl.host_expert(w, 0)))
+    print(f"dense T={T}: max rel L2 {err.max():.3g}", flush=True)
+    assert err.max() <= Y_TOL["bf16"]
+
+
+@pytest.mark.parametrize("name,tokens", [("dense_decode", [0, 31, 63]), ("dense_prefill", [0, 4097, 8191])])
+def test_dense_full_size(name, tokens):
+    _torch()
+    w = wl.WORKLOADS[name]
+    t = wl.device_inputs(w)
+    y = _dense(w, t)
+    y_ref = oracle.swiglu_expert(wl.host_x_rows(w, tokens), *wl.host_expert(w, 0))
+    err = rel_l2(to_np(y)[tokens], y_ref)
+    print(f"{name}: T={w.T} checked {len(tokens)} tokens, max rel L2 {err.max():.3g}", flush=True)
+    assert err.max() <= Y_TOL["bf16"]
+    assert np.isfinite(to_np(y)).all()
+
+
 # ----------------------------------------------------------------- the individual calls
 def test_route_call():
     torch = _torch()
@@ -188,12 +223,12 @@ def test_permute_call_integer_exact():
 
 
 @pytest.mark.parametrize("y_bf16", [False, True])
-def test_grouped_swiglu_and_combine_calls(y_bf16):
+@pytest.mark.parametrize("sizes", [[30, 0, 55, 0, 95], [3, 0, 5, 1, 0]], ids=["tile_kernels", "stream_kernels"])
+def test_grouped_swiglu_and_combine_calls(y_bf16, sizes):
     torch = _torch()
     w = wl.custom("gs", T=90, H=256, I=384, E=5, K=2)
     t = wl.device_inputs(w)
     # groups with 0 rows in the middle and at the end; rows gathered through row_index
-    sizes = [30, 0, 55, 0, 95]
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
     rows = int(off[-1])
     row_index = np.random.default_rng(1).integers(0, w.T, size=rows).astype(np.int32)
@@ -213,8 +248,8 @@ def test_grouped_swiglu_and_combine_calls(y_bf16):
     err = rel_l2(to_np(y_rows), ref)
     assert err.max() <= Y_TOL["bf16"]
 
-    # combine: token t takes rows pair_row[t, :] with weights, plus a shared row block
-    T, K = 40, 3
+    # combine: token t takes rows pair_row[t, :] with weights, plus a shared row block (rows 0..T-1)
+    T, K = min(40, rows), 3
     r = np.random.default_rng(4)
     pair_row = np.stack([r.choice(rows, size=K, replace=False) for _ in range(T)]).astype(np.int32)
     wts = r.uniform(0.1, 1.0, size=(T, K)).astype(np.float32)

@@ -83,3 +83,12 @@ def test_device_generator_matches_host():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(tf["w_router"].cpu().numpy(),
                                   synth.host_tensor(1, wl.S_ROUTER, 0, (16, 256), 0.02, "f32"))
+
+
+def test_dense_workload_draws_its_own_weights():
+    """The dense first-layer FFN uses its own weight streams, not routed expert 0's."""
+    d = wl.custom("d", T=2, H=128, I=256, E=1, K=1, routing="dense", n_shared=0)
+    m = wl.custom("m", T=2, H=128, I=256, E=1, K=1)
+    for a, b in zip(wl.host_expert(d, 0), wl.host_expert(m, 0)):
+        assert a.shape == b.shape and not np.array_equal(a, b)
+    assert wl.WORKLOADS["dense_decode"].I == 18432 and wl.WORKLOADS["dense_prefill"].T == 8192
