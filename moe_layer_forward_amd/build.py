@@ -45,7 +45,7 @@ def _run(cmd, verbose):
 def build_synth_host(verbose=False):
     out = os.path.join(SYNTH, "libsynth_host.so")
     _run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-o", out,
-          os.path.join(SYNTH, "synth_host.c")], verbose)
+          os.path.join(SYNTH, "synth_host.c"), "-lm"], verbose)
     return out
 
 

@@ -56,6 +56,8 @@ def _host_lib():
             fn = getattr(lib, name)
             fn.argtypes = [u32, u32, u32, i64, vp, i64, f32, vp]
             fn.restype = None
+        lib.synth_quantize_q4.argtypes = [vp, i64, vp, vp]
+        lib.synth_quantize_q4.restype = None
         _host = lib
     return _host
 
@@ -72,6 +74,9 @@ def _dev_lib():
                                        ctypes.c_uint32, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
                                        ctypes.c_void_p]
         lib.synth_dev_fill.restype = ctypes.c_int
+        lib.synth_dev_quantize_q4.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p]
+        lib.synth_dev_quantize_q4.restype = ctypes.c_int
         _dev = lib
     return _dev
 
@@ -145,3 +150,39 @@ def device_fill(tensor, seed: int, stream: int, index0: int, n_index: int, per_i
     if rc != 0:
         raise RuntimeError(f"synth_dev_fill failed with status {rc}")
     return tensor
+
+
+# --------------------------------------------------------------------------- 4-bit weight storage
+# Input preparation (an offline checkpoint conversion), identical on host and device: per group of 32
+# consecutive inputs of a row, s = f16(max|w| / 7), q = clamp(rint(w / s), -8, 7); codes 8 per
+# uint32 (input k at bits 4*(k % 8), two's complement), scales as f16 bits.
+
+def host_quantize_q4(w_bits: np.ndarray):
+    """bf16 bits [rows, cols] (cols % 32 == 0) -> (codes uint32 [rows, cols/8], scales uint16 [rows, cols/32])."""
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    rows, cols = w.shape
+    if cols % 32:
+        raise ValueError("cols must be a multiple of 32")
+    codes = np.empty((rows, cols // 8), dtype=np.uint32)
+    scales = np.empty((rows, cols // 32), dtype=np.uint16)
+    _host_lib().synth_quantize_q4(w.ctypes.data, rows * cols // 32, codes.ctypes.data, scales.ctypes.data)
+    return codes, scales
+
+
+def device_quantize_q4(w, codes, scales):
+    """bf16 tensor [..., cols] -> fills int32 codes [..., cols/8] and 16-bit scales [..., cols/32] on the GPU."""
+    import torch
+
+    for t in (w, codes, scales):
+        if not t.is_contiguous():
+            raise ValueError("device_quantize_q4: tensors must be contiguous")
+    if w.dtype != torch.bfloat16 or codes.dtype != torch.int32 or scales.element_size() != 2:
+        raise ValueError("device_quantize_q4: w bf16, codes int32, scales 16-bit")
+    n_groups = w.numel() // 32
+    if w.numel() % 32 or codes.numel() != n_groups * 4 or scales.numel() != n_groups:
+        raise ValueError("device_quantize_q4: shapes do not match")
+    rc = _dev_lib().synth_dev_quantize_q4(w.data_ptr(), n_groups, codes.data_ptr(), scales.data_ptr(),
+                                          torch.cuda.current_stream().cuda_stream)
+    if rc:
+        raise RuntimeError(f"synth_dev_quantize_q4 failed ({rc})")
+    return codes, scales

@@ -11,6 +11,11 @@
 //   counter = (e lo32, e hi32, index, 0), key = (seed, stream)
 //   d = sum of the eight 16-bit halves of the four output words
 //   value = fl32((float)(2*d - 524280) * scale), bf16 by round-to-nearest-even.
+//
+// 4-bit weight storage (synth_dev_quantize_q4), input preparation like an offline checkpoint
+// conversion, the same fp32 operations as the host twin: per group of 32 consecutive inputs,
+//   s = f16_rne(max|w| / 7), q = clamp(rint(w / s), -8, 7) (0 when s == 0),
+// codes 8 per 32-bit word (input k at bits 4*(k % 8), two's complement), scales as f16 bits.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -65,7 +70,49 @@ __global__ void synth_fill_kernel(void* __restrict__ out, uint32_t seed, uint32_
   }
 }
 
+// One group of 32 bf16 weights per thread; groups are consecutive in memory.
+__global__ void synth_quantize_q4_kernel(const uint16_t* __restrict__ w, int64_t n_groups,
+                                         uint32_t* __restrict__ codes, uint16_t* __restrict__ scales) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < n_groups; gi += stride) {
+    float v[32], amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      v[k] = __uint_as_float((uint32_t)w[gi * 32 + k] << 16);
+      amax = fmaxf(amax, fabsf(v[k]));
+    }
+    const _Float16 s16 = (_Float16)__fdiv_rn(amax, 7.0f);
+    const float s = (float)s16;
+    scales[gi] = __builtin_bit_cast(uint16_t, s16);
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int q = 0;
+        if (s > 0.f) {
+          const float t = __builtin_rintf(__fdiv_rn(v[8 * wd + i], s));
+          q = t > 7.f ? 7 : (t < -8.f ? -8 : (int)t);
+        }
+        word |= ((uint32_t)q & 0xfu) << (4 * i);
+      }
+      codes[gi * 4 + wd] = word;
+    }
+  }
+}
+
 }  // namespace
+
+extern "C" int synth_dev_quantize_q4(const void* w, int64_t n_groups, void* codes, void* scales,
+                                     void* hip_stream) {
+  if (!w || !codes || !scales || n_groups < 0) return 1;
+  if (n_groups == 0) return 0;
+  int64_t blocks = (n_groups + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  synth_quantize_q4_kernel<<<(unsigned)blocks, 256, 0, static_cast<hipStream_t>(hip_stream)>>>(
+      static_cast<const uint16_t*>(w), n_groups, static_cast<uint32_t*>(codes), static_cast<uint16_t*>(scales));
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
 
 extern "C" int synth_dev_fill(void* out, int32_t is_bf16, uint32_t seed, uint32_t stream,
                               uint32_t index0, int64_t n_index, int64_t per_index, float scale,

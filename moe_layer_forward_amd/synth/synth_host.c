@@ -26,7 +26,17 @@
  * support +-4.9 sigma; it uses only exact integer arithmetic plus one IEEE
  * multiply, so host and device agree bit for bit.  bf16 output rounds the
  * fp32 value to nearest-even.
+ *
+ * 4-bit weight storage (synth_quantize_q4) prepares quantized copies of bf16
+ * weights, the way a checkpoint is prepared offline; it is input preparation,
+ * and its device twin computes the same fp32 operations:
+ *   per group of 32 consecutive inputs of a row,
+ *     s = f16_rne(max|w| / 7)                 (one IEEE division, then f32->f16)
+ *     q = clamp(rint(w / s), -8, 7)           (q = 0 when s == 0)
+ *   codes: 8 per 32-bit word, input k of the row in bits 4*(k % 8) of word k / 8,
+ *          as 4-bit two's complement; scales: f16 bits, one per group.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stddef.h>
 
@@ -102,4 +112,70 @@ void synth_fill_rows_f32(uint32_t seed, uint32_t stream, uint32_t index, int64_t
   for (int64_t j = 0; j < n_rows; ++j)
     for (int64_t c = 0; c < cols; ++c)
       out[j * cols + c] = synth_value(seed, stream, index, (uint64_t)(row_ids[j] * cols + c), scale);
+}
+
+/* IEEE binary32 -> binary16, round to nearest even (overflow to infinity). */
+static inline uint16_t f32_to_f16_rne(float f) {
+  union { float f; uint32_t u; } v;
+  v.f = f;
+  const uint32_t sign = (v.u >> 16) & 0x8000u, a = v.u & 0x7fffffffu;
+  if (a >= 0x7f800000u) return (uint16_t)(sign | (a > 0x7f800000u ? 0x7e00u : 0x7c00u));
+  if (a >= 0x477ff000u) return (uint16_t)(sign | 0x7c00u);      /* >= 65520 rounds to infinity */
+  if (a >= 0x38800000u) {                                       /* normal binary16 */
+    uint32_t m = a - 0x38000000u;                               /* exponent bias 127 -> 15 */
+    m += 0x0fffu + ((m >> 13) & 1u);
+    return (uint16_t)(sign | (m >> 13));
+  }
+  const uint32_t e = a >> 23;                                   /* subnormal binary16 or zero */
+  if (e < 102) return (uint16_t)sign;                           /* below half the smallest step */
+  const uint32_t mant = (a & 0x7fffffu) | 0x800000u;
+  const uint32_t shift = 126u - e;                              /* value * 2^24 = mant >> shift */
+  uint32_t n = mant >> shift;
+  const uint32_t rem = mant & ((1u << shift) - 1u), half = 1u << (shift - 1u);
+  if (rem > half || (rem == half && (n & 1u))) ++n;
+  return (uint16_t)(sign | n);
+}
+
+static inline float f16_to_f32(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h & 0x8000u) << 16, e = (h >> 10) & 0x1fu, m = h & 0x3ffu;
+  union { float f; uint32_t u; } v;
+  if (e == 0x1f) {
+    v.u = sign | 0x7f800000u | (m << 13);
+  } else if (e) {
+    v.u = sign | ((e + 112u) << 23) | (m << 13);
+  } else {
+    v.f = (float)m * 5.9604644775390625e-08f;                   /* m * 2^-24, exact */
+    v.u |= sign;
+  }
+  return v.f;
+}
+
+/* w: [rows, cols] bf16 bits, cols a multiple of 32 -> codes [rows, cols/8], scales [rows, cols/32]. */
+void synth_quantize_q4(const uint16_t *w, int64_t n_groups, uint32_t *codes, uint16_t *scales) {
+#pragma omp parallel for schedule(static)
+  for (int64_t gi = 0; gi < n_groups; ++gi) {
+    float v[32], amax = 0.f;
+    for (int k = 0; k < 32; ++k) {
+      union { uint32_t u; float f; } b;
+      b.u = (uint32_t)w[gi * 32 + k] << 16;
+      v[k] = b.f;
+      const float av = fabsf(v[k]);
+      if (av > amax) amax = av;
+    }
+    const uint16_t s16 = f32_to_f16_rne(amax / 7.0f);
+    const float s = f16_to_f32(s16);
+    scales[gi] = s16;
+    for (int wd = 0; wd < 4; ++wd) {
+      uint32_t word = 0;
+      for (int i = 0; i < 8; ++i) {
+        int q = 0;
+        if (s > 0.f) {
+          const float t = rintf(v[8 * wd + i] / s);
+          q = t > 7.f ? 7 : (t < -8.f ? -8 : (int)t);
+        }
+        word |= ((uint32_t)q & 0xfu) << (4 * i);
+      }
+      codes[gi * 4 + wd] = word;
+    }
+  }
 }

@@ -42,6 +42,13 @@ Readings where the pages are silent or garbled:
   type-check and is read as that sum.
 * No epsilon in the normalisation (sigmoid scores are > 0).
 * Selected ids are listed by key descending, then id ascending.
+
+4-bit routed experts ([DEEP] §7.2: "pack-quantized", num_bits 4, strategy group, group_size 32,
+symmetric, int; the shared expert and the dense MLP stay BF16): an expert weight is w = q * s, q a
+signed 4-bit integer, s one scale per group of 32 consecutive inputs of an output row.  Readings
+where the page is silent: q is stored as 4-bit two's complement, 8 per 32-bit word, input k in bits
+4*(k % 8) of word k // 8; s is stored as IEEE binary16.  ``dequant_q4`` evaluates w exactly in
+float64; the layer is then the same function of the dequantized weights.
 """
 from __future__ import annotations
 
@@ -174,3 +181,24 @@ def moe_forward(x, w_router, expert, shared, top_k, rsf=RSF_K2, score_bias=None,
 def expert_param_count(hidden, intermediate):
     """Parameters of one SwiGLU expert: gate, up and down each hold H*I ([QA] Q2.1)."""
     return 3 * hidden * intermediate
+
+
+def dequant_q4(codes, scales):
+    """4-bit group-quantised weight -> float64 ([DEEP] §7.2; readings in the module header).
+
+    codes  uint32 [N, K/8]: q of input k in bits 4*(k % 8) of word k // 8, two's complement;
+    scales IEEE binary16 (as uint16 bits or float16) [N, K/32]: one per 32 consecutive inputs.
+    Returns w [N, K] = q * s.
+    """
+    codes = np.asarray(codes, dtype=np.uint32)
+    n, words = codes.shape
+    nib = (codes[:, :, None] >> (4 * np.arange(8, dtype=np.uint32))) & np.uint32(0xF)
+    q = nib.astype(np.int64)
+    q = np.where(q >= 8, q - 16, q).reshape(n, words * 8)
+    sc = np.asarray(scales)
+    if sc.dtype == np.uint16:
+        sc = sc.view(np.float16)
+    sc = sc.astype(np.float64)
+    if sc.shape != (n, words * 8 // 32):
+        raise ValueError("scales must be [N, K/32]")
+    return q * np.repeat(sc, 32, axis=1)

@@ -345,3 +345,46 @@ def test_real_shape_slice_invariants():
     # logits have the std the recipe implies: 0.02 * sqrt(7168) ~ 1.69
     lg = oracle.router_logits(wl.host_x_rows(w, np.arange(8)), wr)
     assert 1.3 < lg.std() < 2.1
+
+
+# ----------------------------------------------------------------- 4-bit routed experts
+def _golden_q4():
+    words, qs, scale_bits, scale = [], [], None, None
+    with open(os.path.join(GOLDEN, "q4_dequant.txt")) as fh:
+        for line in fh:
+            f = line.split()
+            if not f or f[0].startswith("#") or f[0] == "words":
+                continue
+            if f[0] == "scale":
+                scale_bits, scale = int(f[1], 16), float(f[2])
+            else:
+                words.append(int(f[0], 16))
+                qs.extend(int(v) for v in f[1:])
+    return np.array([words], dtype=np.uint32), np.array(qs), scale_bits, scale
+
+
+def test_q4_dequant_golden():
+    """Hand-worked decoding of packed 4-bit codes (tests/golden/q4_dequant.txt)."""
+    codes, qs, scale_bits, scale = _golden_q4()
+    w = oracle.dequant_q4(codes, np.array([[scale_bits]], dtype=np.uint16))
+    np.testing.assert_array_equal(w[0], qs * scale)
+
+
+def test_q4_quantizer_round_trip_bound():
+    """Input preparation and the oracle's decoding agree: |dequant(quant(w)) - w| <= s/2 for every weight,
+    the largest magnitude of a group is kept within s/2, and q stays in [-8, 7]."""
+    from moe_layer_forward_amd import synth
+
+    bits = synth.host_tensor(5, 3, 0, (64, 256), 0.02, "bf16")
+    w = synth.bf16_bits_to_f32(bits).astype(np.float64)
+    codes, scales = synth.host_quantize_q4(bits)
+    deq = oracle.dequant_q4(codes, scales)
+    s = np.repeat(scales.view(np.float16).astype(np.float64), 32, axis=1)
+    assert np.all(np.abs(deq - w) <= s / 2 + 1e-12)
+    amax = np.abs(w).reshape(64, 8, 32).max(axis=2)
+    dmax = np.abs(deq).reshape(64, 8, 32).max(axis=2)
+    assert np.all(np.abs(dmax - amax) <= scales.view(np.float16).astype(np.float64) / 2 + 1e-12)
+    assert np.all(np.abs(deq / np.where(s > 0, s, 1)) <= 8)
+    # a zero group stays zero
+    zc, zs = synth.host_quantize_q4(np.zeros((1, 32), dtype=np.uint16))
+    assert zs[0, 0] == 0 and zc.sum() == 0 and np.all(oracle.dequant_q4(zc, zs) == 0)
