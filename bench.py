@@ -47,7 +47,10 @@ KERNEL_SYMBOLS = {
     "down_tile": ("down_tile_kernel", ["gemm_tile.hip", "tile_core.h", "kernels.h"]),
     "router_logits": ("router_logits_kernel", ["route.hip", "tile_core.h", "kernels.h"]),
     "combine": ("combine_kernel", ["combine.hip", "kernels.h"]),
+    "gateup_q4": ("q4_stream_kernel<true", ["gemm_q4.hip", "tile_core.h", "kernels.h"]),
+    "down_q4": ("q4_stream_kernel<false", ["gemm_q4.hip", "tile_core.h", "kernels.h"]),
 }
+Q4_BYTES = 0.5 + 2 / 32    # bytes per 4-bit weight: the code plus its share of a binary16 scale per 32
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 CALIB_BYTES = 1 << 30      # the calibration copy reads and writes this many bytes
 CALIB_SYMBOL = "neg_kernel"
@@ -113,10 +116,23 @@ class HipEvents:
             self.hip.hipEventDestroy(self.ev[i])
 
 
-def kernel_work(name, w, n_groups_active, rows):
+def kernel_work(name, w, n_touched):
     """Algorithmic (bytes, flops) of one launch of a grouped GEMM kernel: the weights of every group
     with rows read once, the token rows / h read once, the outputs written once."""
     eb = 2 if w.dtype == "bf16" else 4
+    if name in ("gateup_q4", "down_q4"):
+        # routed experts with 4-bit weights (f16 token rows and h), plus the shared expert's bf16
+        # weights and rows in the same launch; y_rows bf16
+        rows = w.T * w.K + w.T * w.n_shared
+        if name == "gateup_q4":
+            wbytes = (n_touched * Q4_BYTES + w.n_shared * 2) * 2 * w.I * w.H
+            return wbytes + w.T * w.H * 2 * (1 + w.n_shared) + rows * w.I * 2, rows * 2 * 2 * w.I * w.H
+        wbytes = (n_touched * Q4_BYTES + w.n_shared * 2) * w.H * w.I
+        return wbytes + rows * w.I * 2 + rows * w.H * 2, rows * 2 * w.H * w.I
+    n_groups_active = n_touched + w.n_shared
+    rows = w.T * w.K + w.T * w.n_shared
+    if w.quant == "int4":  # the bf16 kernels run the shared expert alone
+        n_groups_active, rows = 1, w.T
     if name.startswith("gateup"):
         wbytes = n_groups_active * 2 * w.I * w.H * eb
         return wbytes + w.T * w.H * eb + rows * w.I * eb, rows * 2 * 2 * w.I * w.H
@@ -130,8 +146,8 @@ def layer_work(w, n_touched):
     """Algorithmic bytes and flops of the whole layer: every touched expert's and the shared expert's
     weights once, the router weight, x read and y written once."""
     eb = 2 if w.dtype == "bf16" else 4
-    n_exp = n_touched + w.n_shared
-    bytes_ = n_exp * 3 * w.H * w.I * eb + 2 * w.T * w.H * eb
+    routed_eb = Q4_BYTES if w.quant == "int4" else eb
+    bytes_ = (n_touched * routed_eb + w.n_shared * eb) * 3 * w.H * w.I + 2 * w.T * w.H * eb
     flops = (w.T * w.K + w.T * w.n_shared) * 2 * 3 * w.H * w.I
     if w.routing not in ("preassigned", "dense"):
         bytes_ += w.E * w.H * eb
@@ -165,6 +181,14 @@ def run(w, weights, steps, warmup):
         def step():
             moe.moe_forward_routed(cfg, acts["x"], acts["topk_ids"], acts["topk_weights"], wg, wu, wd,
                                    weights["ws_gate"], weights["ws_up"], weights["ws_down"], workspace=ws, out=y)
+    elif w.quant == "int4":
+        ws = moe.alloc_workspace(cfg, moe.MOE_OP_FORWARD_Q4, T)
+        q4 = {k: weights[k] for k in ("gate_codes", "gate_scales", "up_codes", "up_scales", "down_codes",
+                                      "down_scales")}
+
+        def step():
+            moe.moe_forward_q4(cfg, acts["x"], weights["w_router"], q4, weights["ws_gate"], weights["ws_up"],
+                               weights["ws_down"], logit_offset=acts.get("logit_offset"), workspace=ws, out=y)
     else:
         ws = moe.alloc_workspace(cfg, moe.MOE_OP_FORWARD, T)
 
@@ -213,10 +237,9 @@ def run(w, weights, steps, warmup):
             ids, _ = moe.moe_route(cfg, acts["x"], weights["w_router"], logit_offset=acts.get("logit_offset"))
         counts = np.bincount(ids.cpu().numpy().ravel(), minlength=w.E)
     n_touched = int((counts > 0).sum())
-    rows = T * w.K + T * w.n_shared
     lb, lf = layer_work(w, n_touched)
     dom = max(kern, key=kern.get)
-    kb, kf = kernel_work(dom, w, n_touched + w.n_shared, rows)
+    kb, kf = kernel_work(dom, w, n_touched)
     dom_s = kern[dom] * 1e-3
     peak_flops = BF16_PEAK if w.dtype == "bf16" else F32_PEAK
     if kb is not None and kf / kb < peak_flops / HBM_PEAK:
@@ -343,7 +366,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=list(wl.WORKLOADS))
-    ap.add_argument("--also", default="prefill,skew,ep_share,dense_decode,dense_prefill",
+    ap.add_argument("--also", default="prefill,skew,ep_share,dense_decode,dense_prefill,decode_int4",
                     help="comma-separated workloads measured in the same run and reported beside it ('none')")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="first run one copy of known size (the traffic summary's counter calibration)")
@@ -369,9 +392,10 @@ def main():
     weights_cache = {}
 
     def weights_for(w):
-        # the four full-size MoE workloads share one weight set; the dense workloads share another
-        shared_moe = w.w_seed == 100 and w.routing != "dense"
-        key = (w.w_seed, w.routing == "dense", w.dtype, w.H, w.I, 384 if shared_moe else w.E)
+        # the four full-size MoE workloads share one weight set; the dense workloads share another;
+        # the 4-bit workload has its own (the same weights, quantized)
+        shared_moe = w.w_seed == 100 and w.routing != "dense" and w.quant == "none"
+        key = (w.w_seed, w.routing == "dense", w.dtype, w.H, w.I, 384 if shared_moe else w.E, w.quant)
         if key not in weights_cache:
             src = wl.WORKLOADS["decode"] if shared_moe else w
             log(f"generating weights for {src.name} ...")
@@ -395,7 +419,9 @@ def main():
         log(f"running {w2.name} ...")
         r2 = run(w2, weights_for(w2), args.steps, args.warmup)
         out[w2.name] = {"value": r2["tokens_per_s"], "unit": "tokens/s", "ms_per_step": r2["ms_per_step"],
-                        "config": {"workload": w2.name, "T": w2.T}, "roofline": r2["roofline"],
+                        "config": {"workload": w2.name, "T": w2.T},
+                        "dtype": "f16 x int4 (routed), bf16 (shared)" if w2.quant == "int4" else w2.dtype,
+                        "roofline": r2["roofline"],
                         "layer": r2["layer"], "kernels_us": r2["kernels_us"]}
     weights_cache.clear()
     torch.cuda.empty_cache()

@@ -5,7 +5,8 @@
  *   [DEEP]        "Kimi K2.5 模型架构深度拆解" (pillumina.github.io/posts/architecture/kimi-k2.5):
  *                 §4.2 routing, §4.3 expert FFN, §10.2 MoE data flow Steps 1-7.
  *   [QA]          "Kimi K2.5 架构 QA" (cctoctofx.netlify.app/posts/qa/kimi-k2.5-qa):
- *                 Q2.1 parameters, Q2.3 routed_scaling_factor, Q7.2 bias buffer, Q8.3 dispatch.
+ *                 Q2.1 parameters, Q2.3 routed_scaling_factor, Q7.1 quantized storage,
+ *                 Q7.2 bias buffer, Q8.3 dispatch.
  *   [ZH-INFRA]    Zhihu answer by a K2 inference engineer on the K2 config:
  *                 §2.1 num_experts = 384, §2.4 n_group = 1.
  *   [ZH-PRETRAIN] Zhihu answer by a K2 pretraining author, "架构 / 异": scaling factor 2.5 -> 2.827.
@@ -73,7 +74,8 @@ typedef enum {
   MOE_OP_GROUPED_SWIGLU = 2,
   MOE_OP_COMBINE = 3,
   MOE_OP_FORWARD = 4,
-  MOE_OP_FORWARD_ROUTED = 5
+  MOE_OP_FORWARD_ROUTED = 5,
+  MOE_OP_FORWARD_Q4 = 6
 } moe_op;
 
 /* The MoE config fields of the K2 layer ([DEEP] §4.2-§4.3; [ZH-INFRA] §2.4). Host struct. */
@@ -91,8 +93,8 @@ typedef struct moe_config {
 } moe_config;
 
 /* Bytes of workspace the call `op` needs.
- *   MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_COMBINE, MOE_OP_FORWARD, MOE_OP_FORWARD_ROUTED:
- *       rows = T (tokens), n_groups ignored.
+ *   MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_COMBINE, MOE_OP_FORWARD, MOE_OP_FORWARD_ROUTED,
+ *   MOE_OP_FORWARD_Q4: rows = T (tokens), n_groups ignored.
  *   MOE_OP_GROUPED_SWIGLU: rows = max_rows, n_groups = number of groups.
  * Returns 0 for an invalid config (see moe_last_error()). */
 size_t moe_workspace_size(const moe_config* cfg, int32_t op, int64_t rows, int32_t n_groups);
@@ -174,6 +176,32 @@ int moe_forward_routed(const moe_config* cfg, int64_t T, const void* x, const in
                        const float* topk_weights, const void* w_gate, const void* w_up,
                        const void* w_down, const void* ws_gate, const void* ws_up, const void* ws_down,
                        void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The whole layer with 4-bit routed experts: [DEEP] §7.2 (INT4 weights for the routed experts,
+ * symmetric, one scale per group of 32 inputs; shared expert excluded) and [QA] Q7.1 (only the
+ * routed experts' storage is quantized, the arithmetic stays high-precision), Steps 1-7 of
+ * [DEEP] §10.2.
+ * As moe_forward, except that each routed-expert matrix W [E, N, K] comes as
+ *   codes  [E, N, K/8] uint32: q[n, k] in bits 4*(k % 8) .. 4*(k % 8)+3 of word k/8, a 4-bit
+ *          two's-complement integer in [-8, 7]
+ *   scales [E, N, K/32] IEEE binary16 (uint16 bits): s[n, k/32]
+ *   W[n, k] = q[n, k] * s[n, k/32]
+ * i.e. gate_codes, up_codes [E, I, H/8], gate_scales, up_scales [E, I, H/32],
+ *      down_codes [E, H, I/8], down_scales [E, H, I/32].
+ * Precision: dtype must be MOE_BF16.  The routed experts multiply in binary16 with fp32
+ * accumulation: x is rounded once to binary16 (|x| must stay below 65504), each decoded weight
+ * q*s is rounded once to binary16, SiLU(g)*u is rounded to binary16 between the two matmuls,
+ * y_rows to bf16.  The shared expert and the combine are as in moe_forward.
+ * Shapes: as moe_forward, with hidden_size and moe_intermediate_size multiples of 256.
+ * Each routed expert that received tokens has its codes and scales read once per 16 of its
+ * rows (the kernels stream weights; they are built for decode-sized T).
+ * Workspace: moe_workspace_size(cfg, MOE_OP_FORWARD_Q4, T, 0). */
+int moe_forward_q4(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                   const float* score_bias, const float* logit_offset, const uint32_t* gate_codes,
+                   const uint16_t* gate_scales, const uint32_t* up_codes, const uint16_t* up_scales,
+                   const uint32_t* down_codes, const uint16_t* down_scales, const void* ws_gate,
+                   const void* ws_up, const void* ws_down, void* y, int32_t* topk_ids_out,
+                   float* topk_weights_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Message of the last failed call on this thread ("" if none); valid until the next call. */
 const char* moe_last_error(void);

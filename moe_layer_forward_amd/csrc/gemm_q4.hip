@@ -1,0 +1,570 @@
+// 4-bit routed experts, weight streaming (decode-like shapes, few rows per expert).
+//
+// Routed-expert weights are stored as "Kimi K2.5 模型架构深度拆解" §7.2 configures them: signed
+// 4-bit integers, one scale per 32 consecutive inputs, symmetric (w = q * s).  In memory:
+//   codes  [G, N, K/8]  uint32: q of input k in bits 4*(k % 8) of word k/8, two's complement
+//   scales [G, N, K/32] binary16
+// The page keeps the computation high-precision (only storage is quantized).  gfx950 has packed
+// f16 arithmetic but no packed bf16 arithmetic, so the weights are decoded to f16 (q*s rounded
+// once) and the expert matmuls run on v_mfma_f32_16x16x32_f16 with f16 token rows and fp32
+// accumulation; the token rows are converted from bf16 once per layer (f16_rows_kernel).
+//
+// Decoding two codes costs four instructions: the 8 nibbles of a word are made offset-binary with
+// one xor, ((w >> 4i) & 0x000F000F) | 0x64006400 puts codes i and i+4 into the mantissas of two
+// binary16 values 1024 + u, one packed subtract makes them exact integers and one packed multiply
+// applies the scale.  The pairs come out as inputs (i, i+4), so every operand of these matmuls keeps
+// each group of 8 consecutive inputs in the order 0,4,1,5,2,6,3,7 (the f16 token rows and the f16 h
+// are written that way); the dot product over a group is unchanged by the common permutation.
+//
+// The stream itself is the bf16 weight stream's (gemm_stream.hip): a wave streams two 16-row sets
+// of weight rows (gate + up of 16 h columns, or 32 rows of W_down) through a wave-private 4-stage
+// LDS ring of direct global->LDS loads, one instruction = 8 rows x 128 contiguous bytes (whole
+// lines) with the streaming policy; the 16-byte chunk c of a 128-byte row r sits at c ^ ((r >> 1) & 7)
+// so the 16 rows of one B-operand read hit different banks.  Scales and token rows go to register
+// rings in the same step as their codes.  A step covers 256 inputs: 8 groups, 8 MFMAs per set and
+// pass.  Work-groups = 4 waves; groups from the plan's active list, largest first.
+#include <type_traits>
+
+#include "kernels.h"
+#include "tile_core.h"
+
+namespace moe {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWaves = 4;
+constexpr int kStepK = 256;             // inputs per step
+constexpr int kCodeRowB = kStepK / 2;   // 128 bytes of codes per row per step
+constexpr int kSetCodeB = 16 * kCodeRowB;
+constexpr int kWaveB = 2 * kSetCodeB;   // one wave's part of one ring stage
+constexpr int kStageB = kWaves * kWaveB;
+constexpr int kD = 4;                   // ring stages = steps in flight = steps per scale block
+constexpr int kScaleRowB = kD * 16;     // a row's binary16 scales for the kD steps of a block
+constexpr int kScaleSetB = 16 * kScaleRowB;
+constexpr int kScaleWaveB = 2 * kScaleSetB;  // one wave's part of one scale buffer
+
+// Compile-time loop: f(integral_constant<int, I>) for I = 0 .. N-1.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(const F& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+struct Q4Args {
+  const int32_t* group_offsets;
+  const int32_t* row_index;  // gate/up: token row of each routed row
+  const int32_t* active;
+  const int32_t* counters;
+  int64_t max_rows;
+  const uint32_t* codes0;    // gate (gate/up) or down codes
+  const uint16_t* scales0;
+  const uint32_t* codes1;    // up codes (gate/up)
+  const uint16_t* scales1;
+  const uint16_t* a;         // f16 rows, groups of 8 inputs in the order 0,4,1,5,2,6,3,7
+  uint32_t a_bytes;          // bytes of a the kernel may read (< 4 GiB)
+  void* out;
+  int out_bf16;
+  const float* row_scale;
+  int H, I, n_wg;
+  // The shared expert (bf16 weights and rows) in the same launch: work-groups [0, sh_blocks).
+  int sh_blocks;
+  const int32_t* sh_offsets;    // its rows: [sh_offsets[0], sh_offsets[1])
+  const int32_t* sh_row_index;  // gate/up: token row of each of its rows
+  const uint16_t* sh_w0;        // gate (gate/up) or down weight
+  const uint16_t* sh_w1;        // up weight (gate/up)
+  const uint16_t* sh_a;         // bf16 x (gate/up) or h (down) rows
+  uint32_t sh_a_bytes;
+};
+
+__device__ __forceinline__ int code_swz(int r) { return (r >> 1) & 7; }
+
+// Position of input t (0..7) of a group of 8 in the f16 operand order 0,4,1,5,2,6,3,7.
+__device__ __forceinline__ int pair_pos(int t) { return ((t & 3) << 1) | (t >> 2); }
+
+// The binary16 scale of group J of a step as fp32: the low half of scale word J/2 for even J, the
+// high half for odd J.
+template <int J>
+__device__ __forceinline__ float scale_f32(uint32_t sw) {
+  const uint16_t h = (J & 1) ? (uint16_t)(sw >> 16) : (uint16_t)(sw & 0xffffu);
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// The 8 codes of one word as exact binary16 integers, in the operand order 0,4,1,5,2,6,3,7:
+// code k in bits 4k..4k+3 (two's complement q) -> offset binary u = q + 8; a field in bits 0..3 of a
+// 16-bit half ORed into 0x6400 reads 1024 + u, a field in bits 4..7 ORed into 0x5400 reads 64 + u.
+// The constant parts (1032 and 72 per input position, kBias) are removed by the bias matmul.  Since
+// the OR constant is disjoint from the field, ((w ^ 0x88888888) & M) | C == (w & M) ^ K with
+// K = (0x88888888 & M) | C: one three-input bit operation per pair of codes.
+__device__ __forceinline__ f16x8 decode(uint32_t w) {
+  const uint32_t w8 = w >> 8;
+  u32x4 r;
+  r[0] = (w & 0x000F000Fu) ^ 0x64086408u;   // codes 0, 4: 1024 + u
+  r[1] = (w & 0x00F000F0u) ^ 0x54805480u;   // codes 1, 5: 64 + u
+  r[2] = (w8 & 0x000F000Fu) ^ 0x64086408u;  // codes 2, 6
+  r[3] = (w8 & 0x00F000F0u) ^ 0x54805480u;  // codes 3, 7
+  return __builtin_bit_cast(f16x8, r);
+}
+
+// Minus the constant part of each decoded position (B operand of the bias matmul).
+__device__ __forceinline__ f16x8 bias_operand() {
+  const _Float16 a = (_Float16)-1032.f, b = (_Float16)-72.f;
+  return f16x8{a, a, b, b, a, a, b, b};
+}
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+// Buffer descriptor of `bytes` bytes at base: a load at an offset past the end returns zeros and
+// reads no memory (how the ring's padded steps stay uniform).
+// base and bytes must be wave-uniform (a descriptor in VGPRs makes the compiler wrap each load in a
+// loop over the wave's distinct descriptors).
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void* LdsPtr;
+
+// Register ring slot of one step: the f16 token-row fragments of the step's 8 groups.
+struct Slot {
+  u32x4 a[8];
+};
+
+struct Q4Stream {
+  static constexpr int kLoads = 2 * 2 + 8;  // per step: codes (direct to LDS), token rows
+  static constexpr int kScaleLoads = 2;     // per block of kD steps: scales (into registers)
+  static_assert((kD - 1) * kLoads + kScaleLoads <= 63, "vmcnt");
+
+  const void* cb[2];        // codes of each set's 16 rows (uniform)
+  const void* sb[2];        // scales of each set's 16 rows (uniform)
+  const void* abase;        // token rows (f16)
+  uint32_t c_bytes, s_bytes, a_bytes;
+  uint32_t c_off[2];        // lane offsets of the two direct loads of a set (row, swizzled chunk)
+  uint32_t s_off;           // lane offset of the scale load: row lane/4, bytes 16*(lane%4)..+15 of a block
+  uint32_t a_off;           // lane offset of its token-row fragment (row, k-quarter)
+  int wave_off, sc_wave_off;
+
+  // Loads of step st into ring stage d and slot sl; past the last step (nsteps) they read nothing
+  // and fill zeros.
+  __device__ __forceinline__ void issue(char* const (&ring)[kD], int d, int st, int nsteps, Slot& sl) const {
+    // st opaque to the optimiser: otherwise it precomputes addresses per (step, load) of the
+    // prologue, keeps them live across the whole pass and spills them
+    asm volatile("" : "+s"(st));
+    const bool live = st < nsteps;
+    // record counts through readfirstlane: the descriptors stay scalar (no per-load waterfall loops)
+    const uint32_t cn = __builtin_amdgcn_readfirstlane(live ? c_bytes : 0u);
+    const uint32_t an = __builtin_amdgcn_readfirstlane(live ? a_bytes : 0u);
+    char* dst = ring[d] + wave_off;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const Rsrc rc = make_rsrc(cb[r], cn);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (LdsPtr)(dst + r * kSetCodeB + i * 1024), 16,
+                                                 c_off[i] + (uint32_t)st * kCodeRowB, 0, 0, 2);
+    }
+    const Rsrc ra = make_rsrc(abase, an);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      sl.a[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_off + (uint32_t)st * (2 * kStepK) + 64 * j, 0, 0);
+  }
+
+  // The scales of steps st .. st + kD - 1 (st a multiple of kD) into registers: one 64-byte piece
+  // per row and set, lane l holding bytes 16*(l%4)..+15 of row l/4 (so each scale line is fetched
+  // in two requests, not eight).  Past the last step they read nothing.
+  __device__ __forceinline__ void issue_scales(int st, int nsteps, u32x4 (&sr)[2]) const {
+    asm volatile("" : "+s"(st));
+    const uint32_t sn = __builtin_amdgcn_readfirstlane(st < nsteps ? s_bytes : 0u);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      sr[r] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(sb[r], sn), s_off + (uint32_t)st * 16, 0, 0);
+  }
+
+  // ... and from registers into the wave's scale buffer: [set][row][kD steps x 8 scales].  (Plain
+  // LDS stores: direct loads into more LDS arrays would make the compiler wait for them before
+  // every ring read.)
+  __device__ __forceinline__ void store_scales(char* sc, const u32x4 (&sr)[2]) const {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) *reinterpret_cast<u32x4*>(sc + sc_wave_off + r * kScaleSetB + lane * 16) = sr[r];
+  }
+
+  // One step: for each group j of 32 inputs, c = A_j . (-bias) + A_j . (1024|64 + u) = A_j . q (exact
+  // integer weights, fp32 sums), then acc += s_j * c with the group's scale in fp32.  Software
+  // pipelined by hand: the code words are read one group ahead, and group j's products are scaled
+  // into acc while group j+1's matmuls run (scheduling barriers keep the compiler from hoisting
+  // more and running out of registers).
+  // d: ring stage (= step % kD); sc: the scale buffer holding the step's block.
+  __device__ __forceinline__ void compute(char* const (&ring)[kD], int d, const char* sc, const Slot& sl,
+                                          f32x4 (&acc)[2]) const {
+    const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
+    const char* src = ring[d] + wave_off + c * kCodeRowB + 4 * q;
+    u32x4 sv[2];  // the step's 8 scales of row c of each set
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      sv[r] = *reinterpret_cast<const u32x4*>(sc + sc_wave_off + r * kScaleSetB + c * kScaleRowB + d * 16);
+    const f16x8 nb = bias_operand();
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    auto read = [&](auto jc, uint32_t (&wd)[2]) {
+      constexpr int j = decltype(jc)::value;
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        wd[r] = *reinterpret_cast<const uint32_t*>(src + r * kSetCodeB + ((j ^ code_swz(c)) << 4));
+    };
+    uint32_t wd[2][2];
+    f32x4 pend[2];
+    float pend_s[2];
+    read(std::integral_constant<int, 0>{}, wd[0]);
+    static_for<8>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (j + 1 < 8) read(std::integral_constant<int, j + 1>{}, wd[(j + 1) & 1]);
+      const f16x8 a = __builtin_bit_cast(f16x8, sl.a[j]);
+      const f32x4 cb = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, nb, zero, 0, 0, 0);
+      f32x4 cur[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) cur[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, decode(wd[j & 1][r]), cb, 0, 0, 0);
+      if constexpr (j > 0) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[r][e] = __builtin_fmaf(pend_s[r], pend[r][e], acc[r][e]);
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        pend[r] = cur[r];
+        pend_s[r] = scale_f32<j>(sv[r][j >> 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[r][e] = __builtin_fmaf(pend_s[r], pend[r][e], acc[r][e]);
+  }
+
+  // The K loop of one pass.  Every step issues the loads of the step kD ahead, unconditionally (past
+  // the end they read nothing), and the first step of each block of kD steps first loads the next
+  // block's scales, so the waits are fixed; steps past the end skip the multiply.
+  __device__ __forceinline__ void run(char* const (&ring)[kD], char* sc, int nsteps, f32x4 (&acc)[2]) const {
+    Slot sl[kD];
+    u32x4 sr[2];
+    issue_scales(0, nsteps, sr);
+    static_for<kD>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      issue(ring, i, i, nsteps, sl[i]);
+    });
+    for (int g = 0; g < nsteps; g += kD) {
+      static_for<kD>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        // after step g + i's loads: the next kD - 1 steps' loads, and the next block's scales among
+        // them unless this step starts a block
+        wait_vmcnt<(kD - 1) * kLoads + (i == 0 ? 0 : kScaleLoads)>();
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (i == 0) store_scales(sc, sr);  // this block's scales, loaded a block ago
+        if (g + i < nsteps) compute(ring, i, sc, sl[i], acc);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this stage's LDS reads are done
+        if constexpr (i == 0) issue_scales(g + kD, nsteps, sr);
+        issue(ring, i, g + i + kD, nsteps, sl[i]);
+      });
+    }
+    wait_vmcnt<0>();  // the last block's padding loads still write (zeros) into the ring
+  }
+};
+
+template <bool SWIGLU>
+__device__ __forceinline__ void q4_pass(const Q4Args& p, char* const (&ring)[kD], char* sc, const Q4Stream& base,
+                                        int n0, int64_t mb, int64_t r1) {
+  const int H = p.H, I = p.I, K = SWIGLU ? H : I;
+  const int lane = threadIdx.x & 63;
+  Q4Stream s = base;
+  {
+    const int64_t r = mb + (lane & 15);
+    const int64_t rr = r < r1 ? r : mb;  // rows past the group end repeat its first row, never stored
+    const int64_t src = SWIGLU ? (p.row_index ? (int64_t)p.row_index[rr] : rr) : rr;
+    s.a_off = (uint32_t)(src * K * 2 + (lane >> 4) * 16);
+  }
+  f32x4 acc[2];
+  acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  s.run(ring, sc, K / kStepK, acc);
+
+  // lane holds rows mb + 4*(lane/16) + e, column n0 + lane%16 (+16 for set 1 of down)
+  const int col = n0 + (lane & 15);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t row = mb + 4 * (lane >> 4) + e;
+    if (row >= r1) continue;
+    if (SWIGLU) {
+      // h in f16, each group of 8 columns in the operand order of the down matmul
+      const _Float16 v = (_Float16)swiglu_f32(acc[0][e], acc[1][e]);
+      static_cast<_Float16*>(p.out)[row * I + (col & ~7) + pair_pos(col & 7)] = v;
+    } else {
+      const float sc = p.row_scale ? p.row_scale[row] : 1.f;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const float v = acc[r][e] * sc;
+        if (p.out_bf16)
+          static_cast<uint16_t*>(p.out)[row * H + col + 16 * r] = f32_to_bf16(v);
+        else
+          static_cast<float*>(p.out)[row * H + col + 16 * r] = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// The shared expert (bf16 weights, bf16 token rows), streamed through the same ring by the first
+// work-groups of the launch so that it overlaps the routed experts: a step covers 64 inputs (128
+// bytes of each of a wave's 2 x 16 weight rows, swizzled as the codes are), passes of 32 rows.
+constexpr int kShStepK = 64;
+constexpr int kShNP = 2;  // 16-row MFMA blocks per pass
+
+struct ShSlot {
+  u32x4 a[kShNP][2];
+};
+
+struct ShStream {
+  static constexpr int kLoads = 2 * 2 + 2 * kShNP;
+  static_assert((kD - 1) * kLoads <= 63, "vmcnt");
+
+  const void* wb[2];        // each set's 16 weight rows (uniform)
+  const void* abase;
+  uint32_t w_bytes, a_bytes;
+  uint32_t c_off[2];        // lane offsets of the two direct loads of a set (row, swizzled chunk)
+  uint32_t a_off[kShNP];    // lane offsets of its token-row fragments
+  int wave_off;
+
+  __device__ __forceinline__ void issue(char* const (&ring)[kD], int d, int st, int nsteps, ShSlot& sl) const {
+    asm volatile("" : "+s"(st));
+    const bool live = st < nsteps;
+    const uint32_t wn = __builtin_amdgcn_readfirstlane(live ? w_bytes : 0u);
+    const uint32_t an = __builtin_amdgcn_readfirstlane(live ? a_bytes : 0u);
+    char* dst = ring[d] + wave_off;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const Rsrc rw = make_rsrc(wb[r], wn);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (LdsPtr)(dst + r * kSetCodeB + i * 1024), 16,
+                                                 c_off[i] + (uint32_t)st * (2 * kShStepK), 0, 0, 2);
+    }
+    const Rsrc ra = make_rsrc(abase, an);
+#pragma unroll
+    for (int p = 0; p < kShNP; ++p)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        sl.a[p][j] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_off[p] + (uint32_t)st * (2 * kShStepK) + 64 * j, 0, 0);
+  }
+
+  __device__ __forceinline__ void compute(char* const (&ring)[kD], int d, const ShSlot& sl,
+                                          f32x4 (&acc)[kShNP][2]) const {
+    const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
+    const char* src = ring[d] + wave_off + c * kCodeRowB;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(src + r * kSetCodeB + (((4 * j + q) ^ code_swz(c)) << 4));
+#pragma unroll
+        for (int p = 0; p < kShNP; ++p)
+          acc[p][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, sl.a[p][j]), b, acc[p][r],
+                                                             0, 0, 0);
+      }
+  }
+
+  // As Q4Stream::run, without scales.
+  __device__ __forceinline__ void run(char* const (&ring)[kD], int nsteps, f32x4 (&acc)[kShNP][2]) const {
+    ShSlot sl[kD];
+    static_for<kD>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      issue(ring, i, i, nsteps, sl[i]);
+    });
+    for (int g = 0; g < nsteps; g += kD) {
+      static_for<kD>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        wait_vmcnt<(kD - 1) * kLoads>();
+        __builtin_amdgcn_sched_barrier(0);
+        if (g + i < nsteps) compute(ring, i, sl[i], acc);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue(ring, i, g + i + kD, nsteps, sl[i]);
+      });
+    }
+    wait_vmcnt<0>();
+  }
+};
+
+// Work-group blk of the shared expert: output columns of 4 waves, every row of the expert.
+template <bool SWIGLU>
+__device__ __forceinline__ void shared_part(const Q4Args& p, char* const (&ring)[kD], int blk) {
+  const int H = p.H, I = p.I, K = SWIGLU ? H : I;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blk * (SWIGLU ? 64 : 128) + wave * (SWIGLU ? 16 : 32);
+  const int64_t r0 = p.sh_offsets[0], r1 = p.sh_offsets[1];
+  ShStream s;
+  s.wb[0] = p.sh_w0 + (int64_t)n0 * K;
+  s.wb[1] = SWIGLU ? p.sh_w1 + (int64_t)n0 * K : p.sh_w0 + (int64_t)(n0 + 16) * K;
+  s.abase = p.sh_a;
+  s.w_bytes = (uint32_t)(16 * K * 2);
+  s.a_bytes = p.sh_a_bytes;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 8 * i + (lane >> 3);
+    s.c_off[i] = (uint32_t)(row * K * 2 + (((lane & 7) ^ code_swz(row)) << 4));
+  }
+  s.wave_off = wave * kWaveB;
+  const int col = n0 + (lane & 15);
+  for (int64_t mb = r0; mb < r1; mb += 16 * kShNP) {
+#pragma unroll
+    for (int q = 0; q < kShNP; ++q) {
+      const int64_t r = mb + 16 * q + (lane & 15);
+      const int64_t rr = r < r1 ? r : mb;  // rows past the end repeat row mb, never stored
+      const int64_t src = SWIGLU ? (int64_t)p.sh_row_index[rr] : rr;
+      s.a_off[q] = (uint32_t)(src * K * 2 + (lane >> 4) * 16);
+    }
+    f32x4 acc[kShNP][2];
+#pragma unroll
+    for (int q = 0; q < kShNP; ++q) acc[q][0] = acc[q][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    s.run(ring, K / kShStepK, acc);
+#pragma unroll
+    for (int q = 0; q < kShNP; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = mb + 16 * q + 4 * (lane >> 4) + e;
+        if (row >= r1) continue;
+        if (SWIGLU) {
+          static_cast<uint16_t*>(p.out)[row * I + col] = f32_to_bf16(swiglu_f32(acc[q][0][e], acc[q][1][e]));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 2; ++r) static_cast<uint16_t*>(p.out)[row * H + col + 16 * r] = f32_to_bf16(acc[q][r][e]);
+        }
+      }
+  }
+}
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void q4_stream_kernel(Q4Args p) {
+  // one array per stage: the compiler then tells the stages' direct loads and LDS reads apart
+  __shared__ __align__(16) char s0[kStageB], s1[kStageB], s2[kStageB], s3[kStageB];
+  __shared__ __align__(16) char sc[kWaves * kScaleWaveB];
+  static_assert(kD == 4, "one LDS array per ring stage");
+  char* const ring[kD] = {s0, s1, s2, s3};
+
+  if ((int)blockIdx.x < p.sh_blocks) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    shared_part<SWIGLU>(p, ring, blockIdx.x);
+#endif
+    return;
+  }
+  const int bid = (int)blockIdx.x - p.sh_blocks;
+  const int slot = bid / p.n_wg, nb = bid % p.n_wg;
+  if (slot >= p.counters[0]) return;
+  const int g = p.active[slot];
+  int64_t r0 = p.group_offsets[g], r1 = p.group_offsets[g + 1];
+  if (r0 > p.max_rows) r0 = p.max_rows;
+  if (r1 > p.max_rows) r1 = p.max_rows;
+  const int H = p.H, I = p.I, K = SWIGLU ? H : I, N = SWIGLU ? I : H;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = nb * (SWIGLU ? 64 : 128) + wave * (SWIGLU ? 16 : 32);  // first output column of this wave
+
+  // rows of the two 16-row sets: gate and up rows n0.. (gate/up), or W_down rows n0.. and n0+16..
+  const int64_t row0[2] = {n0, SWIGLU ? n0 : n0 + 16};
+  const uint32_t* cm[2] = {p.codes0 + (int64_t)g * N * (K / 8), (SWIGLU ? p.codes1 : p.codes0) + (int64_t)g * N * (K / 8)};
+  const uint16_t* sm[2] = {p.scales0 + (int64_t)g * N * (K / 32),
+                           (SWIGLU ? p.scales1 : p.scales0) + (int64_t)g * N * (K / 32)};
+  Q4Stream s;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    s.cb[r] = cm[r] + row0[r] * (K / 8);
+    s.sb[r] = sm[r] + row0[r] * (K / 32);
+  }
+  s.abase = p.a;
+  s.a_bytes = p.a_bytes;
+  s.c_bytes = (uint32_t)(16 * (K / 2));
+  s.s_bytes = (uint32_t)(16 * (K / 16));
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 8 * i + (lane >> 3);  // lane's row in the 16-row set; its slot = chunk position
+    s.c_off[i] = (uint32_t)(row * (K / 2) + (((lane & 7) ^ code_swz(row)) << 4));
+  }
+  s.s_off = (uint32_t)((lane >> 2) * (K / 16) + (lane & 3) * 16);
+  s.wave_off = wave * kWaveB;
+  s.sc_wave_off = wave * kScaleWaveB;
+#if defined(__HIP_DEVICE_COMPILE__)
+  for (int64_t mb = r0; mb < r1; mb += 16) q4_pass<SWIGLU>(p, ring, sc, s, n0, mb, r1);
+#else
+  (void)s;
+  (void)n0;
+  (void)r0;
+#endif
+}
+
+// bf16 rows -> f16 rows with each group of 8 inputs in the order 0,4,1,5,2,6,3,7 (one group per thread).
+__global__ __launch_bounds__(256) void f16_rows_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
+                                                       int64_t n_groups) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_groups; i += stride) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(x + 8 * i);
+    _Float16 h[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t bits = (v[t >> 1] >> (16 * (t & 1))) & 0xffffu;
+      h[pair_pos(t)] = (_Float16)__uint_as_float(bits << 16);  // bf16 -> f32 exact, then to f16 (RNE)
+    }
+    *reinterpret_cast<f16x8*>(y + 8 * i) = f16x8{h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]};
+  }
+}
+
+}  // namespace
+
+hipError_t launch_f16_rows(const uint16_t* x, uint16_t* y, int64_t rows, int cols, hipStream_t s) {
+  const int64_t n = rows * cols / 8;
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  f16_rows_kernel<<<(unsigned)blocks, 256, 0, s>>>(x, y, n);
+  return hipGetLastError();
+}
+
+// Bytes of a [rows, cols] f16 operand, as a buffer record count (callers keep operands below 4 GiB).
+static uint32_t operand_bytes(int64_t rows, int cols) {
+  const int64_t b = rows * cols * 2;
+  return b >= 0xffffffffLL ? 0xffffffffu : (uint32_t)b;
+}
+
+// Shared-expert fields of the launch arguments.
+static void set_shared(Q4Args& p, const SharedBf16* sh, bool swiglu, int H, int I) {
+  p.sh_blocks = 0;
+  if (!sh) return;
+  p.sh_blocks = swiglu ? I / 64 : H / 128;
+  p.sh_offsets = sh->offsets;
+  p.sh_row_index = sh->row_index;
+  p.sh_w0 = swiglu ? sh->gate : sh->down;
+  p.sh_w1 = swiglu ? sh->up : nullptr;
+  p.sh_a = swiglu ? sh->x : sh->h;
+  p.sh_a_bytes = swiglu ? operand_bytes(sh->x_rows, H) : operand_bytes(sh->h_rows, I);
+}
+
+hipError_t launch_gateup_q4_stream(const Groups& g, const QWeights& w, const uint16_t* x16, int64_t x_rows,
+                                   uint16_t* h16, const SharedBf16* sh, int H, int I, hipStream_t s) {
+  Q4Args p{g.group_offsets, g.row_index, g.active, g.counters, g.max_rows, w.gate_codes, w.gate_scales,
+           w.up_codes, w.up_scales, x16, operand_bytes(x_rows, H), h16, 0, nullptr, H, I, I / 64};
+  set_shared(p, sh, true, H, I);
+  q4_stream_kernel<true><<<(unsigned)(p.sh_blocks + (int64_t)g.n_groups * p.n_wg), 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_q4_stream(const Groups& g, const QWeights& w, const uint16_t* h16, uint16_t* y_rows,
+                                 const SharedBf16* sh, int H, int I, hipStream_t s) {
+  Q4Args p{g.group_offsets, nullptr, g.active, g.counters, g.max_rows, w.down_codes, w.down_scales, nullptr,
+           nullptr, h16, operand_bytes(g.max_rows, I), y_rows, 1, nullptr, H, I, H / 128};
+  set_shared(p, sh, false, H, I);
+  q4_stream_kernel<false><<<(unsigned)(p.sh_blocks + (int64_t)g.n_groups * p.n_wg), 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -54,6 +54,17 @@ struct Weights {
   int32_t shared_group = -1;
 };
 
+// 4-bit routed-expert weights (w = q * s, one binary16 scale per 32 consecutive inputs): codes
+// [E, N, K/8] (q of input k in bits 4*(k % 8) of word k/8, two's complement), scales [E, N, K/32].
+struct QWeights {
+  const uint32_t* gate_codes = nullptr;  // [E, I, H/8]
+  const uint16_t* gate_scales = nullptr; // [E, I, H/32]
+  const uint32_t* up_codes = nullptr;
+  const uint16_t* up_scales = nullptr;
+  const uint32_t* down_codes = nullptr;  // [E, H, I/8]
+  const uint16_t* down_scales = nullptr; // [E, H, I/32]
+};
+
 // ----------------------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.
 
@@ -97,6 +108,30 @@ hipError_t launch_down_tile_bf16(const Groups& g, const Weights& w, const uint16
                                  bool y_bf16, const float* row_scale, int H, int I, hipStream_t s);
 // Rows per tile used by the tile kernels' plan.
 constexpr int kTileM = 256;  // rows per tile of the tile GEMMs
+
+// grouped SwiGLU, 4-bit routed experts (weight streaming) ----------------------------
+// The shared expert (bf16), computed by the first work-groups of the 4-bit launches: its rows are
+// [offsets[0], offsets[1]) of the row space (token row_index[r] for gate/up), its h rows bf16.
+struct SharedBf16 {
+  const int32_t* offsets = nullptr;    // 2 entries, device
+  const int32_t* row_index = nullptr;  // [rows] device
+  const uint16_t* gate = nullptr;      // [I, H]
+  const uint16_t* up = nullptr;        // [I, H]
+  const uint16_t* down = nullptr;      // [H, I]
+  const uint16_t* x = nullptr;         // bf16 token rows [x_rows, H]
+  int64_t x_rows = 0;
+  const uint16_t* h = nullptr;         // the h buffer [h_rows, I] (its shared rows bf16)
+  int64_t h_rows = 0;
+};
+// y16[r, c] (f16) = x[r, c] with every group of 8 columns in the order 0,4,1,5,2,6,3,7.
+hipError_t launch_f16_rows(const uint16_t* x, uint16_t* y16, int64_t rows, int cols, hipStream_t s);
+// h16[r, I] (f16, same column order) = SiLU(a Wg^T) * (a Wu^T), a = x16 rows (x_rows of them) through
+// row_index; plus the shared expert's h rows (bf16) when sh is given.
+hipError_t launch_gateup_q4_stream(const Groups& g, const QWeights& w, const uint16_t* x16, int64_t x_rows,
+                                   uint16_t* h16, const SharedBf16* sh, int H, int I, hipStream_t s);
+// y_rows[r, H] (bf16) = h16[r] Wd^T, plus the shared expert's rows when sh is given.
+hipError_t launch_down_q4_stream(const Groups& g, const QWeights& w, const uint16_t* h16, uint16_t* y_rows,
+                                 const SharedBf16* sh, int H, int I, hipStream_t s);
 
 // grouped SwiGLU, fp32 (plain kernels) ---------------------------------------------
 hipError_t launch_gateup_f32(const Groups& g, const Weights& w, const float* x, float* h, int H, int I,

@@ -145,16 +145,23 @@ struct SwigluWs {
   moe::Groups g;
 };
 
+// Plan buffers of G groups over at most max_rows rows.
+moe::Groups carve_plan(Carver& cv, int G, int64_t max_rows) {
+  moe::Groups g;
+  g.n_groups = G;
+  g.max_rows = max_rows;
+  g.tile_m = moe::kTileM;
+  g.max_tiles = (int32_t)((max_rows + moe::kTileM - 1) / moe::kTileM + G);
+  g.active = cv.take<int32_t>(G);
+  g.counters = cv.take<int32_t>(2);
+  g.tiles = cv.take<int32_t>(2LL * g.max_tiles);
+  return g;
+}
+
 SwigluWs carve_swiglu(Carver& cv, const moe_config* c, int G, int64_t max_rows) {
   SwigluWs w{};
   w.h = cv.take<char>(max_rows * c->moe_intermediate_size * (int64_t)elem_bytes(c->dtype));
-  w.g.n_groups = G;
-  w.g.max_rows = max_rows;
-  w.g.tile_m = moe::kTileM;
-  w.g.max_tiles = (int32_t)((max_rows + moe::kTileM - 1) / moe::kTileM + G);
-  w.g.active = cv.take<int32_t>(G);
-  w.g.counters = cv.take<int32_t>(2);
-  w.g.tiles = cv.take<int32_t>(2LL * w.g.max_tiles);
+  w.g = carve_plan(cv, G, max_rows);
   return w;
 }
 
@@ -259,6 +266,49 @@ int run_after_routing(const moe_config* c, int64_t T, const void* x, const int32
   return ok();
 }
 
+// Workspace of the forward with 4-bit routed experts.  h holds f16 rows for the routed pairs and
+// bf16 rows for the shared expert's rows after them; y_rows is bf16.
+struct Q4Ws {
+  int32_t* ids;
+  float* weights;
+  float* router_part;
+  int32_t* offsets;
+  int32_t* row_token;
+  int32_t* pair_row;
+  int32_t* perm_scratch;
+  uint16_t* x16;
+  uint16_t* h;
+  moe::Groups routed;
+  void* y_rows;
+};
+
+Q4Ws carve_q4(Carver& cv, const moe_config* c, int64_t T) {
+  const int H = c->hidden_size, I = c->moe_intermediate_size, E = c->n_routed_experts, K = c->top_k;
+  const bool shared = c->n_shared_experts == 1;
+  const int64_t P = T * K;
+  const int64_t rows = P + (shared ? T : 0);
+  Q4Ws w{};
+  w.ids = cv.take<int32_t>(P);
+  w.weights = cv.take<float>(P);
+  w.router_part = cv.take<float>((int64_t)moe::router_nsplit(T, H, E, true) * T * E);
+  w.offsets = cv.take<int32_t>(E + 2);
+  w.row_token = cv.take<int32_t>(rows);
+  w.pair_row = cv.take<int32_t>(P);
+  w.perm_scratch = cv.take<int32_t>(moe::permute_scratch_ints(P, E));
+  w.x16 = cv.take<uint16_t>(T * H);
+  w.h = cv.take<uint16_t>(rows * I);
+  w.routed = carve_plan(cv, E, P);
+  w.y_rows = cv.take<uint16_t>(rows * H);
+  return w;
+}
+
+int check_config_q4(const moe_config* c) {
+  if (c->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "4-bit routed experts need dtype MOE_BF16");
+  if (c->hidden_size % 256 || c->moe_intermediate_size % 256)
+    return fail(MOE_ERR_UNSUPPORTED, "4-bit routed experts need hidden_size and moe_intermediate_size multiples of 256");
+  return MOE_OK;
+}
+
 hipError_t run_router(const moe_config* c, int64_t T, const void* x, const void* w_router, float* part,
                       hipStream_t s) {
   const int H = c->hidden_size, E = c->n_routed_experts;
@@ -317,6 +367,10 @@ size_t moe_workspace_size(const moe_config* cfg, int32_t op, int64_t rows, int32
     case MOE_OP_FORWARD_ROUTED:
       if (check_tokens(rows, cfg) != MOE_OK) return 0;
       carve_forward(cv, cfg, rows, false);
+      break;
+    case MOE_OP_FORWARD_Q4:
+      if (check_config_q4(cfg) != MOE_OK || check_tokens(rows, cfg) != MOE_OK) return 0;
+      carve_q4(cv, cfg, rows);
       break;
     default:
       fail(MOE_ERR_INVALID_ARG, "unknown op %d", op);
@@ -489,6 +543,81 @@ int moe_forward_routed(const moe_config* cfg, int64_t T, const void* x, const in
   if ((st = check_ws(workspace, workspace_bytes, cv.used))) return st;
   return run_after_routing(cfg, T, x, topk_ids, topk_weights, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y, w,
                            static_cast<hipStream_t>(stream));
+}
+
+int moe_forward_q4(const moe_config* cfg, int64_t T, const void* x, const void* w_router, const float* score_bias,
+                   const float* logit_offset, const uint32_t* gate_codes, const uint16_t* gate_scales,
+                   const uint32_t* up_codes, const uint16_t* up_scales, const uint32_t* down_codes,
+                   const uint16_t* down_scales, const void* ws_gate, const void* ws_up, const void* ws_down, void* y,
+                   int32_t* topk_ids_out, float* topk_weights_out, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  prof_reset();
+  int st = check_config(cfg);
+  if (st) return st;
+  if ((st = check_config_q4(cfg))) return st;
+  if ((st = check_tokens(T, cfg))) return st;
+  if (T == 0) return ok();
+  if (!x || !w_router || !gate_codes || !gate_scales || !up_codes || !up_scales || !down_codes || !down_scales || !y)
+    return fail(MOE_ERR_INVALID_ARG, "moe_forward_q4: x, w_router, expert codes and scales and y are required");
+  const bool shared = cfg->n_shared_experts == 1;
+  if (shared && (!ws_gate || !ws_up || !ws_down))
+    return fail(MOE_ERR_INVALID_ARG, "moe_forward_q4: shared expert weights are required");
+  if ((st = check_forward_spans(cfg, T))) return st;
+  const int H = cfg->hidden_size, I = cfg->moe_intermediate_size, E = cfg->n_routed_experts, K = cfg->top_k;
+  const int64_t P = T * K;
+  Carver cv(workspace);
+  Q4Ws w = carve_q4(cv, cfg, T);
+  if ((st = check_ws(workspace, workspace_bytes, cv.used))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* ids = topk_ids_out ? topk_ids_out : w.ids;
+  float* weights = topk_weights_out ? topk_weights_out : w.weights;
+
+  hipError_t e = run_router(cfg, T, x, w_router, w.router_part, s);
+  if (e != hipSuccess) return device_status(e, "router logits");
+  e = timed("topk", s, [&] {
+    return moe::launch_topk(w.router_part, moe::router_nsplit(T, H, E, true), logit_offset, score_bias, T, E, K,
+                            cfg->routed_scaling_factor, ids, weights, s);
+  });
+  if (e != hipSuccess) return device_status(e, "top-k");
+  e = timed("permute", s, [&] {
+    return moe::launch_permute(ids, T, K, E, w.offsets, w.row_token, w.pair_row, w.perm_scratch, shared, s);
+  });
+  if (e != hipSuccess) return device_status(e, "permute");
+  e = timed("f16_rows", s, [&] {
+    return moe::launch_f16_rows(static_cast<const uint16_t*>(x), w.x16, T, H, s);
+  });
+  if (e != hipSuccess) return device_status(e, "f16 rows");
+
+  // routed experts: groups 0..E-1 over rows [0, P); the shared expert (bf16) runs in the same
+  // launches over rows [P, P + T) (row P + t is token t)
+  moe::Groups gr = w.routed;
+  gr.group_offsets = w.offsets;
+  gr.row_index = w.row_token;
+  moe::QWeights qw{gate_codes, gate_scales, up_codes, up_scales, down_codes, down_scales};
+  moe::SharedBf16 sh;
+  sh.offsets = w.offsets + E;
+  sh.row_index = w.row_token;
+  sh.gate = static_cast<const uint16_t*>(ws_gate);
+  sh.up = static_cast<const uint16_t*>(ws_up);
+  sh.down = static_cast<const uint16_t*>(ws_down);
+  sh.x = static_cast<const uint16_t*>(x);
+  sh.x_rows = T;
+  sh.h = w.h;
+  sh.h_rows = P + T;
+  const moe::SharedBf16* shp = shared ? &sh : nullptr;
+  uint16_t* y_rows = static_cast<uint16_t*>(w.y_rows);
+  e = timed("plan", s, [&] { return moe::launch_plan(gr, s); });
+  if (e == hipSuccess)
+    e = timed("gateup_q4", s, [&] { return moe::launch_gateup_q4_stream(gr, qw, w.x16, T, w.h, shp, H, I, s); });
+  if (e == hipSuccess)
+    e = timed("down_q4", s, [&] { return moe::launch_down_q4_stream(gr, qw, w.h, y_rows, shp, H, I, s); });
+  if (e != hipSuccess) return device_status(e, "experts");
+
+  e = timed("combine", s, [&] {
+    return moe::launch_combine(y_rows, true, w.pair_row, weights, shared ? y_rows + P * H : nullptr, y, true, T, K,
+                               H, s);
+  });
+  return device_status(e, "combine");
 }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }

@@ -12,6 +12,8 @@ skew         4096  7168  2048  384   8  bf16    router + Zipf-shaped logit offse
 ep_share    16384  7168  2048    3   1  bf16    pre-dispatched ids/weights, no router
 dense_*     64 /   7168 18432    1   1  bf16    none: the dense SwiGLU FFN of the
             8192                                 model's first layer, all tokens
+decode_int4    64  7168  2048  384   8  bf16    as decode; routed experts stored as
+                                                 4-bit codes + binary16 scales
 ==========  =====  ====  ====  ===  ==  ======  ==================================
 
 
@@ -26,6 +28,11 @@ deviation.  Draws are Irwin-Hall(8) approximately-normal variates (see
 ``synth``).  The four full-shape workloads share one weight set (seed 100);
 their activations use the workload number (2..5) as seed; tiny uses seed 1.
 
+decode_int4 has decode's tokens and weights; its routed experts are those bf16
+weights quantized per group of 32 inputs (s = f16(max|w| / 7), q = clamp(rint(w / s),
+-8, 7)) -- the checkpoint-conversion step, done on the device for the GPU and on
+the host for the oracle by two implementations of the same rule (``synth``).
+
 Synthetic streams: 0 activations, 1 router, 2 gate, 3 up, 4 down, 5/6/7 shared
 gate/up/down, 11/12/13 dense gate/up/down (Philox, index = expert id); 8 skew
 permutation, 9 EP-share ids, 10 EP-share weights (numpy PCG64 from
@@ -39,6 +46,7 @@ logits and the realised histogram is reported.
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 from dataclasses import dataclass, field
 
@@ -70,6 +78,7 @@ class Workload:
     rsf: float = RSF_K2
     sigma_x: float = 1.0
     sigma_router: float = 0.02
+    quant: str = "none"           # 'none' | 'int4' (routed experts stored as 4-bit codes + scales)
     extra: dict = field(default_factory=dict, compare=False)
 
     @property
@@ -85,8 +94,7 @@ class Workload:
         return self.T * self.K
 
     def with_tokens(self, T: int) -> "Workload":
-        return Workload(self.name, T, self.H, self.I, self.E, self.K, self.dtype, self.x_seed, self.w_seed,
-                        self.routing, self.n_shared, self.rsf, self.sigma_x, self.sigma_router)
+        return dataclasses.replace(self, T=T)
 
 
 WORKLOADS = {
@@ -100,12 +108,13 @@ WORKLOADS = {
                              routing="dense", n_shared=0),
     "dense_prefill": Workload("dense_prefill", 8192, 7168, DENSE_I, 1, 1, "bf16", x_seed=7, w_seed=100,
                               routing="dense", n_shared=0),
+    "decode_int4": Workload("decode_int4", 64, 7168, 2048, 384, 8, "bf16", x_seed=2, w_seed=100, quant="int4"),
 }
 
 
-def custom(name, T, H, I, E, K, dtype="bf16", x_seed=11, w_seed=12, routing="router", n_shared=1):
+def custom(name, T, H, I, E, K, dtype="bf16", x_seed=11, w_seed=12, routing="router", n_shared=1, quant="none"):
     """A workload with the same recipe at other sizes (parity cases)."""
-    return Workload(name, T, H, I, E, K, dtype, x_seed, w_seed, routing, n_shared)
+    return Workload(name, T, H, I, E, K, dtype, x_seed, w_seed, routing, n_shared, quant=quant)
 
 
 # --------------------------------------------------------------------------- host side
@@ -159,6 +168,17 @@ def host_expert(w: Workload, e: int):
     return _to_f64(g, w.dtype), _to_f64(u, w.dtype), _to_f64(d, w.dtype)
 
 
+def host_expert_q4(w: Workload, e: int):
+    """4-bit storage of routed expert e: ((codes, scales) of W_gate, W_up, W_down), quantized on the host
+    from the expert's bf16 weights (``synth.host_quantize_q4``)."""
+    sg, su, sd = _expert_streams(w)
+    out = []
+    for stream, shape, sigma in ((sg, (w.I, w.H), w.sigma_gate_up), (su, (w.I, w.H), w.sigma_gate_up),
+                                 (sd, (w.H, w.I), w.sigma_down)):
+        out.append(synth.host_quantize_q4(synth.host_tensor(w.w_seed, stream, e, shape, sigma, "bf16")))
+    return tuple(out)
+
+
 def host_shared(w: Workload):
     if w.n_shared == 0:
         return None
@@ -171,7 +191,9 @@ def host_shared(w: Workload):
 # --------------------------------------------------------------------------- device side
 def device_weights(w: Workload, device="cuda"):
     """Router, routed-expert and shared-expert weights of the workload (the dense FFN as expert 0 for
-    'dense'), generated in HBM."""
+    'dense'), generated in HBM.  For quant 'int4' the routed experts come as gate/up/down codes
+    (int32 words) and scales (int16 words holding binary16), quantized on the device
+    (``synth.device_quantize_q4``) from the same bf16 weights, a chunk of experts at a time."""
     import torch
 
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -180,12 +202,26 @@ def device_weights(w: Workload, device="cuda"):
         t["w_router"] = synth.device_fill(torch.empty((w.E, w.H), dtype=dt, device=device), w.w_seed, S_ROUTER,
                                           0, 1, w.E * w.H, w.sigma_router)
     sg, su, sd = _expert_streams(w)
-    t["w_gate"] = synth.device_fill(torch.empty((w.E, w.I, w.H), dtype=dt, device=device), w.w_seed, sg, 0,
-                                    w.E, w.I * w.H, w.sigma_gate_up)
-    t["w_up"] = synth.device_fill(torch.empty((w.E, w.I, w.H), dtype=dt, device=device), w.w_seed, su, 0,
-                                  w.E, w.I * w.H, w.sigma_gate_up)
-    t["w_down"] = synth.device_fill(torch.empty((w.E, w.H, w.I), dtype=dt, device=device), w.w_seed, sd, 0,
-                                    w.E, w.H * w.I, w.sigma_down)
+    mats = (("gate", sg, (w.I, w.H), w.sigma_gate_up), ("up", su, (w.I, w.H), w.sigma_gate_up),
+            ("down", sd, (w.H, w.I), w.sigma_down))
+    if w.quant == "int4":
+        if w.dtype != "bf16":
+            raise ValueError("4-bit experts are quantized from bf16 weights")
+        chunk = min(w.E, 32)
+        for name, stream, (n, k), sigma in mats:
+            codes = torch.empty((w.E, n, k // 8), dtype=torch.int32, device=device)
+            scales = torch.empty((w.E, n, k // 32), dtype=torch.int16, device=device)
+            buf = torch.empty((chunk, n, k), dtype=torch.bfloat16, device=device)
+            for e0 in range(0, w.E, chunk):
+                m = min(chunk, w.E - e0)
+                synth.device_fill(buf[:m], w.w_seed, stream, e0, m, n * k, sigma)
+                synth.device_quantize_q4(buf[:m], codes[e0:e0 + m], scales[e0:e0 + m])
+            t[f"{name}_codes"], t[f"{name}_scales"] = codes, scales
+            del buf
+    else:
+        for name, stream, (n, k), sigma in mats:
+            t[f"w_{name}"] = synth.device_fill(torch.empty((w.E, n, k), dtype=dt, device=device), w.w_seed, stream,
+                                               0, w.E, n * k, sigma)
     if w.n_shared:
         t["ws_gate"] = synth.device_fill(torch.empty((w.I, w.H), dtype=dt, device=device), w.w_seed, S_SGATE, 0,
                                          1, w.I * w.H, w.sigma_gate_up)

@@ -57,6 +57,14 @@ def rel_l2(y, y_ref):
     return num / den
 
 
+def oracle_expert(w):
+    """Expert weights (float64) as the oracle sees them: the bf16 weights, or for 4-bit workloads
+    the dequantized codes and scales (host quantizer, then ``oracle.dequant_q4``)."""
+    if w.quant == "int4":
+        return lambda e: tuple(oracle.dequant_q4(c, s) for c, s in wl.host_expert_q4(w, e))
+    return lambda e: wl.host_expert(w, e)
+
+
 def oracle_forward_tokens(w, tokens, ids_gpu=None, score_bias=None):
     """Oracle output for the given tokens.  Where ids_gpu differs from the oracle's choice on a
     near-tie, the oracle is evaluated with the GPU's ids (weights from the oracle's scores)."""
@@ -68,7 +76,7 @@ def oracle_forward_tokens(w, tokens, ids_gpu=None, score_bias=None):
                 s = scores[t, ids_gpu[t]]
                 wts[t] = w.rsf * s / s.sum()
     shared = wl.host_shared(w)
-    y = oracle.moe_forward_given_routing(x, ids, wts, lambda e: wl.host_expert(w, e), shared)
+    y = oracle.moe_forward_given_routing(x, ids, wts, oracle_expert(w), shared)
     return y, ids, wts, gap
 
 

@@ -114,6 +114,29 @@ def test_operands_past_4_gib_are_unsupported():
     assert rc == moe.MOE_ERR_UNSUPPORTED
 
 
+def test_q4_forward_argument_checks():
+    # the 4-bit forward checks its config, pointers and workspace before launching anything
+    lib = moe.load_library()
+    fake = ctypes.c_void_p(0x1000)
+
+    def call(cfg, T=64, x=fake, codes=fake, shared=fake, ws=1 << 40):
+        return lib.moe_forward_q4(ctypes.byref(cfg), T, x, fake, None, None, codes, fake, fake, fake, fake, fake,
+                                  shared, fake, fake, fake, None, None, fake, ws, None)
+
+    cfg = moe.make_config()
+    need = moe.moe_workspace_size(cfg, moe.MOE_OP_FORWARD_Q4, 64)
+    # x16 (64 x 7168 f16), h (576 x 2048) and y_rows (576 x 7168) at least
+    assert need > 64 * 7168 * 2 + 576 * (2048 + 7168) * 2
+    assert call(cfg, x=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(cfg, codes=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(cfg, shared=None) == moe.MOE_ERR_INVALID_ARG and "shared" in moe.moe_last_error()
+    assert call(cfg, ws=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(cfg, T=0, x=None, codes=None, shared=None, ws=0) == moe.MOE_OK
+    for bad in (moe.make_config(hidden_size=7168 + 128), moe.make_config(dtype="f32")):
+        assert call(bad) == moe.MOE_ERR_UNSUPPORTED
+        assert lib.moe_workspace_size(ctypes.byref(bad), moe.MOE_OP_FORWARD_Q4, 64, 0) == 0
+
+
 def test_zero_tokens_is_a_no_op():
     cfg = moe.make_config()
     lib = moe.load_library()
