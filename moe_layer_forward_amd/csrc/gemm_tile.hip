@@ -76,6 +76,8 @@ struct TileArgs {
   int out_bf16;
   const float* row_scale;
   int H, I, n_ntiles;
+  int n_ksplit;  // down: K ranges per output tile (partial sums go to part)
+  float* part;   // [n_ksplit, max_rows, H] fp32 when n_ksplit > 1
 };
 
 struct TileRows {
@@ -83,11 +85,16 @@ struct TileRows {
   int64_t rbeg, rend;
 };
 
-__device__ __forceinline__ bool tile_of(const TileArgs& p, int& nt, TileRows& t) {
+// Work item -> (row tile, column slab nt, K range ks); consecutive items (one XCD's share) walk the
+// slabs and K ranges of one row tile.
+__device__ __forceinline__ bool tile_of(const TileArgs& p, int& nt, int& ks, TileRows& t) {
   int64_t L;
-  if (!xcd_work_item((int64_t)p.counters[1] * p.n_ntiles, L)) return false;
-  const int tile = (int)(L / p.n_ntiles);
-  nt = (int)(L % p.n_ntiles);
+  const int per_tile = p.n_ntiles * p.n_ksplit;
+  if (!xcd_work_item((int64_t)p.counters[1] * per_tile, L)) return false;
+  const int tile = (int)(L / per_tile);
+  const int rem = (int)(L % per_tile);
+  nt = rem / p.n_ksplit;
+  ks = rem % p.n_ksplit;
   t.g = p.tiles[2 * tile];
   const int m0 = p.tiles[2 * tile + 1];
   int64_t r0 = p.group_offsets[t.g], r1 = p.group_offsets[t.g + 1];
@@ -346,9 +353,9 @@ __device__ __forceinline__ void a_offsets(Operands& o, int K, RowOf row_of) {
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gateup_tile_kernel(TileArgs p) {
   __shared__ __align__(16) char a0[kStageBytes], a1[kStageBytes], a2[kStageBytes], a3[kStageBytes];
   const Ring smem{{a0, a1, a2, a3}};
-  int nt;
+  int nt, ks;
   TileRows t;
-  if (!tile_of(p, nt, t)) return;
+  if (!tile_of(p, nt, ks, t)) return;
   const int H = p.H, I = p.I;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool sh = t.g == p.w.shared_group;
@@ -389,9 +396,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void down_tile_kernel(TileArgs p) {
   __shared__ __align__(16) char a0[kStageBytes], a1[kStageBytes], a2[kStageBytes], a3[kStageBytes];
   const Ring smem{{a0, a1, a2, a3}};
-  int nt;
+  int nt, ks;
   TileRows t;
-  if (!tile_of(p, nt, t)) return;
+  if (!tile_of(p, nt, ks, t)) return;
   const int H = p.H, I = p.I;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint16_t* wd = t.g == p.w.shared_group ? (const uint16_t*)p.w.s_down
@@ -399,24 +406,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int c0 = nt * 256 + 32 * w;  // first output column of this wave (H is a multiple of 32)
   const bool cols_ok = c0 < H;       // the last slab of an H that is not a multiple of 256
 
+  // this item's K range [k0, k0 + kc) of the h rows and of W_down's rows
+  const int kc = I / p.n_ksplit, k0 = ks * kc;
   Operands o;
-  o.a_base = reinterpret_cast<const char*>(p.a);
+  o.a_base = reinterpret_cast<const char*>(p.a + k0);
   a_offsets(o, I, [&](int rl) -> int64_t {
     const int64_t r = t.rbeg + rl;
     return r < t.rend ? r : t.rbeg;
   });
 #pragma unroll
   for (int s = 0; s < kNSub; ++s)  // idle waves re-read the first rows
-    o.b[s] = reinterpret_cast<const char*>(wd + (int64_t)((cols_ok ? c0 : 0) + 16 * s) * I);
+    o.b[s] = reinterpret_cast<const char*>(wd + (int64_t)((cols_ok ? c0 : 0) + 16 * s) * I + k0);
   o.b_off = (uint32_t)((lane & 15) * I * 2 + 16 * (lane >> 4));
 
   const int64_t rbeg = t.rbeg, rend = t.rend;
   const int m_valid = (int)(rend - rbeg);
   const float* row_scale = p.row_scale;
-  void* out = p.out;
-  run_tile(o, m_valid, I, smem, [&](const auto& acc) {
+  const bool split = p.n_ksplit > 1;
+  void* out = split ? static_cast<void*>(p.part + (int64_t)ks * p.max_rows * H) : p.out;
+  run_tile(o, m_valid, kc, smem, [&](const auto& acc) {
     constexpr int n16 = sizeof(acc) / sizeof(acc[0]);
-    if (p.out_bf16) {
+    if (p.out_bf16 && !split) {
       using Out = OutTile<256>;
       block_sync_lds();  // every wave is done reading the A ring
       static_for<n16>([&](auto ic) {
@@ -433,7 +443,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       Out::store(smem, m_valid, static_cast<uint16_t*>(out), H, rbeg, nt * 256, H);
       return;
     }
-    // fp32 rows (a caller's choice in moe_grouped_swiglu): direct stores
+    // fp32 rows (a caller's choice in moe_grouped_swiglu, or a K range's partial sums): direct stores
     if (!cols_ok) return;
 #pragma unroll
     for (int i = 0; i < n16; ++i)
@@ -449,26 +459,78 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   });
 }
 
-unsigned grid_for(int64_t max_tiles, int n_ntiles) {
-  int64_t n = max_tiles * n_ntiles;
+unsigned grid_for(int64_t max_tiles, int n_ntiles, int n_ksplit = 1) {
+  int64_t n = max_tiles * n_ntiles * n_ksplit;
   n = (n + kXcds - 1) / kXcds * kXcds;
   return (unsigned)n;
 }
 
+// y[r, :] = sum over the K ranges of part[ks, r, :] (in ks order), rows [0, offsets[G]) clamped to
+// max_rows; 8 columns per thread.
+__global__ __launch_bounds__(256) void ksplit_reduce_kernel(const float* __restrict__ part, int n_ksplit,
+                                                            const int32_t* __restrict__ offsets, int G,
+                                                            int64_t max_rows, int H, void* __restrict__ out,
+                                                            int out_bf16) {
+  int64_t rows = offsets[G];
+  if (rows > max_rows) rows = max_rows;
+  const int64_t n = rows * (H / 8);
+  const int64_t plane = max_rows * H;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = 8 * i;  // row e / H, columns e % H .. +7
+    f32x4 lo = *reinterpret_cast<const f32x4*>(part + e), hi = *reinterpret_cast<const f32x4*>(part + e + 4);
+    for (int ks = 1; ks < n_ksplit; ++ks) {
+      lo += *reinterpret_cast<const f32x4*>(part + ks * plane + e);
+      hi += *reinterpret_cast<const f32x4*>(part + ks * plane + e + 4);
+    }
+    if (out_bf16) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        w[j] = (uint32_t)f32_to_bf16(lo[2 * j]) | ((uint32_t)f32_to_bf16(lo[2 * j + 1]) << 16);
+        w[2 + j] = (uint32_t)f32_to_bf16(hi[2 * j]) | ((uint32_t)f32_to_bf16(hi[2 * j + 1]) << 16);
+      }
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + e) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + e) = lo;
+      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + e + 4) = hi;
+    }
+  }
+}
+
 }  // namespace
+
+int down_tile_ksplit(int64_t max_rows, int G, int H, int I) {
+  // items of the unsplit launch if the rows formed full tiles; split K until about 512 work-groups
+  // (two per CU) are busy, keeping at least 8 K steps of 64 per range
+  const int64_t items = ((max_rows + kTileM - 1) / kTileM) * ((H + 255) / 256);
+  (void)G;
+  int split = 1;
+  while (split < 16 && items * split * 2 <= 512 && I % (2 * split * kBK) == 0 && I / (2 * split) >= 8 * kBK)
+    split *= 2;
+  return split;
+}
 
 hipError_t launch_gateup_tile_bf16(const Groups& g, const Weights& w, const uint16_t* x, uint16_t* h, int H, int I,
                                    hipStream_t s) {
-  TileArgs p{g.group_offsets, g.row_index, g.tiles, g.counters, g.max_rows, w, x, h, 1, nullptr, H, I, I / 128};
+  TileArgs p{g.group_offsets, g.row_index, g.tiles, g.counters, g.max_rows, w, x, h, 1, nullptr, H, I, I / 128,
+             1, nullptr};
   gateup_tile_kernel<<<grid_for(g.max_tiles, p.n_ntiles), kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 
 hipError_t launch_down_tile_bf16(const Groups& g, const Weights& w, const uint16_t* h, void* y_rows, bool y_bf16,
-                                 const float* row_scale, int H, int I, hipStream_t s) {
+                                 const float* row_scale, float* part, int H, int I, hipStream_t s) {
+  const int split = down_tile_ksplit(g.max_rows, g.n_groups, H, I);
   TileArgs p{g.group_offsets, nullptr, g.tiles, g.counters, g.max_rows, w, h, y_rows, y_bf16 ? 1 : 0, row_scale,
-             H, I, (H + 255) / 256};
-  down_tile_kernel<<<grid_for(g.max_tiles, p.n_ntiles), kThreads, 0, s>>>(p);
+             H, I, (H + 255) / 256, split, part};
+  down_tile_kernel<<<grid_for(g.max_tiles, p.n_ntiles, split), kThreads, 0, s>>>(p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || split == 1) return e;
+  const int64_t n = g.max_rows * (H / 8);
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  ksplit_reduce_kernel<<<(unsigned)blocks, 256, 0, s>>>(part, split, g.group_offsets, g.n_groups, g.max_rows, H,
+                                                        y_rows, y_bf16 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -104,8 +104,11 @@ hipError_t launch_gateup_tile_bf16(const Groups& g, const Weights& w, const uint
 // y_rows[r, H] = row_scale[r] * h[r] Wd^T   (y fp32 when y_bf16 == false)
 hipError_t launch_down_stream_bf16(const Groups& g, const Weights& w, const uint16_t* h, void* y_rows,
                                    bool y_bf16, const float* row_scale, int H, int I, hipStream_t s);
+// With few row tiles the K dimension is split (down_tile_ksplit ranges, partial sums in part,
+// [split, max_rows, H] fp32, then a reduction into y_rows).
 hipError_t launch_down_tile_bf16(const Groups& g, const Weights& w, const uint16_t* h, void* y_rows,
-                                 bool y_bf16, const float* row_scale, int H, int I, hipStream_t s);
+                                 bool y_bf16, const float* row_scale, float* part, int H, int I, hipStream_t s);
+int down_tile_ksplit(int64_t max_rows, int G, int H, int I);
 // Rows per tile used by the tile kernels' plan.
 constexpr int kTileM = 256;  // rows per tile of the tile GEMMs
 

@@ -139,10 +139,11 @@ int check_forward_spans(const moe_config* c, int64_t T) {
 
 bool use_stream_kernels(int64_t max_rows, int G) { return max_rows <= 4LL * G; }
 
-// Grouped SwiGLU scratch: h, then the plan.
+// Grouped SwiGLU scratch: h, the plan, and the down GEMM's K-range partial sums when it splits K.
 struct SwigluWs {
   void* h;
   moe::Groups g;
+  float* part;
 };
 
 // Plan buffers of G groups over at most max_rows rows.
@@ -162,12 +163,17 @@ SwigluWs carve_swiglu(Carver& cv, const moe_config* c, int G, int64_t max_rows) 
   SwigluWs w{};
   w.h = cv.take<char>(max_rows * c->moe_intermediate_size * (int64_t)elem_bytes(c->dtype));
   w.g = carve_plan(cv, G, max_rows);
+  w.part = nullptr;
+  if (c->dtype == MOE_BF16 && !use_stream_kernels(max_rows, G)) {
+    const int split = moe::down_tile_ksplit(max_rows, G, c->hidden_size, c->moe_intermediate_size);
+    if (split > 1) w.part = cv.take<float>((int64_t)split * max_rows * c->hidden_size);
+  }
   return w;
 }
 
 // Launch plan + both grouped GEMMs over prepared groups.
 hipError_t run_swiglu(const moe_config* c, const moe::Groups& g, const moe::Weights& w, const void* x, void* h,
-                      const float* row_scale, void* y_rows, bool y_bf16, hipStream_t s) {
+                      float* part, const float* row_scale, void* y_rows, bool y_bf16, hipStream_t s) {
   const int H = c->hidden_size, I = c->moe_intermediate_size;
   hipError_t e = timed("plan", s, [&] { return moe::launch_plan(g, s); });
   if (e != hipSuccess) return e;
@@ -194,7 +200,8 @@ hipError_t run_swiglu(const moe_config* c, const moe::Groups& g, const moe::Weig
   });
   if (e != hipSuccess) return e;
   return timed("down_tile", s, [&] {
-    return moe::launch_down_tile_bf16(g, w, static_cast<const uint16_t*>(h), y_rows, y_bf16, row_scale, H, I, s);
+    return moe::launch_down_tile_bf16(g, w, static_cast<const uint16_t*>(h), y_rows, y_bf16, row_scale, part, H, I,
+                                      s);
   });
 }
 
@@ -255,7 +262,7 @@ int run_after_routing(const moe_config* c, int64_t T, const void* x, const int32
     wt.shared_group = E;
   }
   const bool rows_bf16 = c->dtype == MOE_BF16;
-  e = run_swiglu(c, g, wt, x, w.sw.h, nullptr, w.y_rows, rows_bf16, s);
+  e = run_swiglu(c, g, wt, x, w.sw.h, w.sw.part, nullptr, w.y_rows, rows_bf16, s);
   if (e != hipSuccess) return device_status(e, "grouped swiglu");
   const char* yr = static_cast<const char*>(w.y_rows);
   const void* ysh = shared ? yr + P * H * (int64_t)elem_bytes(c->dtype) : nullptr;
@@ -469,7 +476,7 @@ int moe_grouped_swiglu(const moe_config* cfg, int32_t n_groups, const int32_t* g
   wt.gate = w_gate;
   wt.up = w_up;
   wt.down = w_down;
-  hipError_t e = run_swiglu(cfg, w.g, wt, x, w.h, row_scale, y_rows, y_dtype == MOE_BF16,
+  hipError_t e = run_swiglu(cfg, w.g, wt, x, w.h, w.part, row_scale, y_rows, y_dtype == MOE_BF16,
                             static_cast<hipStream_t>(stream));
   return device_status(e, "grouped swiglu");
 }
