@@ -193,8 +193,8 @@ int moe_forward_routed(const moe_config* cfg, int64_t T, const void* x, const in
  * q*s is rounded once to binary16, SiLU(g)*u is rounded to binary16 between the two matmuls,
  * y_rows to bf16.  The shared expert and the combine are as in moe_forward.
  * Shapes: as moe_forward, with hidden_size and moe_intermediate_size multiples of 256.
- * Each routed expert that received tokens has its codes and scales read once per 16 of its
- * rows (the kernels stream weights; they are built for decode-sized T).
+ * Each routed expert that received tokens has its codes and scales read once per 4 of its rows
+ * (the kernels stream weights; they are built for decode-sized T, about one row per expert).
  * Workspace: moe_workspace_size(cfg, MOE_OP_FORWARD_Q4, T, 0). */
 int moe_forward_q4(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
                    const float* score_bias, const float* logit_offset, const uint32_t* gate_codes,

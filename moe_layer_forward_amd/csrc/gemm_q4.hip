@@ -4,25 +4,26 @@
 // 4-bit integers, one scale per 32 consecutive inputs, symmetric (w = q * s).  In memory:
 //   codes  [G, N, K/8]  uint32: q of input k in bits 4*(k % 8) of word k/8, two's complement
 //   scales [G, N, K/32] binary16
-// The page keeps the computation high-precision (only storage is quantized).  gfx950 has packed
-// f16 arithmetic but no packed bf16 arithmetic, so the weights are decoded to f16 (q*s rounded
-// once) and the expert matmuls run on v_mfma_f32_16x16x32_f16 with f16 token rows and fp32
-// accumulation; the token rows are converted from bf16 once per layer (f16_rows_kernel).
+// Only the storage is quantized ("Kimi K2.5 架构 QA" Q7.1): the codes enter the matmuls as exact
+// integers and each group's scale is applied in fp32.  The matmuls run on v_mfma_f32_16x16x32_f16,
+// with the token rows converted once from bf16 to binary16 (f16_rows_kernel) and h kept in binary16.
 //
-// Decoding two codes costs four instructions: the 8 nibbles of a word are made offset-binary with
-// one xor, ((w >> 4i) & 0x000F000F) | 0x64006400 puts codes i and i+4 into the mantissas of two
-// binary16 values 1024 + u, one packed subtract makes them exact integers and one packed multiply
-// applies the scale.  The pairs come out as inputs (i, i+4), so every operand of these matmuls keeps
-// each group of 8 consecutive inputs in the order 0,4,1,5,2,6,3,7 (the f16 token rows and the f16 h
-// are written that way); the dot product over a group is unchanged by the common permutation.
+// Decoding: after xor with 0x88888888 a code is offset binary u = q + 8; a field in bits 0..3 of a
+// 16-bit half ORed into 0x6400 reads 1024 + u, a field in bits 4..7 ORed into 0x5400 reads 64 + u,
+// and since the OR constant is disjoint from the field, xor + mask + OR is one v_bitop3_b32.  A
+// word's 8 codes come out in the order 0,4,1,5,2,6,3,7, so every operand keeps each group of 8
+// inputs in that order (x16 and h are written that way; the dot product is unchanged).  Per group
+// of 32 inputs one MFMA against the constant -(1032 | 72) seeds the accumulator of the two weight
+// sets' MFMAs, which leaves c = sum x*q exactly in fp32; then acc += s * c.
 //
-// The stream itself is the bf16 weight stream's (gemm_stream.hip): a wave streams two 16-row sets
-// of weight rows (gate + up of 16 h columns, or 32 rows of W_down) through a wave-private 4-stage
-// LDS ring of direct global->LDS loads, one instruction = 8 rows x 128 contiguous bytes (whole
-// lines) with the streaming policy; the 16-byte chunk c of a 128-byte row r sits at c ^ ((r >> 1) & 7)
-// so the 16 rows of one B-operand read hit different banks.  Scales and token rows go to register
-// rings in the same step as their codes.  A step covers 256 inputs: 8 groups, 8 MFMAs per set and
-// pass.  Work-groups = 4 waves; groups from the plan's active list, largest first.
+// The stream: a wave streams two 16-row sets of weight rows (gate + up of 16 h columns, or 32 rows
+// of W_down) through a 4-stage LDS ring of direct buffer->LDS loads, one instruction = 8 rows x 128
+// contiguous bytes (whole lines) with the streaming policy; the 16-byte chunk c of a 128-byte row r
+// sits at c ^ ((r >> 1) & 7) so the 16 rows of one B-operand read hit different banks.  A step
+// covers 256 inputs (8 groups).  The token rows of a pass (4 rows) are shared by the work-group's 4
+// waves through the same ring (a barrier per step); the scales come a 4-step block at a time.
+// Work-groups = 4 waves; groups from the plan's active list, largest first; the first work-groups
+// of a launch stream the bf16 shared expert instead.
 #include <type_traits>
 
 #include "kernels.h"
@@ -40,11 +41,15 @@ constexpr int kWaves = 4;
 constexpr int kStepK = 256;             // inputs per step
 constexpr int kCodeRowB = kStepK / 2;   // 128 bytes of codes per row per step
 constexpr int kSetCodeB = 16 * kCodeRowB;
-constexpr int kWaveB = 2 * kSetCodeB;   // one wave's part of one ring stage
-constexpr int kStageB = kWaves * kWaveB;
+constexpr int kWaveB = 2 * kSetCodeB;   // one wave's part of the codes of one ring stage
+constexpr int kCodesB = kWaves * kWaveB;
+constexpr int kPassRows = 4;           // token rows per pass over the weights (MFMA rows 4.. are padding)
+constexpr int kARowB = 2 * kStepK;      // 512 bytes of one f16 token row per step
+constexpr int kAB = kPassRows * kARowB; // a pass's token rows of one step, shared by the waves
+constexpr int kStageB = kCodesB + kAB;
 constexpr int kD = 4;                   // ring stages = steps in flight = steps per scale block
 constexpr int kScaleRowB = kD * 16;     // a row's binary16 scales for the kD steps of a block
-constexpr int kScaleSetB = 16 * kScaleRowB;
+constexpr int kScaleSetB = 16 * kScaleRowB;  // = one 64-lane 16-byte store
 constexpr int kScaleWaveB = 2 * kScaleSetB;  // one wave's part of one scale buffer
 
 // Compile-time loop: f(integral_constant<int, I>) for I = 0 .. N-1.
@@ -129,35 +134,31 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
 
 typedef __attribute__((address_space(3))) void* LdsPtr;
 
-// Register ring slot of one step: the f16 token-row fragments of the step's 8 groups.
-struct Slot {
-  u32x4 a[8];
-};
+// Token rows in a ring stage: row r of the pass at r * kARowB, its 16-byte piece g at position
+// g ^ (4 * r), so the rows one A-operand read touches fall in different banks.
+__device__ __forceinline__ int a_pos(int r, int g) { return g ^ (4 * r); }
 
 struct Q4Stream {
-  static constexpr int kLoads = 2 * 2 + 8;  // per step: codes (direct to LDS), token rows
+  static constexpr int kLoads = 2 * 2 + 1;  // per step: codes, and this wave's half of the token rows
   static constexpr int kScaleLoads = 2;     // per block of kD steps: scales (into registers)
-  static_assert((kD - 1) * kLoads + kScaleLoads <= 63, "vmcnt");
+  static_assert(2 * kLoads + kScaleLoads <= 63, "vmcnt");
 
   const void* cb[2];        // codes of each set's 16 rows (uniform)
   const void* sb[2];        // scales of each set's 16 rows (uniform)
   const void* abase;        // token rows (f16)
   uint32_t c_bytes, s_bytes, a_bytes;
   uint32_t c_off[2];        // lane offsets of the two direct loads of a set (row, swizzled chunk)
-  uint32_t s_off;           // lane offset of the scale load: row lane/4, bytes 16*(lane%4)..+15 of a block
-  uint32_t a_off;           // lane offset of its token-row fragment (row, k-quarter)
-  int wave_off, sc_wave_off;
+  uint32_t s_off;           // lane offset of the scale load (row lane/4, piece lane%4 of a block)
+  uint32_t a_off;           // lane offset of this wave's token-row load (row, swizzled piece)
+  int wave_off, sc_wave_off, a_dst;  // this wave's codes, scale buffer, and token-row half
 
-  // Loads of step st into ring stage d and slot sl; past the last step (nsteps) they read nothing
-  // and fill zeros.
-  __device__ __forceinline__ void issue(char* const (&ring)[kD], int d, int st, int nsteps, Slot& sl) const {
+  // The codes of step st into ring stage d; past the last step (nsteps) they read nothing and fill
+  // zeros.
+  __device__ __forceinline__ void issue_codes(char* const (&ring)[kD], int d, int st, int nsteps) const {
     // st opaque to the optimiser: otherwise it precomputes addresses per (step, load) of the
     // prologue, keeps them live across the whole pass and spills them
     asm volatile("" : "+s"(st));
-    const bool live = st < nsteps;
-    // record counts through readfirstlane: the descriptors stay scalar (no per-load waterfall loops)
-    const uint32_t cn = __builtin_amdgcn_readfirstlane(live ? c_bytes : 0u);
-    const uint32_t an = __builtin_amdgcn_readfirstlane(live ? a_bytes : 0u);
+    const uint32_t cn = __builtin_amdgcn_readfirstlane(st < nsteps ? c_bytes : 0u);
     char* dst = ring[d] + wave_off;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
@@ -167,15 +168,20 @@ struct Q4Stream {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (LdsPtr)(dst + r * kSetCodeB + i * 1024), 16,
                                                  c_off[i] + (uint32_t)st * kCodeRowB, 0, 0, 2);
     }
-    const Rsrc ra = make_rsrc(abase, an);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      sl.a[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_off + (uint32_t)st * (2 * kStepK) + 64 * j, 0, 0);
   }
 
-  // The scales of steps st .. st + kD - 1 (st a multiple of kD) into registers: one 64-byte piece
-  // per row and set, lane l holding bytes 16*(l%4)..+15 of row l/4 (so each scale line is fetched
-  // in two requests, not eight).  Past the last step they read nothing.
+  // Half of the pass's token rows of step st (2 rows, 1 KiB) into ring stage d.  Waves w and w + 2
+  // load the same half: identical bytes to the same place, and every wave issues the same loads.
+  __device__ __forceinline__ void issue_rows(char* const (&ring)[kD], int d, int st, int nsteps) const {
+    asm volatile("" : "+s"(st));
+    const uint32_t an = __builtin_amdgcn_readfirstlane(st < nsteps ? a_bytes : 0u);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(abase, an), (LdsPtr)(ring[d] + kCodesB + a_dst), 16,
+                                             a_off + (uint32_t)st * kARowB, 0, 0, 0);
+  }
+
+  // The scales of steps st .. st + kD - 1 (st a multiple of kD) into registers: lane l holds the
+  // 16 bytes of step st + l%4 of row l/4 (each scale line in two requests, not eight).  Past the
+  // last step they read nothing.
   __device__ __forceinline__ void issue_scales(int st, int nsteps, u32x4 (&sr)[2]) const {
     asm volatile("" : "+s"(st));
     const uint32_t sn = __builtin_amdgcn_readfirstlane(st < nsteps ? s_bytes : 0u);
@@ -195,34 +201,36 @@ struct Q4Stream {
 
   // One step: for each group j of 32 inputs, c = A_j . (-bias) + A_j . (1024|64 + u) = A_j . q (exact
   // integer weights, fp32 sums), then acc += s_j * c with the group's scale in fp32.  Software
-  // pipelined by hand: the code words are read one group ahead, and group j's products are scaled
-  // into acc while group j+1's matmuls run (scheduling barriers keep the compiler from hoisting
-  // more and running out of registers).
-  // d: ring stage (= step % kD); sc: the scale buffer holding the step's block.
-  __device__ __forceinline__ void compute(char* const (&ring)[kD], int d, const char* sc, const Slot& sl,
-                                          f32x4 (&acc)[2]) const {
+  // pipelined by hand: code words and token-row fragments are read one group ahead, and group j's
+  // products are scaled into acc while group j+1's matmuls run (scheduling barriers keep the
+  // compiler from hoisting more).  d: ring stage; sc: the scale buffer holding the step's block.
+  __device__ __forceinline__ void compute(char* const (&ring)[kD], int d, const char* sc, f32x4 (&acc)[2]) const {
     const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
     const char* src = ring[d] + wave_off + c * kCodeRowB + 4 * q;
+    const int ar = c & (kPassRows - 1);  // MFMA rows 4.. repeat rows 0..3 (never stored)
+    const char* arow = ring[d] + kCodesB + ar * kARowB;
     u32x4 sv[2];  // the step's 8 scales of row c of each set
 #pragma unroll
     for (int r = 0; r < 2; ++r)
       sv[r] = *reinterpret_cast<const u32x4*>(sc + sc_wave_off + r * kScaleSetB + c * kScaleRowB + d * 16);
     const f16x8 nb = bias_operand();
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    auto read = [&](auto jc, uint32_t (&wd)[2]) {
+    auto read = [&](auto jc, uint32_t (&wd)[2], u32x4& af) {
       constexpr int j = decltype(jc)::value;
 #pragma unroll
       for (int r = 0; r < 2; ++r)
         wd[r] = *reinterpret_cast<const uint32_t*>(src + r * kSetCodeB + ((j ^ code_swz(c)) << 4));
+      af = *reinterpret_cast<const u32x4*>(arow + (a_pos(ar, 4 * j + q) << 4));
     };
     uint32_t wd[2][2];
+    u32x4 af[2];
     f32x4 pend[2];
     float pend_s[2];
-    read(std::integral_constant<int, 0>{}, wd[0]);
+    read(std::integral_constant<int, 0>{}, wd[0], af[0]);
     static_for<8>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
-      if constexpr (j + 1 < 8) read(std::integral_constant<int, j + 1>{}, wd[(j + 1) & 1]);
-      const f16x8 a = __builtin_bit_cast(f16x8, sl.a[j]);
+      if constexpr (j + 1 < 8) read(std::integral_constant<int, j + 1>{}, wd[(j + 1) & 1], af[(j + 1) & 1]);
+      const f16x8 a = __builtin_bit_cast(f16x8, af[j & 1]);
       const f32x4 cb = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, nb, zero, 0, 0, 0);
       f32x4 cur[2];
 #pragma unroll
@@ -246,32 +254,39 @@ struct Q4Stream {
       for (int e = 0; e < 4; ++e) acc[r][e] = __builtin_fmaf(pend_s[r], pend[r][e], acc[r][e]);
   }
 
-  // The K loop of one pass.  Every step issues the loads of the step kD ahead, unconditionally (past
-  // the end they read nothing), and the first step of each block of kD steps first loads the next
-  // block's scales, so the waits are fixed; steps past the end skip the multiply.
+  // The K loop of one pass.  The token rows of a step are shared by the work-group's waves, so
+  // every step starts with a barrier: after it, every wave's rows of this step have arrived and
+  // every wave is done with the previous step's stage, whose rows are then refilled with those of
+  // step g + kD - 1 (the stage's codes were refilled with that step's at the end of the previous
+  // step).  Loads past the end read nothing, so the waits are fixed; steps
+  // past the end skip the multiply.  Loads in issue order: ... rows(g), codes(g+1), rows(g+1),
+  // codes(g+2), ..., with a block's scales just before the codes of its first step.
   __device__ __forceinline__ void run(char* const (&ring)[kD], char* sc, int nsteps, f32x4 (&acc)[2]) const {
-    Slot sl[kD];
     u32x4 sr[2];
+    __builtin_amdgcn_s_barrier();  // the previous pass is done with the shared rows
     issue_scales(0, nsteps, sr);
     static_for<kD>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      issue(ring, i, i, nsteps, sl[i]);
+      issue_codes(ring, i, i, nsteps);
+      if constexpr (i + 1 < kD) issue_rows(ring, i, i, nsteps);
     });
     for (int g = 0; g < nsteps; g += kD) {
       static_for<kD>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        // after step g + i's loads: the next kD - 1 steps' loads, and the next block's scales among
-        // them unless this step starts a block
-        wait_vmcnt<(kD - 1) * kLoads + (i == 0 ? 0 : kScaleLoads)>();
+        // after rows(g + i): codes and rows of the next kD - 2 steps, the codes of the one after,
+        // and a block's scales among them unless this step starts a block
+        wait_vmcnt<(kD - 1) * 4 + (kD - 2) * 1 + (i == 0 ? 0 : kScaleLoads)>();
+        __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
+        issue_rows(ring, (i + kD - 1) % kD, g + i + kD - 1, nsteps);
         if constexpr (i == 0) store_scales(sc, sr);  // this block's scales, loaded a block ago
-        if (g + i < nsteps) compute(ring, i, sc, sl[i], acc);
+        if (g + i < nsteps) compute(ring, i, sc, acc);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this stage's LDS reads are done
         if constexpr (i == 0) issue_scales(g + kD, nsteps, sr);
-        issue(ring, i, g + i + kD, nsteps, sl[i]);
+        issue_codes(ring, i, g + i + kD, nsteps);
       });
     }
-    wait_vmcnt<0>();  // the last block's padding loads still write (zeros) into the ring
+    wait_vmcnt<0>();  // the last loads past the end still write (zeros) into the ring
   }
 };
 
@@ -280,23 +295,28 @@ __device__ __forceinline__ void q4_pass(const Q4Args& p, char* const (&ring)[kD]
                                         int n0, int64_t mb, int64_t r1) {
   const int H = p.H, I = p.I, K = SWIGLU ? H : I;
   const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   Q4Stream s = base;
-  {
-    const int64_t r = mb + (lane & 15);
+  {  // this wave's rows 2(w % 2) + lane/32, piece position lane % 32
+    const int rl = 2 * (wave & 1) + (lane >> 5);
+    const int64_t r = mb + rl;
     const int64_t rr = r < r1 ? r : mb;  // rows past the group end repeat its first row, never stored
     const int64_t src = SWIGLU ? (p.row_index ? (int64_t)p.row_index[rr] : rr) : rr;
-    s.a_off = (uint32_t)(src * K * 2 + (lane >> 4) * 16);
+    s.a_off = (uint32_t)(src * K * 2 + (a_pos(rl, lane & 31) << 4));
   }
+  s.a_dst = (wave & 1) * 2 * kARowB;
   f32x4 acc[2];
   acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
   s.run(ring, sc, K / kStepK, acc);
 
-  // lane holds rows mb + 4*(lane/16) + e, column n0 + lane%16 (+16 for set 1 of down)
+  // lane holds MFMA rows 4*(lane/16) + e, column n0 + lane%16 (+16 for set 1 of down); the pass's
+  // rows are MFMA rows 0 .. kPassRows-1
   const int col = n0 + (lane & 15);
+  const int64_t rend = mb + kPassRows < r1 ? mb + kPassRows : r1;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int64_t row = mb + 4 * (lane >> 4) + e;
-    if (row >= r1) continue;
+    if ((lane >> 4) != 0 || row >= rend) continue;
     if (SWIGLU) {
       // h in f16, each group of 8 columns in the operand order of the down matmul
       const _Float16 v = (_Float16)swiglu_f32(acc[0][e], acc[1][e]);
@@ -495,7 +515,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   s.wave_off = wave * kWaveB;
   s.sc_wave_off = wave * kScaleWaveB;
 #if defined(__HIP_DEVICE_COMPILE__)
-  for (int64_t mb = r0; mb < r1; mb += 16) q4_pass<SWIGLU>(p, ring, sc, s, n0, mb, r1);
+  for (int64_t mb = r0; mb < r1; mb += kPassRows) q4_pass<SWIGLU>(p, ring, sc, s, n0, mb, r1);
 #else
   (void)s;
   (void)n0;
