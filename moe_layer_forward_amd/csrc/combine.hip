@@ -3,7 +3,7 @@
 // shared expert's output.  Here every token gathers its K rows instead, so no atomics are needed and
 // the result is bitwise reproducible:
 //     y[t] = sum_k w[t,k] * y_rows[pair_row[t,k]]  (k ascending)  + y_shared[t],
-// accumulated in fp32 and rounded once.  One work-group per token, 16-byte loads.
+// accumulated in fp32 and rounded once.  One thread per (token, 8 columns), 16-byte loads.
 #include "kernels.h"
 
 namespace moe {
@@ -32,35 +32,53 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                                                       const int32_t* __restrict__ pair_row,
                                                       const float* __restrict__ weights,
                                                       const void* __restrict__ y_shared, void* __restrict__ y,
-                                                      int K, int H) {
-  const int64_t t = blockIdx.x;
-  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < K; ++k) {
-      const int64_t r = pair_row[t * K + k];
-      const float w = weights[t * K + k];
-      float v[8];
-      load8<ROWS_BF16>(y_rows, r * H + c, v);
+                                                      int64_t T, int K, int H) {
+  // one thread per (token, 8 columns); the K row loads are issued four at a time, the sum keeps
+  // k order
+  const int cpr = H / 8;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T * cpr) return;
+  const int64_t t = i / cpr;
+  const int c = (int)(i % cpr) * 8;
+  const int32_t* pr = pair_row + t * K;
+  const float* wt = weights + t * K;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int k = 0;
+  for (; k + 4 <= K; k += 4) {
+    float v[4][8], w[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+    for (int u = 0; u < 4; ++u) {
+      w[u] = wt[k + u];
+      load8<ROWS_BF16>(y_rows, (int64_t)pr[k + u] * H + c, v[u]);
     }
-    if (y_shared) {
-      float v[8];
-      load8<ROWS_BF16>(y_shared, t * H + c, v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += v[i];
-    }
-    if (Y_BF16) {
-      uint32_t w[4];
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[i] = (uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16);
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + t * H + c) = uint4{w[0], w[1], w[2], w[3]};
-    } else {
-      float4* p = reinterpret_cast<float4*>(static_cast<float*>(y) + t * H + c);
-      p[0] = float4{acc[0], acc[1], acc[2], acc[3]};
-      p[1] = float4{acc[4], acc[5], acc[6], acc[7]};
-    }
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w[u], v[u][e], acc[e]);
+  }
+  for (; k < K; ++k) {
+    float v[8];
+    const float w = wt[k];
+    load8<ROWS_BF16>(y_rows, (int64_t)pr[k] * H + c, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, v[e], acc[e]);
+  }
+  if (y_shared) {
+    float v[8];
+    load8<ROWS_BF16>(y_shared, t * H + c, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += v[e];
+  }
+  if (Y_BF16) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)f32_to_bf16(acc[2 * e]) | ((uint32_t)f32_to_bf16(acc[2 * e + 1]) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + t * H + c) = uint4{w[0], w[1], w[2], w[3]};
+  } else {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(y) + t * H + c);
+    p[0] = float4{acc[0], acc[1], acc[2], acc[3]};
+    p[1] = float4{acc[4], acc[5], acc[6], acc[7]};
   }
 }
 
@@ -68,15 +86,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
 
 hipError_t launch_combine(const void* y_rows, bool rows_bf16, const int32_t* pair_row, const float* weights,
                           const void* y_shared, void* y, bool y_bf16, int64_t T, int K, int H, hipStream_t s) {
-  const unsigned grid = (unsigned)T;
+  const int64_t threads = T * (H / 8);
+  const unsigned grid = (unsigned)((threads + 255) / 256);
   if (rows_bf16 && y_bf16)
-    combine_kernel<true, true><<<grid, 256, 0, s>>>(y_rows, pair_row, weights, y_shared, y, K, H);
+    combine_kernel<true, true><<<grid, 256, 0, s>>>(y_rows, pair_row, weights, y_shared, y, T, K, H);
   else if (rows_bf16)
-    combine_kernel<true, false><<<grid, 256, 0, s>>>(y_rows, pair_row, weights, y_shared, y, K, H);
+    combine_kernel<true, false><<<grid, 256, 0, s>>>(y_rows, pair_row, weights, y_shared, y, T, K, H);
   else if (y_bf16)
-    combine_kernel<false, true><<<grid, 256, 0, s>>>(y_rows, pair_row, weights, y_shared, y, K, H);
+    combine_kernel<false, true><<<grid, 256, 0, s>>>(y_rows, pair_row, weights, y_shared, y, T, K, H);
   else
-    combine_kernel<false, false><<<grid, 256, 0, s>>>(y_rows, pair_row, weights, y_shared, y, K, H);
+    combine_kernel<false, false><<<grid, 256, 0, s>>>(y_rows, pair_row, weights, y_shared, y, T, K, H);
   return hipGetLastError();
 }
 
