@@ -41,14 +41,14 @@ F32_PEAK = 157.3e12        # fp32 vector FLOP/s
 # prints, and the source files that make the kernel (its measured traffic is only reported while
 # their digest is unchanged).
 KERNEL_SYMBOLS = {
-    "gateup_stream": ("stream_kernel<true", ["gemm_stream.hip", "tile_core.h", "kernels.h"]),
-    "down_stream": ("stream_kernel<false", ["gemm_stream.hip", "tile_core.h", "kernels.h"]),
-    "gateup_tile": ("gateup_tile_kernel", ["gemm_tile.hip", "tile_core.h", "kernels.h"]),
-    "down_tile": ("down_tile_kernel", ["gemm_tile.hip", "tile_core.h", "kernels.h"]),
-    "router_logits": ("router_logits_kernel", ["route.hip", "tile_core.h", "kernels.h"]),
-    "combine": ("combine_kernel", ["combine.hip", "kernels.h"]),
-    "gateup_q4": ("q4_stream_kernel<true", ["gemm_q4.hip", "tile_core.h", "kernels.h"]),
-    "down_q4": ("q4_stream_kernel<false", ["gemm_q4.hip", "tile_core.h", "kernels.h"]),
+    "gateup_stream": ("::stream_kernel<true", ["gemm_stream.hip", "tile_core.h", "kernels.h"]),
+    "down_stream": ("::stream_kernel<false", ["gemm_stream.hip", "tile_core.h", "kernels.h"]),
+    "gateup_tile": ("::gateup_tile_kernel", ["gemm_tile.hip", "tile_core.h", "kernels.h"]),
+    "down_tile": ("::down_tile_kernel", ["gemm_tile.hip", "tile_core.h", "kernels.h"]),
+    "router_logits": ("::router_logits_kernel", ["route.hip", "tile_core.h", "kernels.h"]),
+    "combine": ("::combine_kernel", ["combine.hip", "kernels.h"]),
+    "gateup_q4": ("::q4_stream_kernel<true", ["gemm_q4.hip", "tile_core.h", "kernels.h"]),
+    "down_q4": ("::q4_stream_kernel<false", ["gemm_q4.hip", "tile_core.h", "kernels.h"]),
 }
 Q4_BYTES = 0.5 + 2 / 32    # bytes per 4-bit weight: the code plus its share of a binary16 scale per 32
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
