@@ -280,8 +280,10 @@ __global__ __launch_bounds__(256) void stream_kernel(StreamArgs p) {
 #endif
 }
 
-constexpr int kDepthGateUp = 4;  // 4 x 32 KiB of LDS: one work-group per CU
-constexpr int kDepthDown = 4;    // 4 x 32 KiB: one work-group per CU
+// 2 x 32 KiB of LDS: two work-groups per CU, so one's ring fills while the other's drains (4 stages
+// and one work-group per CU measured 1.5% slower on decode, 3.5% on the short down streams)
+constexpr int kDepthGateUp = 2;
+constexpr int kDepthDown = 2;
 
 }  // namespace
 
