@@ -112,7 +112,15 @@ struct Operands {
   uint32_t a_off[kALoads];
   const char* b[kNSub];        // first weight row of each 16-column sub-tile of this wave
   uint32_t b_off;              // row (lane % 16) and 16-byte quarter (lane / 16) of a 64-byte piece
+  int skew, nk;                // step kt loads K step (kt + skew) mod nk (uniform over the work-group)
 };
+
+// Byte offset along K of the step loaded as step kt (kt < nk).
+__device__ __forceinline__ uint32_t kbytes(const Operands& o, int kt) {
+  int ks = kt + o.skew;
+  if (ks >= o.nk) ks -= o.nk;
+  return (uint32_t)ks * kRowBytes;
+}
 
 // B fragments of one K step: [k-substep][column sub-tile].
 struct BFrag {
@@ -199,9 +207,9 @@ __device__ __forceinline__ void kstep(const Operands& o, int kt, int nk, const R
   else
     wait_vmcnt<0>();
   block_sync_lds();
-  if (!kTail || kt + kADist < nk) issue_a<NP>(o, (uint32_t)(kt + kADist) * kRowBytes, ring.st[(D + kADist) % kStages]);
+  if (!kTail || kt + kADist < nk) issue_a<NP>(o, kbytes(o, kt + kADist), ring.st[(D + kADist) % kStages]);
   compute_step<NP>(ring.st[D], b[D], acc);
-  if (!kTail || kt + kDepth < nk) load_b(b[D], o, (uint32_t)(kt + kDepth) * kRowBytes);
+  if (!kTail || kt + kDepth < nk) load_b(b[D], o, kbytes(o, kt + kDepth));
 }
 
 template <int NP>
@@ -214,8 +222,8 @@ __device__ __forceinline__ void kloop(const Operands& o, int nk, const Ring& rin
     // so the compiler's own wait for B(kt) at the loop head sees the full count of later loads
 #pragma unroll
     for (int s = 0; s < kDepth; ++s) {
-      load_b(b[s], o, (uint32_t)s * kRowBytes);
-      if (s < kADist) issue_a<NP>(o, (uint32_t)s * kRowBytes, ring.st[s]);
+      load_b(b[s], o, kbytes(o, s));
+      if (s < kADist) issue_a<NP>(o, kbytes(o, s), ring.st[s]);
     }
     // steady state: every refill of these four steps exists (kt + 7 < nk), no conditions
     for (; kt + 8 <= nk; kt += 4) {
@@ -227,8 +235,8 @@ __device__ __forceinline__ void kloop(const Operands& o, int nk, const Ring& rin
   } else {
 #pragma unroll
     for (int s = 0; s < kDepth; ++s) {
-      if (s < nk) load_b(b[s], o, (uint32_t)s * kRowBytes);
-      if (s < kADist && s < nk) issue_a<NP>(o, (uint32_t)s * kRowBytes, ring.st[s]);
+      if (s < nk) load_b(b[s], o, kbytes(o, s));
+      if (s < kADist && s < nk) issue_a<NP>(o, kbytes(o, s), ring.st[s]);
     }
   }
   // the last 2 to 6 steps (K is a multiple of 128, so nk is even)
@@ -373,6 +381,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   o.b[0] = reinterpret_cast<const char*>(wg + (int64_t)c0 * H);  // gate rows of the wave's 16 columns
   o.b[1] = reinterpret_cast<const char*>(wu + (int64_t)c0 * H);  // their up rows
   o.b_off = (uint32_t)((lane & 15) * H * 2 + 16 * (lane >> 4));
+  o.nk = H / kBK;
+  o.skew = 0;  // 14,336-byte rows (K2) spread over the channels on their own
 
   uint16_t* h = static_cast<uint16_t*>(p.out);
   const int64_t rbeg = t.rbeg;
@@ -418,6 +428,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int s = 0; s < kNSub; ++s)  // idle waves re-read the first rows
     o.b[s] = reinterpret_cast<const char*>(wd + (int64_t)((cols_ok ? c0 : 0) + 16 * s) * I + k0);
   o.b_off = (uint32_t)((lane & 15) * I * 2 + 16 * (lane >> 4));
+  // W_down rows a multiple of 4 KiB apart put the same K step of all 256 rows on few HBM channels:
+  // the column slabs then start their K loops at different steps (and wrap around).  Only while the
+  // tile's h block is small (I <= 4096: at most 2 MiB): the slabs of a tile share it through L2 only
+  // while they walk K together (the dense layer's I = 18432 measured 7% slower with the skew).
+  o.nk = kc / kBK;
+  o.skew = (I * 2) % 4096 == 0 && I <= 4096 ? nt * 5 % o.nk : 0;
 
   const int64_t rbeg = t.rbeg, rend = t.rend;
   const int m_valid = (int)(rend - rbeg);
