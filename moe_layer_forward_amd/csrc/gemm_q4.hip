@@ -527,16 +527,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 __global__ __launch_bounds__(256) void f16_rows_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
                                                        int64_t n_groups) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_groups; i += stride) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(x + 8 * i);
-    _Float16 h[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint32_t bits = (v[t >> 1] >> (16 * (t & 1))) & 0xffffu;
-      h[pair_pos(t)] = (_Float16)__uint_as_float(bits << 16);  // bf16 -> f32 exact, then to f16 (RNE)
-    }
-    *reinterpret_cast<f16x8*>(y + 8 * i) = f16x8{h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]};
-  }
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_groups; i += stride)
+    f16_group_pairs(x + 8 * i, y + 8 * i);
 }
 
 }  // namespace

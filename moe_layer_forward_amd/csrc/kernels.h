@@ -24,6 +24,21 @@ __device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + ex
 // SwiGLU activation of one (gate, up) pair: SiLU(g) * u.
 __device__ __forceinline__ float swiglu_f32(float g, float u) { return g * sigmoid_f32(g) * u; }
 
+// One group of 8 bf16 values -> binary16 (exact widening, then round to nearest even), stored in the
+// order 0,4,1,5,2,6,3,7: the operand order of the 4-bit kernels (a code word decodes in that order).
+__device__ __forceinline__ void f16_group_pairs(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst) {
+  typedef uint32_t u32x4_ __attribute__((ext_vector_type(4)));
+  typedef _Float16 f16x8_ __attribute__((ext_vector_type(8)));
+  const u32x4_ v = *reinterpret_cast<const u32x4_*>(src);
+  _Float16 h[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t bits = (v[t >> 1] >> (16 * (t & 1))) & 0xffffu;
+    h[(t & 3) * 2 + (t >> 2)] = (_Float16)__uint_as_float(bits << 16);
+  }
+  *reinterpret_cast<f16x8_*>(dst) = f16x8_{h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]};
+}
+
 constexpr int kXcds = 8;  // MI355X: 8 XCDs, work-groups dealt round-robin by blockIdx
 
 // ----------------------------------------------------------------------------- launch descriptors
@@ -89,6 +104,13 @@ int64_t permute_scratch_ints(int64_t pairs, int E);
 hipError_t launch_permute(const int32_t* ids, int64_t T, int K, int E, int32_t* group_offsets,
                           int32_t* row_token, int32_t* pair_row, int32_t* scratch, bool shared_rows,
                           hipStream_t s);
+// Few pairs (permute_plan_fused): the permutation above and, when plan.n_groups > 0,
+// launch_plan(plan) in one launch, plus x16[T, H] = the binary16 token rows (f16_group_pairs order)
+// when x16 is given.
+bool permute_plan_fused(int64_t pairs, int E, int G);
+hipError_t launch_permute_plan(const int32_t* ids, int64_t T, int K, int E, int32_t* group_offsets,
+                               int32_t* row_token, int32_t* pair_row, bool shared_rows, const Groups& plan,
+                               const uint16_t* x, uint16_t* x16, int H, hipStream_t s);
 hipError_t launch_gather_rows(const void* x, const int32_t* row_token, void* x_perm, int64_t rows, int H,
                               int elem_bytes, hipStream_t s);
 

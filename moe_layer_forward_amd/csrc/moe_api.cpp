@@ -171,11 +171,12 @@ SwigluWs carve_swiglu(Carver& cv, const moe_config* c, int G, int64_t max_rows) 
   return w;
 }
 
-// Launch plan + both grouped GEMMs over prepared groups.
+// Launch the plan (unless the permutation launch already made it) + both grouped GEMMs.
 hipError_t run_swiglu(const moe_config* c, const moe::Groups& g, const moe::Weights& w, const void* x, void* h,
-                      float* part, const float* row_scale, void* y_rows, bool y_bf16, hipStream_t s) {
+                      float* part, const float* row_scale, void* y_rows, bool y_bf16, hipStream_t s,
+                      bool planned = false) {
   const int H = c->hidden_size, I = c->moe_intermediate_size;
-  hipError_t e = timed("plan", s, [&] { return moe::launch_plan(g, s); });
+  hipError_t e = planned ? hipSuccess : timed("plan", s, [&] { return moe::launch_plan(g, s); });
   if (e != hipSuccess) return e;
   if (c->dtype == MOE_F32) {
     e = timed("gateup_f32", s, [&] {
@@ -244,13 +245,16 @@ int run_after_routing(const moe_config* c, int64_t T, const void* x, const int32
   const int H = c->hidden_size, E = c->n_routed_experts, K = c->top_k;
   const bool shared = c->n_shared_experts == 1;
   const int64_t P = T * K;
-  hipError_t e = timed("permute", s, [&] {
-    return moe::launch_permute(ids, T, K, E, w.offsets, w.row_token, w.pair_row, w.perm_scratch, shared, s);
-  });
-  if (e != hipSuccess) return device_status(e, "permute");
   moe::Groups g = w.sw.g;
   g.group_offsets = w.offsets;
   g.row_index = w.row_token;
+  const bool fused = moe::permute_plan_fused(P, E, g.n_groups);
+  hipError_t e = timed(fused ? "permute_plan" : "permute", s, [&] {
+    return fused ? moe::launch_permute_plan(ids, T, K, E, w.offsets, w.row_token, w.pair_row, shared, g, nullptr,
+                                            nullptr, H, s)
+                 : moe::launch_permute(ids, T, K, E, w.offsets, w.row_token, w.pair_row, w.perm_scratch, shared, s);
+  });
+  if (e != hipSuccess) return device_status(e, "permute");
   moe::Weights wt;
   wt.gate = w_gate;
   wt.up = w_up;
@@ -262,7 +266,7 @@ int run_after_routing(const moe_config* c, int64_t T, const void* x, const int32
     wt.shared_group = E;
   }
   const bool rows_bf16 = c->dtype == MOE_BF16;
-  e = run_swiglu(c, g, wt, x, w.sw.h, w.sw.part, nullptr, w.y_rows, rows_bf16, s);
+  e = run_swiglu(c, g, wt, x, w.sw.h, w.sw.part, nullptr, w.y_rows, rows_bf16, s, fused);
   if (e != hipSuccess) return device_status(e, "grouped swiglu");
   const char* yr = static_cast<const char*>(w.y_rows);
   const void* ysh = shared ? yr + P * H * (int64_t)elem_bytes(c->dtype) : nullptr;
@@ -432,8 +436,11 @@ int moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_ids, int32
   int32_t* scratch = cv.take<int32_t>(moe::permute_scratch_ints(T * K, E));
   if ((st = check_ws(workspace, workspace_bytes, cv.used))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fused = moe::permute_plan_fused(T * K, E, 0);
   hipError_t e = timed("permute", s, [&] {
-    return moe::launch_permute(topk_ids, T, K, E, expert_offsets, row_token, pair_row, scratch, false, s);
+    return fused ? moe::launch_permute_plan(topk_ids, T, K, E, expert_offsets, row_token, pair_row, false,
+                                            moe::Groups{}, nullptr, nullptr, cfg->hidden_size, s)
+                 : moe::launch_permute(topk_ids, T, K, E, expert_offsets, row_token, pair_row, scratch, false, s);
   });
   if (e != hipSuccess) return device_status(e, "permute");
   if (x) {
@@ -586,20 +593,28 @@ int moe_forward_q4(const moe_config* cfg, int64_t T, const void* x, const void* 
                             cfg->routed_scaling_factor, ids, weights, s);
   });
   if (e != hipSuccess) return device_status(e, "top-k");
-  e = timed("permute", s, [&] {
-    return moe::launch_permute(ids, T, K, E, w.offsets, w.row_token, w.pair_row, w.perm_scratch, shared, s);
-  });
-  if (e != hipSuccess) return device_status(e, "permute");
-  e = timed("f16_rows", s, [&] {
-    return moe::launch_f16_rows(static_cast<const uint16_t*>(x), w.x16, T, H, s);
-  });
-  if (e != hipSuccess) return device_status(e, "f16 rows");
-
   // routed experts: groups 0..E-1 over rows [0, P); the shared expert (bf16) runs in the same
   // launches over rows [P, P + T) (row P + t is token t)
   moe::Groups gr = w.routed;
   gr.group_offsets = w.offsets;
   gr.row_index = w.row_token;
+  const bool fused = moe::permute_plan_fused(P, E, gr.n_groups);
+  if (fused) {
+    e = timed("permute_plan", s, [&] {
+      return moe::launch_permute_plan(ids, T, K, E, w.offsets, w.row_token, w.pair_row, shared, gr,
+                                      static_cast<const uint16_t*>(x), w.x16, H, s);
+    });
+    if (e != hipSuccess) return device_status(e, "permute");
+  } else {
+    e = timed("permute", s, [&] {
+      return moe::launch_permute(ids, T, K, E, w.offsets, w.row_token, w.pair_row, w.perm_scratch, shared, s);
+    });
+    if (e != hipSuccess) return device_status(e, "permute");
+    e = timed("f16_rows", s, [&] {
+      return moe::launch_f16_rows(static_cast<const uint16_t*>(x), w.x16, T, H, s);
+    });
+    if (e != hipSuccess) return device_status(e, "f16 rows");
+  }
   moe::QWeights qw{gate_codes, gate_scales, up_codes, up_scales, down_codes, down_scales};
   moe::SharedBf16 sh;
   sh.offsets = w.offsets + E;
@@ -613,7 +628,7 @@ int moe_forward_q4(const moe_config* cfg, int64_t T, const void* x, const void* 
   sh.h_rows = P + T;
   const moe::SharedBf16* shp = shared ? &sh : nullptr;
   uint16_t* y_rows = static_cast<uint16_t*>(w.y_rows);
-  e = timed("plan", s, [&] { return moe::launch_plan(gr, s); });
+  if (!fused) e = timed("plan", s, [&] { return moe::launch_plan(gr, s); });
   if (e == hipSuccess)
     e = timed("gateup_q4", s, [&] { return moe::launch_gateup_q4_stream(gr, qw, w.x16, T, w.h, shp, H, I, s); });
   if (e == hipSuccess)

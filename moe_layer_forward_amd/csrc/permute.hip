@@ -142,9 +142,9 @@ __device__ int32_t block_excl_scan(int32_t v, int32_t* sh, int32_t* total) {
 constexpr int kBuckets = 64;     // size classes for largest-first ordering (16-row passes, capped)
 constexpr int kPlanPerThread = 4;  // groups per thread -> at most 4096 groups
 
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ off, int G, int64_t max_rows,
-                                                    int tile_m, int max_tiles, int32_t* __restrict__ active,
-                                                    int32_t* __restrict__ counters, int32_t* __restrict__ tiles) {
+// The plan of G groups (one 1024-thread work-group): active groups largest first, and their tiles.
+__device__ void plan_block(const int32_t* __restrict__ off, int G, int64_t max_rows, int tile_m, int max_tiles,
+                           int32_t* __restrict__ active, int32_t* __restrict__ counters, int32_t* __restrict__ tiles) {
   __shared__ int32_t bucket_cnt[kBuckets];
   __shared__ int32_t bucket_cur[kBuckets];
   __shared__ int32_t scan_buf[1024];
@@ -223,6 +223,87 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   if (tid == 0) counters[1] = total < max_tiles ? total : max_tiles;
 }
 
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ off, int G, int64_t max_rows,
+                                                    int tile_m, int max_tiles, int32_t* __restrict__ active,
+                                                    int32_t* __restrict__ counters, int32_t* __restrict__ tiles) {
+  plan_block(off, G, max_rows, tile_m, max_tiles, active, counters, tiles);
+}
+
+// Few pairs (P <= kChunk): histogram, scan, stable scatter and (when plan.n_groups > 0) the plan in
+// one 1024-thread work-group (16 waves, each ranking P/16 consecutive pairs as scatter_kernel does,
+// so the rows come out in the same order); the other work-groups of the launch convert the token
+// rows to binary16 when x16 is given.
+constexpr int kSmallWaves = 16;
+constexpr int kSmallExperts = 512;
+
+__global__ __launch_bounds__(1024) void permute_plan_small_kernel(
+    const int32_t* __restrict__ ids, int64_t T, int K, int E, int nbits, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ pair_row, int shared_rows, Groups plan,
+    const uint16_t* __restrict__ x, uint16_t* __restrict__ x16, int64_t x_groups) {
+  if (blockIdx.x > 0) {
+    const int64_t stride = (int64_t)(gridDim.x - 1) * 1024;
+    for (int64_t i = (int64_t)(blockIdx.x - 1) * 1024 + threadIdx.x; i < x_groups; i += stride)
+      f16_group_pairs(x + 8 * i, x16 + 8 * i);
+    return;
+  }
+  __shared__ int32_t cur[kSmallWaves][kSmallExperts];
+  __shared__ int32_t scan_buf[1024];
+  const int64_t P = T * K;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
+  const int64_t per = (P + kSmallWaves - 1) / kSmallWaves;
+  const int64_t wbeg = wave * per;
+  const int64_t wend = wbeg + per < P ? wbeg + per : P;
+  for (int e = tid; e < kSmallWaves * kSmallExperts; e += 1024) (&cur[0][0])[e] = 0;
+  __syncthreads();
+  for (int64_t q = wbeg + lane; q < wend; q += 64) atomicAdd(&cur[wave][clamp_id(ids[q], E)], 1);
+  __syncthreads();
+  // segment offsets: expert e's total, exclusive scan over the experts (one per thread)
+  int32_t tot = 0;
+  if (tid < E)
+    for (int w = 0; w < kSmallWaves; ++w) tot += cur[w][tid];
+  int32_t all;
+  int32_t run = block_excl_scan(tot, scan_buf, &all);
+  if (tid < E) {
+    offsets[tid] = run;
+    for (int w = 0; w < kSmallWaves; ++w) {  // each wave's first row of expert e
+      const int32_t c = cur[w][tid];
+      cur[w][tid] = run;
+      run += c;
+    }
+  }
+  if (tid == 0) {
+    offsets[E] = (int32_t)P;
+    if (shared_rows) offsets[E + 1] = (int32_t)(P + T);
+  }
+  __syncthreads();
+  const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t p0 = wbeg; p0 < wend; p0 += 64) {
+    const int64_t q = p0 + lane;
+    const bool valid = q < wend;
+    const int e = valid ? clamp_id(ids[q], E) : 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t bal = __ballot((e >> b) & 1);
+      peers &= ((e >> b) & 1) ? bal : ~bal;
+    }
+    if (valid) {
+      const int rank = __popcll(peers & lower);
+      const int32_t row = cur[wave][e] + rank;
+      row_token[row] = (int32_t)(q / K);
+      pair_row[q] = row;
+      const int n = __popcll(peers);
+      if (rank == n - 1) cur[wave][e] = row + 1;
+    }
+  }
+  if (shared_rows)
+    for (int64_t t = tid; t < T; t += 1024) row_token[P + t] = (int32_t)t;
+  if (plan.n_groups == 0) return;  // permutation only
+  __threadfence_block();
+  __syncthreads();  // offsets written above are read back by the plan
+  plan_block(offsets, plan.n_groups, plan.max_rows, plan.tile_m, plan.max_tiles, plan.active, plan.counters,
+             plan.tiles);
+}
+
 __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ row_token,
                                                      uint4* __restrict__ x_perm, int64_t rows, int chunks_per_row) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -247,6 +328,25 @@ hipError_t launch_permute(const int32_t* ids, int64_t T, int K, int E, int32_t* 
   hist_kernel<<<nblk, 256, 0, s>>>(ids, P, E, scratch);
   scan_kernel<<<1, 1024, 0, s>>>(scratch, nblk, E, group_offsets, P, shared_rows ? T : 0);
   scatter_kernel<<<nblk, 256, 0, s>>>(ids, P, K, E, nbits, scratch, row_token, pair_row, T, shared_rows ? 1 : 0);
+  return hipGetLastError();
+}
+
+bool permute_plan_fused(int64_t pairs, int E, int G) {
+  return pairs <= kChunk && E <= kSmallExperts && G <= kPlanPerThread * 1024;
+}
+
+hipError_t launch_permute_plan(const int32_t* ids, int64_t T, int K, int E, int32_t* group_offsets,
+                               int32_t* row_token, int32_t* pair_row, bool shared_rows, const Groups& plan,
+                               const uint16_t* x, uint16_t* x16, int H, hipStream_t s) {
+  if (!permute_plan_fused(T * K, E, plan.n_groups)) return hipErrorInvalidValue;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const int64_t x_groups = x16 ? T * H / 8 : 0;
+  int64_t conv = (x_groups + 1023) / 1024;
+  if (conv > 256) conv = 256;
+  permute_plan_small_kernel<<<(unsigned)(1 + conv), 1024, 0, s>>>(ids, T, K, E, nbits, group_offsets, row_token,
+                                                                  pair_row, shared_rows ? 1 : 0, plan, x, x16,
+                                                                  x_groups);
   return hipGetLastError();
 }
 

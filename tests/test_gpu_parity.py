@@ -209,7 +209,9 @@ def test_route_call():
 def test_permute_call_integer_exact():
     torch = _torch()
     r = np.random.default_rng(3)
-    for T, K, E in [(1, 1, 1), (37, 3, 11), (5000, 8, 384), (700, 2, 7)]:
+    # up to 4096 pairs the permutation runs as one work-group (16 waves), above as chunked kernels
+    for T, K, E in [(1, 1, 1), (37, 3, 11), (5000, 8, 384), (700, 2, 7), (512, 8, 512), (513, 8, 384),
+                    (4096, 1, 3)]:
         ids = np.stack([r.choice(E, size=K, replace=False) for _ in range(T)]).astype(np.int32)
         cfg = moe.make_config(hidden_size=256, moe_intermediate_size=128, n_routed_experts=E, top_k=K)
         x = torch.randn((T, 256), dtype=torch.bfloat16, device="cuda")
