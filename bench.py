@@ -116,6 +116,51 @@ class HipEvents:
             self.hip.hipEventDestroy(self.ev[i])
 
 
+def measure_peaks():
+    """Measured peaks of this GPU (the published ones are HBM_PEAK and BF16_PEAK): a streaming read
+    of 4 GiB, a 2 GiB copy (read + write bytes) and a loop of independent bf16 MFMAs, each the best
+    of 5 timed launches on torch's current stream."""
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "moe_layer_forward_amd", "libmoe_peaks.so"))
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32
+    lib.peaks_read.argtypes = [vp, i64, vp, vp]
+    lib.peaks_copy.argtypes = [vp, vp, i64, vp]
+    lib.peaks_mfma.argtypes = [i32, i32, vp, vp]
+    stream = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(256, dtype=torch.float32, device="cuda")
+
+    def best(launch):
+        times = []
+        for r in range(6):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            rc = launch()
+            b.record()
+            if rc:
+                raise RuntimeError(f"peaks launch failed ({rc})")
+            torch.cuda.synchronize()
+            if r:
+                times.append(a.elapsed_time(b) * 1e-3)
+        return min(times)
+
+    rd = 4 << 30
+    buf = torch.empty(rd, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    t_read = best(lambda: lib.peaks_read(buf.data_ptr(), rd, sink.data_ptr(), stream))
+    half = rd // 2
+    t_copy = best(lambda: lib.peaks_copy(buf.data_ptr(), buf.data_ptr() + half, half, stream))
+    del buf
+    torch.cuda.empty_cache()
+    blocks, iters = 256 * 4, 2000
+    t_mfma = best(lambda: lib.peaks_mfma(blocks, iters, sink.data_ptr(), stream))
+    flops = blocks * 4 * 4 * iters * 32768
+    return {"hbm_read_GB_s": rd / t_read / 1e9, "hbm_copy_GB_s": 2 * half / t_copy / 1e9,
+            "mfma_bf16_TFLOP_s": flops / t_mfma / 1e12,
+            "how": "streaming read of 4 GiB; 2 GiB copy counted as read + write; 4 independent "
+                   "v_mfma_f32_32x32x16_bf16 chains per wave, 16 waves per CU; best of 5"}
+
+
 def kernel_work(name, w, n_touched):
     """Algorithmic (bytes, flops) of one launch of a grouped GEMM kernel: the weights of every group
     with rows read once, the token rows / h read once, the outputs written once."""
@@ -224,8 +269,27 @@ def run(w, weights, steps, warmup):
     for i in range(steps):
         for j, n in enumerate(names):
             kern[n] += ev.elapsed_ms(i * per + 2 * j, i * per + 2 * j + 1) / steps
+    # GPU time of each step: the first kernel's start to the last kernel's end
+    step_ms = sorted(ev.elapsed_ms(i * per, i * per + per - 1) for i in range(steps))
     ev.close()
     ms = (t1 - t0) * 1e3 / steps
+
+    flushed_ms = None
+    if w.routing == "preassigned":
+        # this workload's 0.35 GB of weights could stay in the 256 MB last-level cache between calls:
+        # time it again with 1 GiB written between the calls
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        times = []
+        for _ in range(steps):
+            flush.fill_(0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            step()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        flushed_ms = sorted(times)[len(times) // 2]
+        del flush
 
     # routing actually realised (counts touched experts for the byte accounting)
     if w.routing == "dense":
@@ -255,7 +319,12 @@ def run(w, weights, steps, warmup):
     s = ms * 1e-3
     layer = {"GB_s": lb / s / 1e9, "TFLOP_s": lf / s / 1e12, "hbm_frac": lb / s / HBM_PEAK,
              "mfma_frac": lf / s / peak_flops, "alg_bytes": lb, "alg_flops": lf, "touched_experts": n_touched,
-             "rows_per_expert_max": int(counts.max()), "experts_le2_rows": int((counts <= 2).sum())}
+             "rows_per_expert_max": int(counts.max()), "rows_per_expert_mean": float(counts.sum() / max(n_touched, 1)),
+             "experts_le2_rows": int((counts <= 2).sum()),
+             "step_gpu_ms": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0], "max": step_ms[-1]}}
+    if flushed_ms is not None:
+        layer["flushed_ms_median"] = flushed_ms
+        layer["flushed_mfma_frac"] = lf / (flushed_ms * 1e-3) / peak_flops
     return {"tokens_per_s": T / s, "ms_per_step": ms, "roofline": roof, "layer": layer,
             "kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()}}
 
@@ -371,6 +440,7 @@ def main():
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="first run one copy of known size (the traffic summary's counter calibration)")
     ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens in the oracle's CPU-baseline sample (0: skip)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip measuring this GPU's read/copy/MFMA peaks")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this implementation runs on one GPU; --gpus must be 1 (sharding across GPUs is "
@@ -425,6 +495,13 @@ def main():
                         "layer": r2["layer"], "kernels_us": r2["kernels_us"]}
     weights_cache.clear()
     torch.cuda.empty_cache()
+    if not args.no_peaks:
+        log("measuring this GPU's peaks ...")
+        pk = measure_peaks()
+        out["measured_peaks"] = pk
+        for layer in [out["layer"]] + [v["layer"] for v in out.values() if isinstance(v, dict) and "layer" in v]:
+            layer["hbm_frac_of_measured_read"] = layer["GB_s"] / pk["hbm_read_GB_s"]
+            layer["mfma_frac_of_measured"] = layer["TFLOP_s"] / pk["mfma_bf16_TFLOP_s"]
     if args.cpu_tokens > 0:
         log("timing the oracle on the host ...")
         out["cpu_baseline"] = cpu_baseline(main_w, min(args.cpu_tokens, main_w.T))

@@ -5,6 +5,7 @@
 compiles, next to their sources:
 
 * ``libmoe.so``           -- the MoE layer kernels behind the C ABI of ``include/moe.h``;
+* ``libmoe_peaks.so``     -- measured machine peaks (streaming read, copy, MFMA loop) for the benchmark;
 * ``synth/libsynth_dev.so``  -- device side of the seeded input generator;
 * ``synth/libsynth_host.so`` -- host side of the seeded input generator (gcc, OpenMP).
 """
@@ -69,9 +70,16 @@ def build_moe(verbose=False):
     return out
 
 
+def build_peaks(verbose=False):
+    out = os.path.join(PKG, "libmoe_peaks.so")
+    _run([HIPCC, *HIP_FLAGS, "-o", out, os.path.join(CSRC, "peaks.hip")], verbose)
+    return out
+
+
 def build_all(verbose=False):
     build_synth_host(verbose)
     build_synth_dev(verbose)
+    build_peaks(verbose)
     if all(os.path.exists(os.path.join(CSRC, s)) for s in MOE_SOURCES):
         build_moe(verbose)
     else:

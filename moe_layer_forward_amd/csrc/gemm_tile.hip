@@ -219,11 +219,14 @@ __device__ __forceinline__ void kloop(const Operands& o, int nk, const Ring& rin
   int kt = 0;
   if (nk >= 8) {
     // prologue in the steady-state order B(0), A(0), B(1), A(1), B(2), A(2), B(3); unconditional,
-    // so the compiler's own wait for B(kt) at the loop head sees the full count of later loads
+    // and fenced against reordering, so the compiler's own wait for B(kt) at the loop head sees the
+    // full count of later loads (a reordered prologue makes it drain every load once per 4 steps)
 #pragma unroll
     for (int s = 0; s < kDepth; ++s) {
       load_b(b[s], o, kbytes(o, s));
+      __builtin_amdgcn_sched_barrier(0);
       if (s < kADist) issue_a<NP>(o, kbytes(o, s), ring.st[s]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // steady state: every refill of these four steps exists (kt + 7 < nk), no conditions
     for (; kt + 8 <= nk; kt += 4) {

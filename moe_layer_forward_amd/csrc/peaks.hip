@@ -1,0 +1,105 @@
+// Measured machine peaks that the benchmark reports beside the published ones: a streaming HBM
+// read, a streaming copy, and a loop of independent bf16 MFMAs.  Measurement support only; the
+// layer does not use this library.
+//
+//   peaks_read : a work-group reads 32 KiB contiguous per round, 8 x 16 bytes in flight per thread
+//   peaks_copy : the same, storing each chunk to dst
+//   peaks_mfma : each wave runs `iters` rounds of 4 independent v_mfma_f32_32x32x16_bf16
+//                (32,768 FLOP each); 4 waves per work-group
+// Results are folded into a sink that is written only on an impossible value, so nothing is
+// optimised away.  Every entry point returns a hipError_t (0 = success).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// A work-group reads 8 x 256 consecutive chunks (32 KiB) per round, 8 loads in flight per thread.
+constexpr int kUnroll = 8;
+
+__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t n, uint32_t* sink) {
+  uint32_t acc = 0;
+  const int64_t round = (int64_t)gridDim.x * 256 * kUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * kUnroll + threadIdx.x; base < n; base += round) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int64_t i = base + (int64_t)j * 256;
+      v[j] = i < n ? __builtin_nontemporal_load(src + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) acc ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
+  }
+  if (acc == 0x9e3779b9u) sink[threadIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+__global__ __launch_bounds__(256) void mfma_kernel(int iters, float* sink) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = (__bf16)(float)((lane + j) & 7);
+    b[j] = (__bf16)(float)((lane * 3 + j) & 7);
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    acc[c] = f32x16{};
+    acc[c][0] = (float)(c + lane);
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += acc[c][e];
+  if (s == -1.2345f) sink[threadIdx.x] = s;
+}
+
+unsigned stream_grid(int64_t chunks, int per_thread) {
+  int64_t g = (chunks + 256 * per_thread - 1) / (256 * per_thread);
+  const int64_t cap = 256 * 8;  // 8 work-groups per CU, each looping
+  return (unsigned)(g < cap ? (g > 0 ? g : 1) : cap);
+}
+
+}  // namespace
+
+extern "C" {
+
+// Reads `bytes` (a multiple of 16) from src.  sink: 256 uint32 of device scratch.
+int peaks_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink || bytes <= 0 || bytes % 16) return (int)hipErrorInvalidValue;
+  const int64_t n = bytes / 16;
+  read_kernel<<<stream_grid(n, kUnroll), 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<const u32x4*>(src), n, sink);
+  return (int)hipGetLastError();
+}
+
+// Copies `bytes` (a multiple of 16) from src to dst (the two must not overlap).
+int peaks_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (!src || !dst || bytes <= 0 || bytes % 16) return (int)hipErrorInvalidValue;
+  const int64_t n = bytes / 16;
+  copy_kernel<<<stream_grid(n, 1), 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<const u32x4*>(src),
+                                                                            static_cast<u32x4*>(dst), n);
+  return (int)hipGetLastError();
+}
+
+// `blocks` work-groups of 4 waves, each wave 4 * iters MFMAs of 32,768 FLOP.  sink: 256 floats.
+int peaks_mfma(int32_t blocks, int32_t iters, float* sink, void* stream) {
+  if (!sink || blocks <= 0 || iters <= 0) return (int)hipErrorInvalidValue;
+  mfma_kernel<<<blocks, 256, 0, static_cast<hipStream_t>(stream)>>>(iters, sink);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"
