@@ -161,6 +161,33 @@ def measure_peaks():
                    "v_mfma_f32_32x32x16_bf16 chains per wave, 16 waves per CU; best of 5"}
 
 
+def vendor_gemm(E=385, M=192, H=7168, I=2048, reps=10):
+    """Context for the prefill GEMMs: the vendor library (torch.bmm, i.e. hipBLASLt) on the same
+    shapes as dense batched products -- every expert with exactly M rows, no row gather, no SwiGLU
+    epilogue, weights already laid out K x N.  Returns ms and TFLOP/s per product."""
+    import torch
+
+    out = {}
+    for name, K, N in (("gate_up", H, 2 * I), ("down", I, H)):
+        a = torch.randn(E, M, K, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(E, K, N, device="cuda", dtype=torch.bfloat16)  # contiguous right operand
+        for _ in range(3):
+            c = torch.bmm(a, b)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            c = torch.bmm(a, b)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / reps
+        out[name] = {"E": E, "M": M, "K": K, "N": N, "ms": ms, "TFLOP_s": 2.0 * E * M * K * N / ms / 1e9,
+                     "weight_GB_s": E * K * N * 2 / ms / 1e6}
+        del a, b, c
+        torch.cuda.empty_cache()
+    return out
+
+
 def kernel_work(name, w, n_touched):
     """Algorithmic (bytes, flops) of one launch of a grouped GEMM kernel: the weights of every group
     with rows read once, the token rows / h read once, the outputs written once."""
@@ -441,6 +468,8 @@ def main():
                     help="first run one copy of known size (the traffic summary's counter calibration)")
     ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens in the oracle's CPU-baseline sample (0: skip)")
     ap.add_argument("--no-peaks", action="store_true", help="skip measuring this GPU's read/copy/MFMA peaks")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only time torch.bmm (hipBLASLt) on the prefill GEMM shapes and print that (context)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this implementation runs on one GPU; --gpus must be 1 (sharding across GPUs is "
@@ -452,6 +481,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.vendor_gemm:
+        print(json.dumps({"vendor_gemm": vendor_gemm()}), flush=True)
+        return
     main_w = wl.WORKLOADS[args.workload]
     if args.pmc_calibrate:
         a = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda")
