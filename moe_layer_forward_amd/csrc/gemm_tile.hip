@@ -76,7 +76,7 @@ struct TileArgs {
   int out_bf16;
   const float* row_scale;
   int H, I, n_ntiles;
-  int n_ksplit;  // down: K ranges per output tile (partial sums go to part)
+  int n_ksplit;  // down: K ranges per output tile (partial sums go to part, then a reduction kernel)
   float* part;   // [n_ksplit, max_rows, H] fp32 when n_ksplit > 1
 };
 
@@ -516,17 +516,39 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(const float* __restr
   }
 }
 
+constexpr int kCUs = 256;  // MI355X compute units; one tile work-group per CU
+
+// K ranges per work item for a launch of `items` items over nk K steps: with fewer items than CUs,
+// the divisor s of nk (s <= 16, an even number of at least 4 steps per range, as the K loop's tail
+// expects) with the smallest ceil(items * s / CUs) / s, i.e. the fewest rounds of work per range,
+// each range's partial sums (part_frac of an item's weight bytes, written and read back once)
+// counted against it.
+int tile_ksplit(int64_t items, int nk, double part_frac) {
+  if (items <= 0 || items >= kCUs) return 1;
+  int best = 1;
+  double best_cost = 1.0;
+  for (int sp = 2; sp <= 16; ++sp) {
+    if (nk % sp || nk / sp < 4 || (nk / sp) % 2) continue;
+    const int64_t rounds = (items * sp + kCUs - 1) / kCUs;
+    const double cost = (double)rounds / sp * (1.0 + sp * part_frac);
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = sp;
+    }
+  }
+  return best;
+}
+
+int64_t rows_per_tile_est(int64_t max_rows) { return max_rows < kTileM ? max_rows : kTileM; }
+
 }  // namespace
 
 int down_tile_ksplit(int64_t max_rows, int G, int H, int I) {
-  // items of the unsplit launch if the rows formed full tiles; split K until about 512 work-groups
-  // (two per CU) are busy, keeping at least 8 K steps of 64 per range
-  const int64_t items = ((max_rows + kTileM - 1) / kTileM) * ((H + 255) / 256);
   (void)G;
-  int split = 1;
-  while (split < 16 && items * split * 2 <= 512 && I % (2 * split * kBK) == 0 && I / (2 * split) >= 8 * kBK)
-    split *= 2;
-  return split;
+  // items if the rows formed full tiles; an item's partial sums: rows x 256 columns fp32
+  const int64_t items = ((max_rows + kTileM - 1) / kTileM) * ((H + 255) / 256);
+  const double part_frac = (double)rows_per_tile_est(max_rows) * 256 * 4 * 2 / (256.0 * I * 2);
+  return tile_ksplit(items, I / kBK, part_frac);
 }
 
 hipError_t launch_gateup_tile_bf16(const Groups& g, const Weights& w, const uint16_t* x, uint16_t* h, int H, int I,
@@ -540,6 +562,7 @@ hipError_t launch_gateup_tile_bf16(const Groups& g, const Weights& w, const uint
 hipError_t launch_down_tile_bf16(const Groups& g, const Weights& w, const uint16_t* h, void* y_rows, bool y_bf16,
                                  const float* row_scale, float* part, int H, int I, hipStream_t s) {
   const int split = down_tile_ksplit(g.max_rows, g.n_groups, H, I);
+  if (split > 1 && !part) return hipErrorInvalidValue;
   TileArgs p{g.group_offsets, nullptr, g.tiles, g.counters, g.max_rows, w, h, y_rows, y_bf16 ? 1 : 0, row_scale,
              H, I, (H + 255) / 256, split, part};
   down_tile_kernel<<<grid_for(g.max_tiles, p.n_ntiles, split), kThreads, 0, s>>>(p);

@@ -174,6 +174,22 @@ def test_dense_ffn_every_token(T):
     assert err.max() <= Y_TOL["bf16"]
 
 
+def test_dense_ffn_split_k_every_token():
+    """Few rows and a wide layer: the down GEMM splits K (16 ranges of fp32 partial sums, reduced in
+    K-range order); every token against the oracle."""
+    _torch()
+    w = wl.custom("dense_split", T=16, H=2048, I=4096, E=1, K=1, routing="dense", n_shared=0)
+    # the workspace holds the K-range partial sums only when K is split: at least 2 ranges of
+    # 16 rows x H fp32 (256 KiB) beside h (128 KiB) and the plan
+    ws = moe.moe_workspace_size(moe.config_for(w), moe.MOE_OP_GROUPED_SWIGLU, w.T, 1)
+    assert ws >= 2 * w.T * w.H * 4 + w.T * w.I * 2
+    t = wl.device_inputs(w)
+    y = _dense(w, t)
+    err = rel_l2(to_np(y), oracle.swiglu_expert(wl.host_x(w), *wl.host_expert(w, 0)))
+    print(f"dense split-K T={w.T}: max rel L2 {err.max():.3g}", flush=True)
+    assert err.max() <= Y_TOL["bf16"]
+
+
 @pytest.mark.parametrize("name,tokens", [("dense_decode", [0, 31, 63]), ("dense_prefill", [0, 4097, 8191])])
 def test_dense_full_size(name, tokens):
     _torch()
