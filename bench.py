@@ -472,8 +472,8 @@ def main():
                     help="only time torch.bmm (hipBLASLt) on the prefill GEMM shapes and print that (context)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this implementation runs on one GPU; --gpus must be 1 (sharding across GPUs is "
-              "described in DESIGN.md but not built)", file=sys.stderr)
+        print("bench.py: this implementation runs on one GPU; --gpus must be 1 (the layer is not sharded "
+              "across GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import torch
