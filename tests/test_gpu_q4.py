@@ -3,7 +3,8 @@
 The oracle evaluates the layer in float64 on the dequantized weights (q * s of the host quantizer's
 codes and scales); the GPU multiplies in binary16 with fp32 accumulation, so the bf16 output bar
 (per-row relative L2 <= 2e-2) applies.  Cases: small sizes on every token (several 16-row passes
-per expert and a ragged tail; no shared expert; the shared expert on the tile kernels), and the
+per expert and a ragged tail; no shared expert; the shared expert over many row passes; more than
+4096 (token, expert) pairs, where the permutation runs as chunked kernels), and the
 full decode shape on sampled tokens.  The two quantizers (device for the GPU inputs, host for the
 oracle) are checked bit-exact against each other.
 """
@@ -55,8 +56,9 @@ def _check(w, t, tokens=None):
 @pytest.mark.parametrize("T,H,I,E,K,shared", [
     (70, 512, 256, 8, 2, 1),     # ~17.5 rows per expert: two passes, ragged
     (5, 768, 512, 40, 4, 0),     # one or two rows per expert, no shared expert
-    (200, 256, 512, 16, 2, 1),   # shared expert on the tile kernels (T > 128)
-], ids=["passes", "no_shared", "shared_tile"])
+    (200, 256, 512, 16, 2, 1),   # the shared expert's 200 rows in seven 32-row passes
+    (600, 256, 256, 32, 8, 1),   # 4800 pairs: the chunked permutation, separate binary16 rows and plan
+], ids=["passes", "no_shared", "shared_passes", "many_pairs"])
 def test_q4_small_every_token(T, H, I, E, K, shared):
     _torch()
     w = wl.custom(f"q4_{T}", T, H, I, E, K, x_seed=31, w_seed=32, n_shared=shared, quant="int4")
