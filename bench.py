@@ -227,7 +227,7 @@ def layer_work(w, n_touched):
     return bytes_, flops
 
 
-def run(w, weights, steps, warmup):
+def run(w, weights, steps, warmup, graph=True):
     import numpy as np
     import torch
 
@@ -301,6 +301,31 @@ def run(w, weights, steps, warmup):
     ev.close()
     ms = (t1 - t0) * 1e3 / steps
 
+    # the same step captured once as a HIP graph and replayed (a serving loop's launch mode): the
+    # library launches only kernels on the caller's stream, so the call is capturable as it is
+    graph_ms = None
+    if graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        graph_ms = a.elapsed_time(b) / steps
+        del g
+
     flushed_ms = None
     if w.routing == "preassigned":
         # this workload's 0.35 GB of weights could stay in the 256 MB last-level cache between calls:
@@ -349,6 +374,9 @@ def run(w, weights, steps, warmup):
              "rows_per_expert_max": int(counts.max()), "rows_per_expert_mean": float(counts.sum() / max(n_touched, 1)),
              "experts_le2_rows": int((counts <= 2).sum()),
              "step_gpu_ms": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0], "max": step_ms[-1]}}
+    if graph_ms is not None:
+        layer["graph_ms_per_step"] = graph_ms
+        layer["graph_tokens_per_s"] = T / (graph_ms * 1e-3)
     if flushed_ms is not None:
         layer["flushed_ms_median"] = flushed_ms
         layer["flushed_mfma_frac"] = lf / (flushed_ms * 1e-3) / peak_flops
@@ -468,6 +496,7 @@ def main():
                     help="first run one copy of known size (the traffic summary's counter calibration)")
     ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens in the oracle's CPU-baseline sample (0: skip)")
     ap.add_argument("--no-peaks", action="store_true", help="skip measuring this GPU's read/copy/MFMA peaks")
+    ap.add_argument("--no-graph", action="store_true", help="skip timing the step as a replayed HIP graph")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="only time torch.bmm (hipBLASLt) on the prefill GEMM shapes and print that (context)")
     args = ap.parse_args()
@@ -506,7 +535,7 @@ def main():
         return weights_cache[key]
 
     log(f"running {main_w.name} ...")
-    res = run(main_w, weights_for(main_w), args.steps, args.warmup)
+    res = run(main_w, weights_for(main_w), args.steps, args.warmup, graph=not args.no_graph)
     out = {
         "metric": METRIC, "value": res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
@@ -519,7 +548,7 @@ def main():
     for name in [n for n in args.also.split(",") if n and n not in ("none", args.workload)]:
         w2 = wl.WORKLOADS[name]
         log(f"running {w2.name} ...")
-        r2 = run(w2, weights_for(w2), args.steps, args.warmup)
+        r2 = run(w2, weights_for(w2), args.steps, args.warmup, graph=not args.no_graph)
         out[w2.name] = {"value": r2["tokens_per_s"], "unit": "tokens/s", "ms_per_step": r2["ms_per_step"],
                         "config": {"workload": w2.name, "T": w2.T},
                         "dtype": "f16 x int4 (routed), bf16 (shared)" if w2.quant == "int4" else w2.dtype,

@@ -212,15 +212,22 @@ def moe_combine(cfg, y_rows, pair_row, topk_weights, y_shared=None, out=None):
 
 
 def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, ws_gate=None, ws_up=None, ws_down=None, score_bias=None,
-                logit_offset=None, return_routing=False, workspace=None, out=None):
-    """The whole layer: returns y [T, H] (and (topk_ids, topk_weights) when return_routing)."""
+                logit_offset=None, return_routing=False, workspace=None, out=None, routing_out=None):
+    """The whole layer: returns y [T, H] (and (topk_ids, topk_weights) when return_routing).
+    routing_out: caller-owned (topk_ids int32 [T, K], topk_weights fp32 [T, K]) to write the routing
+    into (with out and workspace, a call that allocates nothing, e.g. inside a graph capture)."""
     import torch
 
     T = x.shape[0]
     dev, stream = _dev(x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, score_bias, logit_offset)
     y = out if out is not None else torch.empty((T, cfg.hidden_size), dtype=_elem(cfg), device=dev)
     ids = wts = None
-    if return_routing:
+    if routing_out is not None:
+        ids, wts = routing_out
+        if (ids.dtype != torch.int32 or wts.dtype != torch.float32 or tuple(ids.shape) != (T, cfg.top_k)
+                or tuple(wts.shape) != (T, cfg.top_k) or not ids.is_contiguous() or not wts.is_contiguous()):
+            raise ValueError("routing_out must be contiguous (int32 [T, K], float32 [T, K]) tensors")
+    elif return_routing:
         ids = torch.empty((T, cfg.top_k), dtype=torch.int32, device=dev)
         wts = torch.empty((T, cfg.top_k), dtype=torch.float32, device=dev)
     ws = workspace if workspace is not None else alloc_workspace(cfg, MOE_OP_FORWARD, T, 0, dev)
@@ -228,7 +235,7 @@ def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, ws_gate=None, ws_up=None
                                       _ptr(logit_offset), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(ws_gate),
                                       _ptr(ws_up), _ptr(ws_down), _ptr(y), _ptr(ids), _ptr(wts), _ptr(ws),
                                       ws.numel(), stream))
-    return (y, ids, wts) if return_routing else y
+    return (y, ids, wts) if (return_routing or routing_out is not None) else y
 
 
 def moe_forward_routed(cfg, x, topk_ids, topk_weights, w_gate, w_up, w_down, ws_gate=None, ws_up=None, ws_down=None,
