@@ -150,44 +150,63 @@ struct Q4Stream {
   uint32_t c_off[2];        // lane offsets of the two direct loads of a set (row, swizzled chunk)
   uint32_t s_off;           // lane offset of the scale load (row lane/4, piece lane%4 of a block)
   uint32_t a_off;           // lane offset of this wave's token-row load (row, swizzled piece)
+  uint32_t blk_cb, blk_sb;  // bytes between consecutive column blocks of the codes / the scales
   int wave_off, sc_wave_off, a_dst;  // this wave's codes, scale buffer, and token-row half
 
-  // The codes of step st into ring stage d; past the last step (nsteps) they read nothing and fill
-  // zeros.
-  __device__ __forceinline__ void issue_codes(char* const (&ring)[kD], int d, int st, int nsteps) const {
-    // st opaque to the optimiser: otherwise it precomputes addresses per (step, load) of the
-    // prologue, keeps them live across the whole pass and spills them
-    asm volatile("" : "+s"(st));
-    const uint32_t cn = __builtin_amdgcn_readfirstlane(st < nsteps ? c_bytes : 0u);
+  // Position (b, k) + off steps, where a column block has ksteps steps: one carry is enough to
+  // tell live steps (b < the chain length) from the padded ones past the end.
+  __device__ __forceinline__ static void adv(int b, int k, int off, int ksteps, int& b2, int& k2) {
+    k2 = k + off;
+    b2 = b;
+    if (k2 >= ksteps) {
+      k2 -= ksteps;
+      ++b2;
+    }
+  }
+
+  // The codes of step k of column block b into ring stage d; past the last block (nblk) they read
+  // nothing and fill zeros.
+  __device__ __forceinline__ void issue_codes(char* const (&ring)[kD], int d, int b, int k, int nblk) const {
+    // b, k through readfirstlane: scalar, and opaque to the optimiser, which would otherwise
+    // precompute addresses per (step, load) of the prologue, keep them live across the whole pass
+    // and spill them
+    b = __builtin_amdgcn_readfirstlane(b);
+    k = __builtin_amdgcn_readfirstlane(k);
+    const uint32_t cn = __builtin_amdgcn_readfirstlane(b < nblk ? c_bytes : 0u);
+    const uint32_t base = (uint32_t)b * blk_cb + (uint32_t)k * kCodeRowB;
     char* dst = ring[d] + wave_off;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const Rsrc rc = make_rsrc(cb[r], cn);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (LdsPtr)(dst + r * kSetCodeB + i * 1024), 16,
-                                                 c_off[i] + (uint32_t)st * kCodeRowB, 0, 0, 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (LdsPtr)(dst + r * kSetCodeB + i * 1024), 16, c_off[i] + base,
+                                                 0, 0, 2);
     }
   }
 
-  // Half of the pass's token rows of step st (2 rows, 1 KiB) into ring stage d.  Waves w and w + 2
-  // load the same half: identical bytes to the same place, and every wave issues the same loads.
-  __device__ __forceinline__ void issue_rows(char* const (&ring)[kD], int d, int st, int nsteps) const {
-    asm volatile("" : "+s"(st));
-    const uint32_t an = __builtin_amdgcn_readfirstlane(st < nsteps ? a_bytes : 0u);
+  // Half of the pass's token rows of step k (2 rows, 1 KiB) into ring stage d (the same rows for
+  // every column block).  Waves w and w + 2 load the same half: identical bytes to the same place,
+  // and every wave issues the same loads.
+  __device__ __forceinline__ void issue_rows(char* const (&ring)[kD], int d, int b, int k, int nblk) const {
+    b = __builtin_amdgcn_readfirstlane(b);
+    k = __builtin_amdgcn_readfirstlane(k);
+    const uint32_t an = __builtin_amdgcn_readfirstlane(b < nblk ? a_bytes : 0u);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(abase, an), (LdsPtr)(ring[d] + kCodesB + a_dst), 16,
-                                             a_off + (uint32_t)st * kARowB, 0, 0, 0);
+                                             a_off + (uint32_t)k * kARowB, 0, 0, 0);
   }
 
-  // The scales of steps st .. st + kD - 1 (st a multiple of kD) into registers: lane l holds the
-  // 16 bytes of step st + l%4 of row l/4 (each scale line in two requests, not eight).  Past the
-  // last step they read nothing.
-  __device__ __forceinline__ void issue_scales(int st, int nsteps, u32x4 (&sr)[2]) const {
-    asm volatile("" : "+s"(st));
-    const uint32_t sn = __builtin_amdgcn_readfirstlane(st < nsteps ? s_bytes : 0u);
+  // The scales of steps k .. k + kD - 1 of column block b (k a multiple of kD) into registers: lane l
+  // holds the 16 bytes of step k + l%4 of row l/4 (each scale line in two requests, not eight).  Past
+  // the last block they read nothing.
+  __device__ __forceinline__ void issue_scales(int b, int k, int nblk, u32x4 (&sr)[2]) const {
+    b = __builtin_amdgcn_readfirstlane(b);
+    k = __builtin_amdgcn_readfirstlane(k);
+    const uint32_t sn = __builtin_amdgcn_readfirstlane(b < nblk ? s_bytes : 0u);
+    const uint32_t base = (uint32_t)b * blk_sb + (uint32_t)k * 16;
 #pragma unroll
     for (int r = 0; r < 2; ++r)
-      sr[r] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(sb[r], sn), s_off + (uint32_t)st * 16, 0, 0);
+      sr[r] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(sb[r], sn), s_off + base, 0, 0);
   }
 
   // ... and from registers into the wave's scale buffer: [set][row][kD steps x 8 scales].  (Plain
@@ -254,43 +273,66 @@ struct Q4Stream {
       for (int e = 0; e < 4; ++e) acc[r][e] = __builtin_fmaf(pend_s[r], pend[r][e], acc[r][e]);
   }
 
-  // The K loop of one pass.  The token rows of a step are shared by the work-group's waves, so
-  // every step starts with a barrier: after it, every wave's rows of this step have arrived and
-  // every wave is done with the previous step's stage, whose rows are then refilled with those of
-  // step g + kD - 1 (the stage's codes were refilled with that step's at the end of the previous
-  // step).  Loads past the end read nothing, so the waits are fixed; steps
-  // past the end skip the multiply.  Loads in issue order: ... rows(g), codes(g+1), rows(g+1),
-  // codes(g+2), ..., with a block's scales just before the codes of its first step.
-  __device__ __forceinline__ void run(char* const (&ring)[kD], char* sc, int nsteps, f32x4 (&acc)[2]) const {
+  // The K loop of one pass over CHAIN consecutive column blocks of ksteps steps each (one pipeline:
+  // the loads of block b + 1's first steps are issued during block b's last steps; CHAIN > 1 needs
+  // ksteps % kD == 0).  The token rows of a step are shared by the work-group's waves, so every
+  // step starts with a barrier: after it, every wave's rows of this step have arrived and every
+  // wave is done with the previous step's stage, whose rows are then refilled with those of the
+  // step kD - 1 later (the stage's codes were refilled at the end of the previous step).  Loads past
+  // the end read nothing, so the waits are fixed; steps past a block's end (CHAIN == 1 only) skip
+  // the multiply.  Loads in issue order: ... rows(v), codes(v+1), rows(v+1), codes(v+2), ..., with
+  // a scale block's scales just before the codes of its first step.
+  template <int CHAIN>
+  __device__ __forceinline__ void run(char* const (&ring)[kD], char* sc, int ksteps, f32x4 (&acc)[CHAIN][2]) const {
     u32x4 sr[2];
     __builtin_amdgcn_s_barrier();  // the previous pass is done with the shared rows
-    issue_scales(0, nsteps, sr);
+    // the prologue in issue order, fenced against reordering (the waits below count on it)
+    issue_scales(0, 0, CHAIN, sr);
+    __builtin_amdgcn_sched_barrier(0);
     static_for<kD>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      issue_codes(ring, i, i, nsteps);
-      if constexpr (i + 1 < kD) issue_rows(ring, i, i, nsteps);
+      int b2, k2;
+      adv(0, 0, i, ksteps, b2, k2);
+      issue_codes(ring, i, b2, k2, CHAIN);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (i + 1 < kD) issue_rows(ring, i, b2, k2, CHAIN);
+      __builtin_amdgcn_sched_barrier(0);
     });
-    for (int g = 0; g < nsteps; g += kD) {
-      static_for<kD>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        // after rows(g + i): codes and rows of the next kD - 2 steps, the codes of the one after,
-        // and a block's scales among them unless this step starts a block
-        wait_vmcnt<(kD - 1) * 4 + (kD - 2) * 1 + (i == 0 ? 0 : kScaleLoads)>();
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        issue_rows(ring, (i + kD - 1) % kD, g + i + kD - 1, nsteps);
-        if constexpr (i == 0) store_scales(sc, sr);  // this block's scales, loaded a block ago
-        if (g + i < nsteps) compute(ring, i, sc, acc);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this stage's LDS reads are done
-        if constexpr (i == 0) issue_scales(g + kD, nsteps, sr);
-        issue_codes(ring, i, g + i + kD, nsteps);
-      });
-    }
+    static_for<CHAIN>([&](auto bc) {
+      constexpr int b = decltype(bc)::value;
+      for (int g = 0; g < ksteps; g += kD) {
+        static_for<kD>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          const int k = g + i;
+          // after rows(v): codes and rows of the next kD - 2 steps, the codes of the one after,
+          // and a scale block's scales among them unless this step starts one
+          wait_vmcnt<(kD - 1) * 4 + (kD - 2) * 1 + (i == 0 ? 0 : kScaleLoads)>();
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+          int b2, k2;
+          adv(b, k, kD - 1, ksteps, b2, k2);
+          issue_rows(ring, (i + kD - 1) % kD, b2, k2, CHAIN);
+          if constexpr (i == 0) store_scales(sc, sr);  // this scale block, loaded a block ago
+          if (k < ksteps) compute(ring, i, sc, acc[b]);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this stage's LDS reads are done
+          if constexpr (i == 0) {
+            adv(b, g, kD, ksteps, b2, k2);
+            issue_scales(b2, k2, CHAIN, sr);
+          }
+          adv(b, k, kD, ksteps, b2, k2);
+          issue_codes(ring, i, b2, k2, CHAIN);
+        });
+      }
+    });
     wait_vmcnt<0>();  // the last loads past the end still write (zeros) into the ring
   }
 };
 
-template <bool SWIGLU>
+// Column blocks per work-group of the down launch (a pipeline over 2 x 128 W_down rows): W_down's
+// rows are short (I/256 steps), so one block alone would mostly fill and drain the ring.
+constexpr int kDownChain = 2;
+
+template <bool SWIGLU, int CHAIN>
 __device__ __forceinline__ void q4_pass(const Q4Args& p, char* const (&ring)[kD], char* sc, const Q4Stream& base,
                                         int n0, int64_t mb, int64_t r1) {
   const int H = p.H, I = p.I, K = SWIGLU ? H : I;
@@ -305,32 +347,36 @@ __device__ __forceinline__ void q4_pass(const Q4Args& p, char* const (&ring)[kD]
     s.a_off = (uint32_t)(src * K * 2 + (a_pos(rl, lane & 31) << 4));
   }
   s.a_dst = (wave & 1) * 2 * kARowB;
-  f32x4 acc[2];
-  acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  s.run(ring, sc, K / kStepK, acc);
+  f32x4 acc[CHAIN][2];
+#pragma unroll
+  for (int b = 0; b < CHAIN; ++b) acc[b][0] = acc[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  s.template run<CHAIN>(ring, sc, K / kStepK, acc);
 
-  // lane holds MFMA rows 4*(lane/16) + e, column n0 + lane%16 (+16 for set 1 of down); the pass's
-  // rows are MFMA rows 0 .. kPassRows-1
+  // lane holds MFMA rows 4*(lane/16) + e, column n0 + lane%16 (+16 for set 1 of down, +128 per
+  // further column block); the pass's rows are MFMA rows 0 .. kPassRows-1
   const int col = n0 + (lane & 15);
   const int64_t rend = mb + kPassRows < r1 ? mb + kPassRows : r1;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int64_t row = mb + 4 * (lane >> 4) + e;
     if ((lane >> 4) != 0 || row >= rend) continue;
-    if (SWIGLU) {
+    if constexpr (SWIGLU) {
       // h in f16, each group of 8 columns in the operand order of the down matmul
-      const _Float16 v = (_Float16)swiglu_f32(acc[0][e], acc[1][e]);
+      const _Float16 v = (_Float16)swiglu_f32(acc[0][0][e], acc[0][1][e]);
       static_cast<_Float16*>(p.out)[row * I + (col & ~7) + pair_pos(col & 7)] = v;
     } else {
       const float sc = p.row_scale ? p.row_scale[row] : 1.f;
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const float v = acc[r][e] * sc;
-        if (p.out_bf16)
-          static_cast<uint16_t*>(p.out)[row * H + col + 16 * r] = f32_to_bf16(v);
-        else
-          static_cast<float*>(p.out)[row * H + col + 16 * r] = v;
-      }
+      for (int b = 0; b < CHAIN; ++b)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const float v = acc[b][r][e] * sc;
+          const int64_t at = row * H + col + 128 * b + 16 * r;
+          if (p.out_bf16)
+            static_cast<uint16_t*>(p.out)[at] = f32_to_bf16(v);
+          else
+            static_cast<float*>(p.out)[at] = v;
+        }
     }
   }
 }
@@ -465,7 +511,7 @@ __device__ __forceinline__ void shared_part(const Q4Args& p, char* const (&ring)
   }
 }
 
-template <bool SWIGLU>
+template <bool SWIGLU, int CHAIN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void q4_stream_kernel(Q4Args p) {
   // one array per stage: the compiler then tells the stages' direct loads and LDS reads apart
   __shared__ __align__(16) char s0[kStageB], s1[kStageB], s2[kStageB], s3[kStageB];
@@ -479,6 +525,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #endif
     return;
   }
+  static_assert(SWIGLU ? CHAIN == 1 : CHAIN >= 1, "column-block chains are for the down launch");
   const int bid = (int)blockIdx.x - p.sh_blocks;
   const int slot = bid / p.n_wg, nb = bid % p.n_wg;
   if (slot >= p.counters[0]) return;
@@ -489,7 +536,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int H = p.H, I = p.I, K = SWIGLU ? H : I, N = SWIGLU ? I : H;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = nb * (SWIGLU ? 64 : 128) + wave * (SWIGLU ? 16 : 32);  // first output column of this wave
+  // first output column of this wave (down: in the first of the work-group's CHAIN column blocks)
+  const int n0 = nb * CHAIN * (SWIGLU ? 64 : 128) + wave * (SWIGLU ? 16 : 32);
 
   // rows of the two 16-row sets: gate and up rows n0.. (gate/up), or W_down rows n0.. and n0+16..
   const int64_t row0[2] = {n0, SWIGLU ? n0 : n0 + 16};
@@ -504,8 +552,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   s.abase = p.a;
   s.a_bytes = p.a_bytes;
-  s.c_bytes = (uint32_t)(16 * (K / 2));
-  s.s_bytes = (uint32_t)(16 * (K / 16));
+  // column block b of this wave's rows starts 128 rows (down) further on; the descriptors span all
+  s.blk_cb = (uint32_t)(128 * (K / 2));
+  s.blk_sb = (uint32_t)(128 * (K / 16));
+  s.c_bytes = (uint32_t)((CHAIN - 1) * s.blk_cb + 16 * (K / 2));
+  s.s_bytes = (uint32_t)((CHAIN - 1) * s.blk_sb + 16 * (K / 16));
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = 8 * i + (lane >> 3);  // lane's row in the 16-row set; its slot = chunk position
@@ -515,7 +566,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   s.wave_off = wave * kWaveB;
   s.sc_wave_off = wave * kScaleWaveB;
 #if defined(__HIP_DEVICE_COMPILE__)
-  for (int64_t mb = r0; mb < r1; mb += kPassRows) q4_pass<SWIGLU>(p, ring, sc, s, n0, mb, r1);
+  for (int64_t mb = r0; mb < r1; mb += kPassRows) q4_pass<SWIGLU, CHAIN>(p, ring, sc, s, n0, mb, r1);
 #else
   (void)s;
   (void)n0;
@@ -566,16 +617,22 @@ hipError_t launch_gateup_q4_stream(const Groups& g, const QWeights& w, const uin
   Q4Args p{g.group_offsets, g.row_index, g.active, g.counters, g.max_rows, w.gate_codes, w.gate_scales,
            w.up_codes, w.up_scales, x16, operand_bytes(x_rows, H), h16, 0, nullptr, H, I, I / 64};
   set_shared(p, sh, true, H, I);
-  q4_stream_kernel<true><<<(unsigned)(p.sh_blocks + (int64_t)g.n_groups * p.n_wg), 256, 0, s>>>(p);
+  q4_stream_kernel<true, 1><<<(unsigned)(p.sh_blocks + (int64_t)g.n_groups * p.n_wg), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
 hipError_t launch_down_q4_stream(const Groups& g, const QWeights& w, const uint16_t* h16, uint16_t* y_rows,
                                  const SharedBf16* sh, int H, int I, hipStream_t s) {
+  // chained column blocks when they divide the columns and the K steps fill whole scale blocks
+  const bool chain = (H / 128) % kDownChain == 0 && (I / kStepK) % kD == 0;
   Q4Args p{g.group_offsets, nullptr, g.active, g.counters, g.max_rows, w.down_codes, w.down_scales, nullptr,
-           nullptr, h16, operand_bytes(g.max_rows, I), y_rows, 1, nullptr, H, I, H / 128};
+           nullptr, h16, operand_bytes(g.max_rows, I), y_rows, 1, nullptr, H, I, H / 128 / (chain ? kDownChain : 1)};
   set_shared(p, sh, false, H, I);
-  q4_stream_kernel<false><<<(unsigned)(p.sh_blocks + (int64_t)g.n_groups * p.n_wg), 256, 0, s>>>(p);
+  const unsigned grid = (unsigned)(p.sh_blocks + (int64_t)g.n_groups * p.n_wg);
+  if (chain)
+    q4_stream_kernel<false, kDownChain><<<grid, 256, 0, s>>>(p);
+  else
+    q4_stream_kernel<false, 1><<<grid, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
