@@ -4,7 +4,8 @@
 // (gate + up -> SiLU -> multiply -> down), batched over experts as the grouped GEMM that
 // "Kimi K2.5 架构 QA" Q8.3 names in place of the per-expert loop.
 //
-// Work item = (row tile of one group, column slab).  Row tiles come from the device-side plan
+// Work item = (row tile of one group, column slab; for down with few row tiles also a K range,
+// whose fp32 partial sums a second kernel adds in K order).  Row tiles come from the device-side plan
 // (largest groups first, kTileM = 256 rows each, so a K2 expert's ~170 prefill rows are one tile
 // and every weight byte is read from HBM once).  With ~170 rows per expert the layer moves ~170
 // FLOP per weight byte, below the MI355X ridge (~310), so these kernels are weight streams first
@@ -13,7 +14,7 @@
 //   * B (weights) never touches LDS.  Each wave owns 32 weight rows (output columns) and loads them
 //     straight into v_mfma_f32_16x16x32_bf16 B-operand registers: one load instruction covers 64
 //     contiguous bytes of each of 16 rows, and kDepth K steps of it are in flight per wave (a
-//     register ring), which is what keeps HBM busy.  8 waves, two per SIMD (up to 128 accumulators
+//     register ring).  8 waves, two per SIMD (up to 128 accumulators
 //     and the 64-register ring fit a wave's 256 registers), so one wave's MFMAs cover the other's
 //     waits.
 //   * A (token rows) is shared by the 8 waves and staged through a kStages-deep LDS ring with
