@@ -76,19 +76,23 @@ __global__ __launch_bounds__(512) void router_logits_kernel(const uint16_t* __re
     }
 }
 
+// One wave per logit: the lanes split the dot product, a fixed-order butterfly adds the partial sums.
 __global__ __launch_bounds__(256) void router_logits_f32_kernel(const float* __restrict__ x,
                                                                 const float* __restrict__ w,
                                                                 float* __restrict__ logits, int64_t T, int H,
                                                                 int E) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (i >= T * E) return;
   const int64_t t = i / E;
   const int e = (int)(i - t * E);
   const float* xr = x + t * H;
   const float* wr = w + (int64_t)e * H;
   float acc = 0.f;
-  for (int k = 0; k < H; ++k) acc = fmaf(xr[k], wr[k], acc);
-  logits[i] = acc;
+  for (int k = lane; k < H; k += 64) acc = fmaf(xr[k], wr[k], acc);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (lane == 0) logits[i] = acc;
 }
 
 __device__ __forceinline__ uint32_t order_bits(float v) {
@@ -216,8 +220,8 @@ hipError_t launch_router_logits_bf16(const uint16_t* x, const uint16_t* w_router
 
 hipError_t launch_router_logits_f32(const float* x, const float* w_router, float* logits, int64_t T, int H, int E,
                                     hipStream_t s) {
-  const int64_t n = T * E;
-  router_logits_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(x, w_router, logits, T, H, E);
+  const int64_t n = T * E;  // one wave per logit, 4 per work-group
+  router_logits_f32_kernel<<<(unsigned)((n + 3) / 4), 256, 0, s>>>(x, w_router, logits, T, H, E);
   return hipGetLastError();
 }
 
