@@ -58,6 +58,8 @@ def _host_lib():
             fn.restype = None
         lib.synth_quantize_q4.argtypes = [vp, i64, vp, vp]
         lib.synth_quantize_q4.restype = None
+        lib.synth_quantize_fp8.argtypes = [vp, i64, i64, i64, vp, vp]
+        lib.synth_quantize_fp8.restype = None
         _host = lib
     return _host
 
@@ -77,6 +79,9 @@ def _dev_lib():
         lib.synth_dev_quantize_q4.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_void_p]
         lib.synth_dev_quantize_q4.restype = ctypes.c_int
+        lib.synth_dev_quantize_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.synth_dev_quantize_fp8.restype = ctypes.c_int
         _dev = lib
     return _dev
 
@@ -185,4 +190,46 @@ def device_quantize_q4(w, codes, scales):
                                           torch.cuda.current_stream().cuda_stream)
     if rc:
         raise RuntimeError(f"synth_dev_quantize_q4 failed ({rc})")
+    return codes, scales
+
+
+# --------------------------------------------------------------------------- 8-bit weight storage
+# Input preparation of the same kind, identical on host and device: per 128 x 128 block of a matrix,
+# s = max|w| / 448 (fp32), c = OCP E4M3 code of w / s, rounded to nearest even and saturating at
+# +-448 (0 when s == 0); codes one byte per weight, scales fp32 [rows/128, cols/128].
+
+def host_quantize_fp8(w_bits: np.ndarray):
+    """bf16 bits [rows, cols] (multiples of 128) -> (codes uint8 [rows, cols], scales float32
+    [rows/128, cols/128])."""
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    rows, cols = w.shape
+    if rows % 128 or cols % 128:
+        raise ValueError("rows and cols must be multiples of 128")
+    codes = np.empty((rows, cols), dtype=np.uint8)
+    scales = np.empty((rows // 128, cols // 128), dtype=np.float32)
+    _host_lib().synth_quantize_fp8(w.ctypes.data, 1, rows, cols, codes.ctypes.data, scales.ctypes.data)
+    return codes, scales
+
+
+def device_quantize_fp8(w, codes, scales):
+    """bf16 tensor [..., rows, cols] -> fills uint8 codes of the same shape and float32 scales
+    [..., rows/128, cols/128] on the GPU."""
+    import torch
+
+    for t in (w, codes, scales):
+        if not t.is_contiguous():
+            raise ValueError("device_quantize_fp8: tensors must be contiguous")
+    if w.dtype != torch.bfloat16 or codes.dtype != torch.uint8 or scales.dtype != torch.float32:
+        raise ValueError("device_quantize_fp8: w bf16, codes uint8, scales float32")
+    if w.dim() < 2:
+        raise ValueError("device_quantize_fp8: w must be [..., rows, cols]")
+    rows, cols = w.shape[-2], w.shape[-1]
+    n_mats = w.numel() // (rows * cols) if rows * cols else 0
+    if (rows % 128 or cols % 128 or tuple(codes.shape) != tuple(w.shape)
+            or scales.numel() != n_mats * (rows // 128) * (cols // 128)):
+        raise ValueError("device_quantize_fp8: shapes do not match")
+    rc = _dev_lib().synth_dev_quantize_fp8(w.data_ptr(), n_mats, rows, cols, codes.data_ptr(), scales.data_ptr(),
+                                           torch.cuda.current_stream().cuda_stream)
+    if rc:
+        raise RuntimeError(f"synth_dev_quantize_fp8 failed ({rc})")
     return codes, scales

@@ -35,6 +35,14 @@
  *     q = clamp(rint(w / s), -8, 7)           (q = 0 when s == 0)
  *   codes: 8 per 32-bit word, input k of the row in bits 4*(k % 8) of word k / 8,
  *          as 4-bit two's complement; scales: f16 bits, one per group.
+ *
+ * 8-bit weight storage (synth_quantize_fp8), input preparation of the same kind: per 128 x 128
+ * block of a matrix,
+ *     s = max|w| / 448                        (one IEEE division; fp32 scale)
+ *     c = e4m3(w / s)                         (one IEEE division, then round to nearest even,
+ *                                              saturating at +-448; c = 0 when s == 0)
+ *   codes: one byte per weight in the matrix's layout, OCP E4M3 (sign, 4 exponent bits with
+ *   bias 7, 3 mantissa bits; largest 448); scales: fp32 [rows/128, cols/128].
  */
 #include <math.h>
 #include <stdint.h>
@@ -177,5 +185,54 @@ void synth_quantize_q4(const uint16_t *w, int64_t n_groups, uint32_t *codes, uin
       }
       codes[gi * 4 + wd] = word;
     }
+  }
+}
+
+/* OCP E4M3 code of an fp32 value: round to nearest even, saturating at +-448 (the format has no
+ * infinities; S.1111.111 is NaN and never produced).  Every step is exact except the rintf. */
+static uint8_t f32_to_e4m3_rne(float t) {
+  union { float f; uint32_t u; } b;
+  b.f = t;
+  const uint8_t sign = (uint8_t)((b.u >> 24) & 0x80u);
+  b.u &= 0x7fffffffu;
+  const float a = b.f;
+  if (!(a < 448.0f)) return sign | 0x7e;
+  if (a < 0.015625f) return sign | (uint8_t)rintf(a * 512.0f); /* quantum 2^-9; 8 -> 0x08 = 2^-6 */
+  int e = (int)(b.u >> 23) - 127;                                 /* 2^e <= a < 2^(e+1), -6 <= e <= 8 */
+  union { float f; uint32_t u; } p;
+  p.u = (uint32_t)(127 + 3 - e) << 23;                            /* 2^(3 - e) */
+  float q = rintf(a * p.f);                                       /* 8 .. 16 */
+  if (q == 16.0f) {
+    q = 8.0f;
+    ++e;
+  }
+  return sign | (uint8_t)(((e + 7) << 3) | ((int)q - 8));
+}
+
+/* w: n_mats matrices [rows, cols] of bf16 bits (rows, cols multiples of 128) ->
+ * codes [n_mats, rows, cols] bytes, scales [n_mats, rows/128, cols/128] fp32. */
+void synth_quantize_fp8(const uint16_t *w, int64_t n_mats, int64_t rows, int64_t cols, uint8_t *codes,
+                        float *scales) {
+  const int64_t br = rows / 128, bc = cols / 128, n_blocks = n_mats * br * bc;
+#pragma omp parallel for schedule(static)
+  for (int64_t bi = 0; bi < n_blocks; ++bi) {
+    const int64_t m = bi / (br * bc), r0 = (bi / bc) % br * 128, c0 = bi % bc * 128;
+    const int64_t base = m * rows * cols;
+    float amax = 0.f;
+    for (int64_t r = r0; r < r0 + 128; ++r)
+      for (int64_t c = c0; c < c0 + 128; ++c) {
+        union { uint32_t u; float f; } b;
+        b.u = (uint32_t)w[base + r * cols + c] << 16;
+        const float av = fabsf(b.f);
+        if (av > amax) amax = av;
+      }
+    const float s = amax / 448.0f;
+    scales[bi] = s;
+    for (int64_t r = r0; r < r0 + 128; ++r)
+      for (int64_t c = c0; c < c0 + 128; ++c) {
+        union { uint32_t u; float f; } b;
+        b.u = (uint32_t)w[base + r * cols + c] << 16;
+        codes[base + r * cols + c] = s > 0.f ? f32_to_e4m3_rne(b.f / s) : 0;
+      }
   }
 }

@@ -49,6 +49,14 @@ signed 4-bit integer, s one scale per group of 32 consecutive inputs of an outpu
 where the page is silent: q is stored as 4-bit two's complement, 8 per 32-bit word, input k in bits
 4*(k % 8) of word k // 8; s is stored as IEEE binary16.  ``dequant_q4`` evaluates w exactly in
 float64; the layer is then the same function of the dequantized weights.
+
+FP8 routed experts (the Baidu developer article on K2-Instruct, developer.baidu.com article
+8800668, §3.2 item 1: FP8 quantization halves the weight memory; the page names neither the
+format nor the scaling).  Readings: the routed-expert weights are stored as OCP E4M3 codes (sign,
+4 exponent bits with bias 7, 3 mantissa bits, exponent 0 subnormal, no infinities, S.1111.111 NaN)
+with one fp32 scale per 128 x 128 block of each matrix, w = e4m3(c) * s[n // 128, k // 128]; only
+the storage is quantized, as for the 4-bit weights ([QA] Q7.1).  ``dequant_fp8`` evaluates w
+exactly in float64; the layer is then the same function of the dequantized weights.
 """
 from __future__ import annotations
 
@@ -202,3 +210,28 @@ def dequant_q4(codes, scales):
     if sc.shape != (n, words * 8 // 32):
         raise ValueError("scales must be [N, K/32]")
     return q * np.repeat(sc, 32, axis=1)
+
+
+def e4m3_value(codes):
+    """OCP E4M3 codes (uint8) -> float64 values: bit 7 sign, bits 6..3 exponent e (bias 7), bits 2..0
+    mantissa m; e = 0 gives the subnormal 2^-6 * m/8, else 2^(e-7) * (1 + m/8); e = 15, m = 7 is NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    return np.where((e == 15) & (m == 7), np.nan, sign * mag)
+
+
+def dequant_fp8(codes, scales, block=128):
+    """FP8 block-scaled weight -> float64 (readings in the module header).
+
+    codes  uint8 [N, K]: OCP E4M3;  scales float32 [N/block, K/block]: one per block x block tile.
+    Returns w [N, K] = e4m3(code) * s[n // block, k // block].
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    n, k = codes.shape
+    sc = np.asarray(scales, dtype=np.float64)
+    if n % block or k % block or sc.shape != (n // block, k // block):
+        raise ValueError("scales must be [N/block, K/block]")
+    return e4m3_value(codes) * np.repeat(np.repeat(sc, block, axis=0), block, axis=1)

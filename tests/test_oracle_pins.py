@@ -388,3 +388,69 @@ def test_q4_quantizer_round_trip_bound():
     # a zero group stays zero
     zc, zs = synth.host_quantize_q4(np.zeros((1, 32), dtype=np.uint16))
     assert zs[0, 0] == 0 and zc.sum() == 0 and np.all(oracle.dequant_q4(zc, zs) == 0)
+
+
+# --------------------------------------------------------------------------- FP8 (E4M3) weights
+def test_fp8_e4m3_matches_library_decoding():
+    """Every one of the 256 codes decodes as PyTorch's float8_e4m3fn does (an independent
+    implementation of the OCP E4M3 format), NaN codes included."""
+    import torch
+
+    c = np.arange(256, dtype=np.uint8)
+    v = oracle.e4m3_value(c)
+    ref = torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(v), np.isnan(ref))
+    assert np.isnan(v[[0x7F, 0xFF]]).all()
+    np.testing.assert_array_equal(v[~np.isnan(v)], ref[~np.isnan(ref)])
+
+
+def test_fp8_e4m3_closed_forms():
+    """The format's landmarks and spacing: smallest subnormal 2^-9, largest subnormal 7 * 2^-9,
+    smallest normal 2^-6, one, largest 448; the positive codes increase strictly with a step of
+    2^(max(e, 1) - 10) in binade e; the sign bit negates."""
+    v = oracle.e4m3_value(np.arange(256, dtype=np.uint8))
+    assert v[0x00] == 0.0 and v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9
+    assert v[0x08] == 2.0 ** -6 and v[0x38] == 1.0 and v[0x7E] == 448.0
+    steps = np.diff(v[:0x7F])
+    e = (np.arange(1, 0x7F) >> 3)
+    np.testing.assert_array_equal(steps, 2.0 ** (np.maximum(e - ((np.arange(1, 0x7F) & 7) == 0), 1) - 10))
+    np.testing.assert_array_equal(v[0x80:0xFF], -v[0x00:0x7F])
+
+
+def test_fp8_dequant_block_scales_brute_force():
+    """dequant_fp8 against an element-by-element loop over a non-square grid of blocks with distinct
+    scales (a transposed or misplaced block index fails)."""
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 256, size=(256, 384), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C  # no NaN codes
+    scales = rng.uniform(0.5, 2.0, size=(2, 3)).astype(np.float32)
+    w = oracle.dequant_fp8(codes, scales)
+    table = oracle.e4m3_value(np.arange(256, dtype=np.uint8))
+    for i in range(0, 256, 7):
+        for j in range(0, 384, 5):
+            assert w[i, j] == table[codes[i, j]] * float(scales[i // 128, j // 128])
+
+
+def test_fp8_quantizer_round_trip_bound():
+    """Input preparation and the oracle's decoding agree: every weight is kept within half a step
+    of E4M3 at its magnitude (times the block scale), each block's largest magnitude maps to 448,
+    and an all-zero block stays zero."""
+    import torch
+    from moe_layer_forward_amd import synth
+
+    bits = synth.host_tensor(6, 3, 0, (256, 384), 0.02, "bf16")
+    w = synth.bf16_bits_to_f32(bits).astype(np.float64)
+    codes, scales = synth.host_quantize_fp8(bits)
+    deq = oracle.dequant_fp8(codes, scales)
+    s = np.repeat(np.repeat(scales.astype(np.float64), 128, axis=0), 128, axis=1)
+    t = np.abs(w) / s
+    e = np.floor(np.log2(np.maximum(t, 2.0 ** -6)))
+    half_step = 2.0 ** (e - 4)
+    assert np.all(np.abs(deq - w) <= half_step * s * (1 + 1e-6))
+    blocks = np.abs(codes.reshape(2, 128, 3, 128).transpose(0, 2, 1, 3).reshape(6, -1) & 0x7F)
+    assert np.all(blocks.max(axis=1) == 0x7E)
+    # the codes are the library's round-to-nearest-even of w / s (computed in fp32, as the quantizer does)
+    t32 = torch.from_numpy(synth.bf16_bits_to_f32(bits)) / torch.from_numpy(np.repeat(np.repeat(scales, 128, 0), 128, 1))
+    np.testing.assert_array_equal(t32.to(torch.float8_e4m3fn).view(torch.uint8).numpy(), codes)
+    zc, zs = synth.host_quantize_fp8(np.zeros((128, 128), dtype=np.uint16))
+    assert zs[0, 0] == 0 and zc.sum() == 0 and np.all(oracle.dequant_fp8(zc, zs) == 0)
