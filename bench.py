@@ -47,10 +47,14 @@ KERNEL_SYMBOLS = {
     "down_tile": ("::down_tile_kernel", ["gemm_tile.hip", "tile_core.h", "kernels.h"]),
     "router_logits": ("::router_logits_kernel", ["route.hip", "tile_core.h", "kernels.h"]),
     "combine": ("::combine_kernel", ["combine.hip", "kernels.h"]),
-    "gateup_q4": ("::q4_stream_kernel<true", ["gemm_q4.hip", "tile_core.h", "kernels.h"]),
-    "down_q4": ("::q4_stream_kernel<false", ["gemm_q4.hip", "tile_core.h", "kernels.h"]),
+    "gateup_q4": ("::q_stream_kernel<(moe::QFormat)0, true", ["gemm_quant.hip", "tile_core.h", "kernels.h"]),
+    "down_q4": ("::q_stream_kernel<(moe::QFormat)0, false", ["gemm_quant.hip", "tile_core.h", "kernels.h"]),
+    "gateup_fp8": ("::q_stream_kernel<(moe::QFormat)1, true", ["gemm_quant.hip", "tile_core.h", "kernels.h"]),
+    "down_fp8": ("::q_stream_kernel<(moe::QFormat)1, false", ["gemm_quant.hip", "tile_core.h", "kernels.h"]),
 }
 Q4_BYTES = 0.5 + 2 / 32    # bytes per 4-bit weight: the code plus its share of a binary16 scale per 32
+FP8_BYTES = 1 + 4 / 128 ** 2  # bytes per FP8 weight: the code plus its share of an fp32 scale per 128 x 128
+QUANT_BYTES = {"int4": Q4_BYTES, "fp8": FP8_BYTES}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 CALIB_BYTES = 1 << 30      # the calibration copy reads and writes this many bytes
 CALIB_SYMBOL = "neg_kernel"
@@ -192,18 +196,19 @@ def kernel_work(name, w, n_touched):
     """Algorithmic (bytes, flops) of one launch of a grouped GEMM kernel: the weights of every group
     with rows read once, the token rows / h read once, the outputs written once."""
     eb = 2 if w.dtype == "bf16" else 4
-    if name in ("gateup_q4", "down_q4"):
-        # routed experts with 4-bit weights (f16 token rows and h), plus the shared expert's bf16
+    if name in ("gateup_q4", "down_q4", "gateup_fp8", "down_fp8"):
+        # routed experts with quantized weights (f16 token rows and h), plus the shared expert's bf16
         # weights and rows in the same launch; y_rows bf16
+        qb = QUANT_BYTES[w.quant]
         rows = w.T * w.K + w.T * w.n_shared
-        if name == "gateup_q4":
-            wbytes = (n_touched * Q4_BYTES + w.n_shared * 2) * 2 * w.I * w.H
+        if name.startswith("gateup"):
+            wbytes = (n_touched * qb + w.n_shared * 2) * 2 * w.I * w.H
             return wbytes + w.T * w.H * 2 * (1 + w.n_shared) + rows * w.I * 2, rows * 2 * 2 * w.I * w.H
-        wbytes = (n_touched * Q4_BYTES + w.n_shared * 2) * w.H * w.I
+        wbytes = (n_touched * qb + w.n_shared * 2) * w.H * w.I
         return wbytes + rows * w.I * 2 + rows * w.H * 2, rows * 2 * w.H * w.I
     n_groups_active = n_touched + w.n_shared
     rows = w.T * w.K + w.T * w.n_shared
-    if w.quant == "int4":  # the bf16 kernels run the shared expert alone
+    if w.quant != "none":  # the bf16 kernels run the shared expert alone
         n_groups_active, rows = 1, w.T
     if name.startswith("gateup"):
         wbytes = n_groups_active * 2 * w.I * w.H * eb
@@ -218,7 +223,7 @@ def layer_work(w, n_touched):
     """Algorithmic bytes and flops of the whole layer: every touched expert's and the shared expert's
     weights once, the router weight, x read and y written once."""
     eb = 2 if w.dtype == "bf16" else 4
-    routed_eb = Q4_BYTES if w.quant == "int4" else eb
+    routed_eb = QUANT_BYTES.get(w.quant, eb)
     bytes_ = (n_touched * routed_eb + w.n_shared * eb) * 3 * w.H * w.I + 2 * w.T * w.H * eb
     flops = (w.T * w.K + w.T * w.n_shared) * 2 * 3 * w.H * w.I
     if w.routing not in ("preassigned", "dense"):
@@ -253,14 +258,15 @@ def run(w, weights, steps, warmup, graph=True):
         def step():
             moe.moe_forward_routed(cfg, acts["x"], acts["topk_ids"], acts["topk_weights"], wg, wu, wd,
                                    weights["ws_gate"], weights["ws_up"], weights["ws_down"], workspace=ws, out=y)
-    elif w.quant == "int4":
-        ws = moe.alloc_workspace(cfg, moe.MOE_OP_FORWARD_Q4, T)
-        q4 = {k: weights[k] for k in ("gate_codes", "gate_scales", "up_codes", "up_scales", "down_codes",
-                                      "down_scales")}
+    elif w.quant in ("int4", "fp8"):
+        q4 = w.quant == "int4"
+        ws = moe.alloc_workspace(cfg, moe.MOE_OP_FORWARD_Q4 if q4 else moe.MOE_OP_FORWARD_FP8, T)
+        qw = {k: weights[k] for k in moe.QUANT_KEYS}
+        fwd = moe.moe_forward_q4 if q4 else moe.moe_forward_fp8
 
         def step():
-            moe.moe_forward_q4(cfg, acts["x"], weights["w_router"], q4, weights["ws_gate"], weights["ws_up"],
-                               weights["ws_down"], logit_offset=acts.get("logit_offset"), workspace=ws, out=y)
+            fwd(cfg, acts["x"], weights["w_router"], qw, weights["ws_gate"], weights["ws_up"], weights["ws_down"],
+                logit_offset=acts.get("logit_offset"), workspace=ws, out=y)
     else:
         ws = moe.alloc_workspace(cfg, moe.MOE_OP_FORWARD, T)
 
@@ -490,7 +496,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=list(wl.WORKLOADS))
-    ap.add_argument("--also", default="prefill,skew,ep_share,tiny,dense_decode,dense_prefill,decode_int4",
+    ap.add_argument("--also", default="prefill,skew,ep_share,tiny,dense_decode,dense_prefill,decode_int4,decode_fp8",
                     help="comma-separated workloads measured in the same run and reported beside it ('none')")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="first run one copy of known size (the traffic summary's counter calibration)")
@@ -551,7 +557,8 @@ def main():
         r2 = run(w2, weights_for(w2), args.steps, args.warmup, graph=not args.no_graph)
         out[w2.name] = {"value": r2["tokens_per_s"], "unit": "tokens/s", "ms_per_step": r2["ms_per_step"],
                         "config": {"workload": w2.name, "T": w2.T},
-                        "dtype": "f16 x int4 (routed), bf16 (shared)" if w2.quant == "int4" else w2.dtype,
+                        "dtype": {"int4": "f16 x int4 (routed), bf16 (shared)",
+                                  "fp8": "f16 x e4m3 (routed), bf16 (shared)"}.get(w2.quant, w2.dtype),
                         "roofline": r2["roofline"],
                         "layer": r2["layer"], "kernels_us": r2["kernels_us"]}
     weights_cache.clear()

@@ -10,6 +10,8 @@
  *   [ZH-INFRA]    Zhihu answer by a K2 inference engineer on the K2 config:
  *                 §2.1 num_experts = 384, §2.4 n_group = 1.
  *   [ZH-PRETRAIN] Zhihu answer by a K2 pretraining author, "架构 / 异": scaling factor 2.5 -> 2.827.
+ *   [BAIDU]       Baidu developer article on K2-Instruct (developer.baidu.com, article 8800668):
+ *                 §3.2 inference acceleration, item 1 (FP8 quantization).
  *
  * The layer, per token t (rows are independent):
  *   l_e = x_t . Wr_e (+ o_e);  s_e = sigmoid(l_e);  key_e = s_e + b_e
@@ -75,7 +77,8 @@ typedef enum {
   MOE_OP_COMBINE = 3,
   MOE_OP_FORWARD = 4,
   MOE_OP_FORWARD_ROUTED = 5,
-  MOE_OP_FORWARD_Q4 = 6
+  MOE_OP_FORWARD_Q4 = 6,
+  MOE_OP_FORWARD_FP8 = 7
 } moe_op;
 
 /* The MoE config fields of the K2 layer ([DEEP] §4.2-§4.3; [ZH-INFRA] §2.4). Host struct. */
@@ -94,7 +97,7 @@ typedef struct moe_config {
 
 /* Bytes of workspace the call `op` needs.
  *   MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_COMBINE, MOE_OP_FORWARD, MOE_OP_FORWARD_ROUTED,
- *   MOE_OP_FORWARD_Q4: rows = T (tokens), n_groups ignored.
+ *   MOE_OP_FORWARD_Q4, MOE_OP_FORWARD_FP8: rows = T (tokens), n_groups ignored.
  *   MOE_OP_GROUPED_SWIGLU: rows = max_rows, n_groups = number of groups.
  * Returns 0 for an invalid config (see moe_last_error()). */
 size_t moe_workspace_size(const moe_config* cfg, int32_t op, int64_t rows, int32_t n_groups);
@@ -202,6 +205,36 @@ int moe_forward_q4(const moe_config* cfg, int64_t T, const void* x, const void* 
                    const uint32_t* down_codes, const uint16_t* down_scales, const void* ws_gate,
                    const void* ws_up, const void* ws_down, void* y, int32_t* topk_ids_out,
                    float* topk_weights_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The whole layer with FP8 routed experts: the FP8 quantization of [BAIDU] §3.2 item 1 (weights
+ * in 8 bits, half the bytes of bf16), which fixes neither the format nor the scaling.  Read here
+ * as OCP E4M3 codes with one fp32 scale per 128 x 128 block of each routed-expert matrix; as for
+ * the 4-bit weights ([QA] Q7.1) only the storage is quantized, the shared expert stays bf16, and
+ * the layer is Steps 1-7 of [DEEP] §10.2.
+ * As moe_forward, except that each routed-expert matrix W [E, N, K] comes as
+ *   codes  [E, N, K] uint8: OCP E4M3 (bit 7 sign, bits 6..3 exponent with bias 7, bits 2..0
+ *          mantissa; exponent 0 = subnormal, 2^-6 * m/8; largest 448).  0x7f and 0xff (NaN) are
+ *          not valid codes.
+ *   scales [E, N/128, K/128] fp32: s[n/128, k/128]
+ *   W[n, k] = e4m3(code[n, k]) * s[n/128, k/128]
+ * i.e. gate_codes, up_codes [E, I, H], gate_scales, up_scales [E, I/128, H/128],
+ *      down_codes [E, H, I], down_scales [E, H/128, I/128].
+ * Precision: dtype must be MOE_BF16.  The routed experts multiply in binary16 with fp32
+ * accumulation: x is rounded once to binary16 (|x| must stay below 65504), every code enters the
+ * matmul exactly (E4M3 values are binary16 values), each 128-input block's partial sum is
+ * multiplied by its scale in fp32, SiLU(g)*u is rounded to binary16 between the two matmuls,
+ * y_rows to bf16.  The shared expert and the combine are as in moe_forward.
+ * Shapes: as moe_forward, with hidden_size and moe_intermediate_size multiples of 128 and at
+ * most 8192 (else MOE_ERR_UNSUPPORTED).
+ * Each routed expert that received tokens has its codes read once per 8 of its rows (the kernels
+ * stream weights; they are built for decode-sized T, about one row per expert).
+ * Workspace: moe_workspace_size(cfg, MOE_OP_FORWARD_FP8, T, 0). */
+int moe_forward_fp8(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                    const float* score_bias, const float* logit_offset, const uint8_t* gate_codes,
+                    const float* gate_scales, const uint8_t* up_codes, const float* up_scales,
+                    const uint8_t* down_codes, const float* down_scales, const void* ws_gate,
+                    const void* ws_up, const void* ws_down, void* y, int32_t* topk_ids_out,
+                    float* topk_weights_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Message of the last failed call on this thread ("" if none); valid until the next call. */
 const char* moe_last_error(void);

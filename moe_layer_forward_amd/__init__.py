@@ -21,10 +21,11 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_GROUPED_SWIGLU, MOE_OP_COMBINE, MOE_OP_FORWARD,
- MOE_OP_FORWARD_ROUTED, MOE_OP_FORWARD_Q4) = range(7)
+ MOE_OP_FORWARD_ROUTED, MOE_OP_FORWARD_Q4, MOE_OP_FORWARD_FP8) = range(8)
 
 EXPORTED = ("moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "moe_forward",
-            "moe_forward_routed", "moe_forward_q4", "moe_last_error", "moe_profile_events", "moe_profile_count", "moe_profile_kernel")
+            "moe_forward_routed", "moe_forward_q4", "moe_forward_fp8", "moe_last_error", "moe_profile_events",
+            "moe_profile_count", "moe_profile_kernel")
 
 
 class MoeConfig(ctypes.Structure):
@@ -76,8 +77,9 @@ def load_library():
         lib.moe_forward.argtypes = [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.moe_forward_routed.argtypes = [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.moe_forward_q4.argtypes = [cfgp, i64] + [vp] * 17 + [sz, vp]
+        lib.moe_forward_fp8.argtypes = [cfgp, i64] + [vp] * 17 + [sz, vp]
         for name in ("moe_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "moe_forward",
-                     "moe_forward_routed", "moe_forward_q4"):
+                     "moe_forward_routed", "moe_forward_q4", "moe_forward_fp8"):
             getattr(lib, name).restype = ctypes.c_int
         lib.moe_last_error.argtypes = []
         lib.moe_last_error.restype = ctypes.c_char_p
@@ -253,6 +255,33 @@ def moe_forward_routed(cfg, x, topk_ids, topk_weights, w_gate, w_up, w_down, ws_
     return y
 
 
+QUANT_KEYS = ("gate_codes", "gate_scales", "up_codes", "up_scales", "down_codes", "down_scales")
+
+
+def _forward_quant(entry, op, word_bytes, cfg, x, w_router, q, ws_gate, ws_up, ws_down, score_bias, logit_offset,
+                   return_routing, workspace, out):
+    import torch
+
+    T = x.shape[0]
+    qt = [q[n] for n in QUANT_KEYS]
+    for n, t in zip(QUANT_KEYS, qt):
+        want = word_bytes[0] if n.endswith("codes") else word_bytes[1]
+        if t.element_size() != want:
+            raise ValueError(f"{n} must hold {8 * want}-bit elements, got {t.dtype}")
+    dev, stream = _dev(x, w_router, *qt, ws_gate, ws_up, ws_down, score_bias, logit_offset)
+    y = out if out is not None else torch.empty((T, cfg.hidden_size), dtype=torch.bfloat16, device=dev)
+    ids = wts = None
+    if return_routing:
+        ids = torch.empty((T, cfg.top_k), dtype=torch.int32, device=dev)
+        wts = torch.empty((T, cfg.top_k), dtype=torch.float32, device=dev)
+    ws = workspace if workspace is not None else alloc_workspace(cfg, op, T, 0, dev)
+    _check(getattr(load_library(), entry)(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(score_bias),
+                                          _ptr(logit_offset), *[_ptr(t) for t in qt], _ptr(ws_gate), _ptr(ws_up),
+                                          _ptr(ws_down), _ptr(y), _ptr(ids), _ptr(wts), _ptr(ws), ws.numel(),
+                                          stream))
+    return (y, ids, wts) if return_routing else y
+
+
 def moe_forward_q4(cfg, x, w_router, q4, ws_gate=None, ws_up=None, ws_down=None, score_bias=None,
                    logit_offset=None, return_routing=False, workspace=None, out=None):
     """The layer with 4-bit routed experts: returns y [T, H] bf16 (and the routing when asked).
@@ -260,25 +289,18 @@ def moe_forward_q4(cfg, x, w_router, q4, ws_gate=None, ws_up=None, ws_down=None,
     q4 holds the routed experts' codes and scales: a mapping with keys gate_codes, gate_scales,
     up_codes, up_scales, down_codes, down_scales (codes int32/uint32 words, scales 16-bit words of
     binary16 values; layouts as in include/moe.h)."""
-    import torch
+    return _forward_quant("moe_forward_q4", MOE_OP_FORWARD_Q4, (4, 2), cfg, x, w_router, q4, ws_gate, ws_up,
+                          ws_down, score_bias, logit_offset, return_routing, workspace, out)
 
-    T = x.shape[0]
-    names = ("gate_codes", "gate_scales", "up_codes", "up_scales", "down_codes", "down_scales")
-    qt = [q4[n] for n in names]
-    for n, t in zip(names, qt):
-        if t.element_size() != (4 if n.endswith("codes") else 2):
-            raise ValueError(f"{n} must hold {'32' if n.endswith('codes') else '16'}-bit words, got {t.dtype}")
-    dev, stream = _dev(x, w_router, *qt, ws_gate, ws_up, ws_down, score_bias, logit_offset)
-    y = out if out is not None else torch.empty((T, cfg.hidden_size), dtype=torch.bfloat16, device=dev)
-    ids = wts = None
-    if return_routing:
-        ids = torch.empty((T, cfg.top_k), dtype=torch.int32, device=dev)
-        wts = torch.empty((T, cfg.top_k), dtype=torch.float32, device=dev)
-    ws = workspace if workspace is not None else alloc_workspace(cfg, MOE_OP_FORWARD_Q4, T, 0, dev)
-    _check(load_library().moe_forward_q4(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(score_bias),
-                                         _ptr(logit_offset), *[_ptr(t) for t in qt], _ptr(ws_gate), _ptr(ws_up),
-                                         _ptr(ws_down), _ptr(y), _ptr(ids), _ptr(wts), _ptr(ws), ws.numel(), stream))
-    return (y, ids, wts) if return_routing else y
+
+def moe_forward_fp8(cfg, x, w_router, f8, ws_gate=None, ws_up=None, ws_down=None, score_bias=None,
+                    logit_offset=None, return_routing=False, workspace=None, out=None):
+    """The layer with FP8 routed experts: returns y [T, H] bf16 (and the routing when asked).
+
+    f8 holds the routed experts' codes and scales under the same keys as for moe_forward_q4 (codes
+    uint8 OCP E4M3 [E, N, K], scales float32 [E, N/128, K/128]; layouts as in include/moe.h)."""
+    return _forward_quant("moe_forward_fp8", MOE_OP_FORWARD_FP8, (1, 4), cfg, x, w_router, f8, ws_gate, ws_up,
+                          ws_down, score_bias, logit_offset, return_routing, workspace, out)
 
 
 def moe_profile_events(events_array, n_events: int):

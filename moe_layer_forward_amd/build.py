@@ -30,7 +30,7 @@ HIP_FLAGS = [
 ]
 
 MOE_SOURCES = ["moe_api.cpp", "route.hip", "permute.hip", "gemm_stream.hip", "gemm_tile.hip",
-               "gemm_q4.hip", "gemm_simple.hip", "combine.hip"]
+               "gemm_quant.hip", "gemm_simple.hip", "combine.hip"]
 
 
 def _run(cmd, verbose):

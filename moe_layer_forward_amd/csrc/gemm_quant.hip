@@ -1,27 +1,41 @@
-// 4-bit routed experts, weight streaming (decode-like shapes, few rows per expert).
+// Quantized routed experts, weight streaming (decode-like shapes, few rows per expert).
 //
-// Routed-expert weights are stored as "Kimi K2.5 模型架构深度拆解" §7.2 configures them: signed
-// 4-bit integers, one scale per 32 consecutive inputs, symmetric (w = q * s).  In memory:
-//   codes  [G, N, K/8]  uint32: q of input k in bits 4*(k % 8) of word k/8, two's complement
-//   scales [G, N, K/32] binary16
-// Only the storage is quantized ("Kimi K2.5 架构 QA" Q7.1): the codes enter the matmuls as exact
-// integers and each group's scale is applied in fp32.  The matmuls run on v_mfma_f32_16x16x32_f16,
-// with the token rows converted once from bf16 to binary16 (f16_rows_kernel) and h kept in binary16.
+// Two storage formats of the routed-expert weights W [G, N, K], one kernel design:
+//  * 4-bit, as "Kimi K2.5 模型架构深度拆解" §7.2 configures them: signed 4-bit integers, one scale
+//    per 32 consecutive inputs, symmetric (w = q * s).  In memory:
+//      codes  [G, N, K/8]  uint32: q of input k in bits 4*(k % 8) of word k/8, two's complement
+//      scales [G, N, K/32] binary16
+//  * 8-bit floating point, the FP8 quantization of the Baidu developer article on K2-Instruct
+//    (developer.baidu.com article 8800668, §3.2 item 1), which fixes neither format nor scaling;
+//    read here as OCP E4M3 codes with one fp32 scale per 128 x 128 block of each matrix:
+//      codes  [G, N, K] bytes (sign, 4 exponent bits with bias 7, 3 mantissa bits)
+//      scales [G, N/128, K/128] fp32;  w = e4m3(code) * s
+// Only the storage is quantized ("Kimi K2.5 架构 QA" Q7.1): the matmuls run on
+// v_mfma_f32_16x16x32_f16 with every code entering exactly, the token rows converted once from bf16
+// to binary16 (f16_rows_kernel) and h kept in binary16, and the scales are applied in fp32 to
+// partial sums.
 //
-// Decoding: after xor with 0x88888888 a code is offset binary u = q + 8; a field in bits 0..3 of a
-// 16-bit half ORed into 0x6400 reads 1024 + u, a field in bits 4..7 ORed into 0x5400 reads 64 + u,
-// and since the OR constant is disjoint from the field, xor + mask + OR is one v_bitop3_b32.  A
-// word's 8 codes come out in the order 0,4,1,5,2,6,3,7, so every operand keeps each group of 8
-// inputs in that order (x16 and h are written that way; the dot product is unchanged).  Per group
-// of 32 inputs one MFMA against the constant -(1032 | 72) seeds the accumulator of the two weight
-// sets' MFMAs, which leaves c = sum x*q exactly in fp32; then acc += s * c.
+// 4-bit decoding: after xor with 0x88888888 a code is offset binary u = q + 8; a field in bits 0..3
+// of a 16-bit half ORed into 0x6400 reads 1024 + u, a field in bits 4..7 ORed into 0x5400 reads
+// 64 + u, and since the OR constant is disjoint from the field, xor + mask + OR is one
+// v_bitop3_b32.  A word's 8 codes come out in the order 0,4,1,5,2,6,3,7, so every operand keeps
+// each group of 8 inputs in that order (x16 and h are written that way; the dot product is
+// unchanged).  Per group of 32 inputs one MFMA against the constant -(1032 | 72) seeds the
+// accumulator of the two weight sets' MFMAs, which leaves c = sum x*q exactly in fp32; then
+// acc += s * c.
+// FP8 decoding: a byte permute puts the codes of inputs (0,4,1,5) and (2,6,3,7) of a group of 8 into
+// one word each (the same operand order), and v_cvt_scalef32_pk_f16_fp8 with scale 1 turns two
+// codes into two binary16 values (every E4M3 value is a normal binary16 value, so exactly).  The 4
+// MFMAs of a step (128 inputs, one scale block) sum into a partial that is scaled into acc in fp32.
 //
 // The stream: a wave streams two 16-row sets of weight rows (gate + up of 16 h columns, or 32 rows
 // of W_down) through a 4-stage LDS ring of direct buffer->LDS loads, one instruction = 8 rows x 128
 // contiguous bytes (whole lines) with the streaming policy; the 16-byte chunk c of a 128-byte row r
 // sits at c ^ ((r >> 1) & 7) so the 16 rows of one B-operand read hit different banks.  A step
-// covers 256 inputs (8 groups).  The token rows of a pass (4 rows) are shared by the work-group's 4
-// waves through the same ring (a barrier per step); the scales come a 4-step block at a time.
+// covers 128 bytes of codes per row (256 inputs of 4-bit codes, 128 of FP8).  The token rows of a
+// pass (4 rows of 256 inputs, or 8 rows of 128) are shared by the work-group's 4 waves through the
+// same ring (a barrier per step); the 4-bit scales come a 4-step block at a time through LDS, the
+// FP8 scales of a wave's whole rows sit one per lane in a register.
 // Work-groups = 4 waves; groups from the plan's active list, largest first; the first work-groups
 // of a launch stream the bf16 shared expert instead.
 #include <type_traits>
@@ -33,24 +47,49 @@ namespace moe {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = 4;
-constexpr int kStepK = 256;             // inputs per step
-constexpr int kCodeRowB = kStepK / 2;   // 128 bytes of codes per row per step
+constexpr int kCodeRowB = 128;          // bytes of codes per row per step
 constexpr int kSetCodeB = 16 * kCodeRowB;
 constexpr int kWaveB = 2 * kSetCodeB;   // one wave's part of the codes of one ring stage
 constexpr int kCodesB = kWaves * kWaveB;
-constexpr int kPassRows = 4;           // token rows per pass over the weights (MFMA rows 4.. are padding)
-constexpr int kARowB = 2 * kStepK;      // 512 bytes of one f16 token row per step
-constexpr int kAB = kPassRows * kARowB; // a pass's token rows of one step, shared by the waves
+constexpr int kAB = 2048;               // a pass's token rows of one step, shared by the waves
 constexpr int kStageB = kCodesB + kAB;
-constexpr int kD = 4;                   // ring stages = steps in flight = steps per scale block
+constexpr int kD = 4;                   // ring stages = steps in flight = steps per 4-bit scale block
 constexpr int kScaleRowB = kD * 16;     // a row's binary16 scales for the kD steps of a block
 constexpr int kScaleSetB = 16 * kScaleRowB;  // = one 64-lane 16-byte store
 constexpr int kScaleWaveB = 2 * kScaleSetB;  // one wave's part of one scale buffer
+
+// Per-format geometry: inputs per step, token rows per pass (MFMA rows past them are padding).
+template <QFormat F>
+struct Fmt;
+template <>
+struct Fmt<QFormat::kInt4> {
+  static constexpr int kStepK = 256;
+  static constexpr int kPassRows = 4;
+};
+template <>
+struct Fmt<QFormat::kFp8> {
+  static constexpr int kStepK = 128;
+  static constexpr int kPassRows = 8;
+  static constexpr int kBlock = 128;   // scale block edge
+  static constexpr int kMaxSteps = 64; // a wave's row of scales fits one register of 64 lanes
+};
+// bytes of f16 token row per step, and bytes of codes per weight row of K inputs
+template <QFormat F>
+constexpr int a_row_bytes() {
+  return 2 * Fmt<F>::kStepK;
+}
+template <QFormat F>
+constexpr int64_t code_row_bytes(int64_t K) {
+  return K * kCodeRowB / Fmt<F>::kStepK;
+}
+static_assert(Fmt<QFormat::kInt4>::kPassRows * a_row_bytes<QFormat::kInt4>() == kAB, "token rows of a step");
+static_assert(Fmt<QFormat::kFp8>::kPassRows * a_row_bytes<QFormat::kFp8>() == kAB, "token rows of a step");
 
 // Compile-time loop: f(integral_constant<int, I>) for I = 0 .. N-1.
 template <int N, int I = 0, class F>
@@ -61,16 +100,16 @@ __device__ __forceinline__ void static_for(const F& f) {
   }
 }
 
-struct Q4Args {
+struct QArgs {
   const int32_t* group_offsets;
   const int32_t* row_index;  // gate/up: token row of each routed row
   const int32_t* active;
   const int32_t* counters;
   int64_t max_rows;
-  const uint32_t* codes0;    // gate (gate/up) or down codes
-  const uint16_t* scales0;
-  const uint32_t* codes1;    // up codes (gate/up)
-  const uint16_t* scales1;
+  const void* codes0;        // gate (gate/up) or down codes
+  const void* scales0;
+  const void* codes1;        // up codes (gate/up)
+  const void* scales1;
   const uint16_t* a;         // f16 rows, groups of 8 inputs in the order 0,4,1,5,2,6,3,7
   uint32_t a_bytes;          // bytes of a the kernel may read (< 4 GiB)
   void* out;
@@ -122,6 +161,19 @@ __device__ __forceinline__ f16x8 bias_operand() {
   return f16x8{a, a, b, b, a, a, b, b};
 }
 
+// The 8 E4M3 codes of inputs 0..7 (bytes of w.x then w.y) as binary16 values in the operand order
+// 0,4,1,5,2,6,3,7: v_perm_b32 gathers bytes (0,4,1,5) and (2,6,3,7), and each conversion takes the
+// low or the high byte pair of a word.
+__device__ __forceinline__ f16x8 decode_fp8(u32x2 w) {
+  const uint32_t p0 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // bytes: codes 0, 4, 1, 5
+  const uint32_t p1 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // codes 2, 6, 3, 7
+  const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(p0, 1.0f, false);
+  const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(p0, 1.0f, true);
+  const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(p1, 1.0f, false);
+  const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(p1, 1.0f, true);
+  return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
 // Buffer descriptor of `bytes` bytes at base: a load at an offset past the end returns zeros and
@@ -134,21 +186,29 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
 
 typedef __attribute__((address_space(3))) void* LdsPtr;
 
-// Token rows in a ring stage: row r of the pass at r * kARowB, its 16-byte piece g at position
-// g ^ (4 * r), so the rows one A-operand read touches fall in different banks.
-__device__ __forceinline__ int a_pos(int r, int g) { return g ^ (4 * r); }
+// Token rows in a ring stage: row r of the pass at r * a_row_bytes, its 16-byte piece g at a
+// position xor-ed with the row (4-bit: 4 rows of 32 pieces, g ^ 4r; FP8: 8 rows of 16 pieces,
+// g ^ r), so the rows one A-operand read touches fall in different banks.
+template <QFormat F>
+__device__ __forceinline__ int a_pos(int r, int g) {
+  return F == QFormat::kInt4 ? g ^ (4 * r) : g ^ r;
+}
 
-struct Q4Stream {
+template <QFormat F>
+struct QStream {
+  static constexpr bool kQ4 = F == QFormat::kInt4;
+  static constexpr int kPassRows = Fmt<F>::kPassRows;
+  static constexpr int kARowB = a_row_bytes<F>();
   static constexpr int kLoads = 2 * 2 + 1;  // per step: codes, and this wave's half of the token rows
-  static constexpr int kScaleLoads = 2;     // per block of kD steps: scales (into registers)
+  static constexpr int kScaleLoads = kQ4 ? 2 : 0;  // per block of kD steps: 4-bit scales (into registers)
   static_assert(2 * kLoads + kScaleLoads <= 63, "vmcnt");
 
   const void* cb[2];        // codes of each set's 16 rows (uniform)
-  const void* sb[2];        // scales of each set's 16 rows (uniform)
+  const void* sb[2];        // scales of each set's rows (uniform; FP8: the wave's block row)
   const void* abase;        // token rows (f16)
-  uint32_t c_bytes, s_bytes, a_bytes;
+  uint32_t c_bytes, s_bytes, a_bytes;  // bytes the descriptors of codes, scales, token rows span
   uint32_t c_off[2];        // lane offsets of the two direct loads of a set (row, swizzled chunk)
-  uint32_t s_off;           // lane offset of the scale load (row lane/4, piece lane%4 of a block)
+  uint32_t s_off;           // 4-bit: lane offset of the scale load (row lane/4, piece lane%4 of a block)
   uint32_t a_off;           // lane offset of this wave's token-row load (row, swizzled piece)
   uint32_t blk_cb, blk_sb;  // bytes between consecutive column blocks of the codes / the scales
   int wave_off, sc_wave_off, a_dst;  // this wave's codes, scale buffer, and token-row half
@@ -185,9 +245,9 @@ struct Q4Stream {
     }
   }
 
-  // Half of the pass's token rows of step k (2 rows, 1 KiB) into ring stage d (the same rows for
-  // every column block).  Waves w and w + 2 load the same half: identical bytes to the same place,
-  // and every wave issues the same loads.
+  // Half of the pass's token rows of step k (1 KiB) into ring stage d (the same rows for every
+  // column block).  Waves w and w + 2 load the same half: identical bytes to the same place, and
+  // every wave issues the same loads.
   __device__ __forceinline__ void issue_rows(char* const (&ring)[kD], int d, int b, int k, int nblk) const {
     b = __builtin_amdgcn_readfirstlane(b);
     k = __builtin_amdgcn_readfirstlane(k);
@@ -196,9 +256,9 @@ struct Q4Stream {
                                              a_off + (uint32_t)k * kARowB, 0, 0, 0);
   }
 
-  // The scales of steps k .. k + kD - 1 of column block b (k a multiple of kD) into registers: lane l
-  // holds the 16 bytes of step k + l%4 of row l/4 (each scale line in two requests, not eight).  Past
-  // the last block they read nothing.
+  // 4-bit: the scales of steps k .. k + kD - 1 of column block b (k a multiple of kD) into
+  // registers: lane l holds the 16 bytes of step k + l%4 of row l/4 (each scale line in two
+  // requests, not eight).  Past the last block they read nothing.
   __device__ __forceinline__ void issue_scales(int b, int k, int nblk, u32x4 (&sr)[2]) const {
     b = __builtin_amdgcn_readfirstlane(b);
     k = __builtin_amdgcn_readfirstlane(k);
@@ -218,15 +278,15 @@ struct Q4Stream {
     for (int r = 0; r < 2; ++r) *reinterpret_cast<u32x4*>(sc + sc_wave_off + r * kScaleSetB + lane * 16) = sr[r];
   }
 
-  // One step: for each group j of 32 inputs, c = A_j . (-bias) + A_j . (1024|64 + u) = A_j . q (exact
-  // integer weights, fp32 sums), then acc += s_j * c with the group's scale in fp32.  Software
-  // pipelined by hand: code words and token-row fragments are read one group ahead, and group j's
-  // products are scaled into acc while group j+1's matmuls run (scheduling barriers keep the
-  // compiler from hoisting more).  d: ring stage; sc: the scale buffer holding the step's block.
-  __device__ __forceinline__ void compute(char* const (&ring)[kD], int d, const char* sc, f32x4 (&acc)[2]) const {
+  // One 4-bit step: for each group j of 32 inputs, c = A_j . (-bias) + A_j . (1024|64 + u) = A_j . q
+  // (exact integer weights, fp32 sums), then acc += s_j * c with the group's scale in fp32.
+  // Software pipelined by hand: code words and token-row fragments are read one group ahead, and
+  // group j's products are scaled into acc while group j+1's matmuls run (scheduling barriers keep
+  // the compiler from hoisting more).  d: ring stage; sc: the scale buffer holding the step's block.
+  __device__ __forceinline__ void compute_q4(char* const (&ring)[kD], int d, const char* sc, f32x4 (&acc)[2]) const {
     const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
     const char* src = ring[d] + wave_off + c * kCodeRowB + 4 * q;
-    const int ar = c & (kPassRows - 1);  // MFMA rows 4.. repeat rows 0..3 (never stored)
+    const int ar = c & (kPassRows - 1);  // MFMA rows kPassRows.. repeat the pass's rows (never stored)
     const char* arow = ring[d] + kCodesB + ar * kARowB;
     u32x4 sv[2];  // the step's 8 scales of row c of each set
 #pragma unroll
@@ -239,7 +299,7 @@ struct Q4Stream {
 #pragma unroll
       for (int r = 0; r < 2; ++r)
         wd[r] = *reinterpret_cast<const uint32_t*>(src + r * kSetCodeB + ((j ^ code_swz(c)) << 4));
-      af = *reinterpret_cast<const u32x4*>(arow + (a_pos(ar, 4 * j + q) << 4));
+      af = *reinterpret_cast<const u32x4*>(arow + (a_pos<F>(ar, 4 * j + q) << 4));
     };
     uint32_t wd[2][2];
     u32x4 af[2];
@@ -273,6 +333,40 @@ struct Q4Stream {
       for (int e = 0; e < 4; ++e) acc[r][e] = __builtin_fmaf(pend_s[r], pend[r][e], acc[r][e]);
   }
 
+  // One FP8 step (128 inputs = one scale block along K): 4 groups of 32 inputs, lane (column c,
+  // quarter q) holding inputs 32j + 8q .. +7 of group j; the 4 products of a set sum into a partial
+  // in fp32, and acc += s * partial with the block's scale, read from lane `si` of fsc (each set's
+  // scale of column block b, step k in lane b * ksteps + k).
+  __device__ __forceinline__ void compute_fp8(char* const (&ring)[kD], int d, int si, const uint32_t (&fsc)[2],
+                                              f32x4 (&acc)[2]) const {
+    const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
+    const char* src = ring[d] + wave_off + c * kCodeRowB + 8 * (q & 1);
+    const int ar = c & (kPassRows - 1);  // MFMA rows kPassRows.. repeat the pass's rows (never stored)
+    const char* arow = ring[d] + kCodesB + ar * kARowB;
+    u32x2 wd[4][2];
+    u32x4 af[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        wd[j][r] = *reinterpret_cast<const u32x2*>(src + r * kSetCodeB + (((2 * j + (q >> 1)) ^ code_swz(c)) << 4));
+      af[j] = *reinterpret_cast<const u32x4*>(arow + (a_pos<F>(ar, 4 * j + q) << 4));
+    }
+    f32x4 part[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        part[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, af[j]), decode_fp8(wd[j][r]),
+                                                        part[r], 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(fsc[r], si));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[r][e] = __builtin_fmaf(s, part[r][e], acc[r][e]);
+    }
+  }
+
   // The K loop of one pass over CHAIN consecutive column blocks of ksteps steps each (one pipeline:
   // the loads of block b + 1's first steps are issued during block b's last steps; CHAIN > 1 needs
   // ksteps % kD == 0).  The token rows of a step are shared by the work-group's waves, so every
@@ -281,13 +375,22 @@ struct Q4Stream {
   // step kD - 1 later (the stage's codes were refilled at the end of the previous step).  Loads past
   // the end read nothing, so the waits are fixed; steps past a block's end (CHAIN == 1 only) skip
   // the multiply.  Loads in issue order: ... rows(v), codes(v+1), rows(v+1), codes(v+2), ..., with
-  // a scale block's scales just before the codes of its first step.
+  // (4-bit) a scale block's scales just before the codes of its first step.
+  // FP8: the pass's scales go to one register per set (lane b * ksteps + k), loaded first.
   template <int CHAIN>
   __device__ __forceinline__ void run(char* const (&ring)[kD], char* sc, int ksteps, f32x4 (&acc)[CHAIN][2]) const {
     u32x4 sr[2];
+    uint32_t fsc[2];
     __builtin_amdgcn_s_barrier();  // the previous pass is done with the shared rows
     // the prologue in issue order, fenced against reordering (the waits below count on it)
-    issue_scales(0, 0, CHAIN, sr);
+    if constexpr (kQ4) {
+      issue_scales(0, 0, CHAIN, sr);
+    } else {
+      const int lane = threadIdx.x & 63;
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        fsc[r] = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(sb[r], s_bytes), lane * 4, 0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
     static_for<kD>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
@@ -298,6 +401,10 @@ struct Q4Stream {
       if constexpr (i + 1 < kD) issue_rows(ring, i, b2, k2, CHAIN);
       __builtin_amdgcn_sched_barrier(0);
     });
+    // FP8: have the compiler wait for the scales here, where it can count the loads issued after
+    // them (they arrive before the first codes anyway); left to the K loop, it loses count across
+    // the column blocks and drains every load in flight at the first scale read
+    if constexpr (!kQ4) asm volatile("" : "+v"(fsc[0]), "+v"(fsc[1]));
     static_for<CHAIN>([&](auto bc) {
       constexpr int b = decltype(bc)::value;
       for (int g = 0; g < ksteps; g += kD) {
@@ -305,17 +412,22 @@ struct Q4Stream {
           constexpr int i = decltype(ic)::value;
           const int k = g + i;
           // after rows(v): codes and rows of the next kD - 2 steps, the codes of the one after,
-          // and a scale block's scales among them unless this step starts one
+          // and (4-bit) a scale block's scales among them unless this step starts one
           wait_vmcnt<(kD - 1) * 4 + (kD - 2) * 1 + (i == 0 ? 0 : kScaleLoads)>();
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_sched_barrier(0);
           int b2, k2;
           adv(b, k, kD - 1, ksteps, b2, k2);
           issue_rows(ring, (i + kD - 1) % kD, b2, k2, CHAIN);
-          if constexpr (i == 0) store_scales(sc, sr);  // this scale block, loaded a block ago
-          if (k < ksteps) compute(ring, i, sc, acc[b]);
+          if constexpr (kQ4 && i == 0) store_scales(sc, sr);  // this scale block, loaded a block ago
+          if (k < ksteps) {
+            if constexpr (kQ4)
+              compute_q4(ring, i, sc, acc[b]);
+            else
+              compute_fp8(ring, i, __builtin_amdgcn_readfirstlane(b * ksteps + k), fsc, acc[b]);
+          }
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this stage's LDS reads are done
-          if constexpr (i == 0) {
+          if constexpr (kQ4 && i == 0) {
             adv(b, g, kD, ksteps, b2, k2);
             issue_scales(b2, k2, CHAIN, sr);
           }
@@ -329,28 +441,32 @@ struct Q4Stream {
 };
 
 // Column blocks per work-group of the down launch (a pipeline over 2 x 128 W_down rows): W_down's
-// rows are short (I/256 steps), so one block alone would mostly fill and drain the ring.
+// rows are short (I/256 4-bit steps, I/128 FP8 steps), so one block alone would mostly fill and
+// drain the ring.
 constexpr int kDownChain = 2;
 
-template <bool SWIGLU, int CHAIN>
-__device__ __forceinline__ void q4_pass(const Q4Args& p, char* const (&ring)[kD], char* sc, const Q4Stream& base,
-                                        int n0, int64_t mb, int64_t r1) {
+template <QFormat F, bool SWIGLU, int CHAIN>
+__device__ __forceinline__ void q_pass(const QArgs& p, char* const (&ring)[kD], char* sc, const QStream<F>& base,
+                                       int n0, int64_t mb, int64_t r1) {
+  constexpr int kPassRows = Fmt<F>::kPassRows;
+  constexpr int kARowB = a_row_bytes<F>();
+  constexpr int kRowLanes = kARowB / 16;  // lanes per token row of a wave's load
   const int H = p.H, I = p.I, K = SWIGLU ? H : I;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  Q4Stream s = base;
-  {  // this wave's rows 2(w % 2) + lane/32, piece position lane % 32
-    const int rl = 2 * (wave & 1) + (lane >> 5);
+  QStream<F> s = base;
+  {  // this wave's row (kPassRows/2)(w % 2) + lane/kRowLanes, piece position lane % kRowLanes
+    const int rl = (kPassRows / 2) * (wave & 1) + lane / kRowLanes;
     const int64_t r = mb + rl;
     const int64_t rr = r < r1 ? r : mb;  // rows past the group end repeat its first row, never stored
     const int64_t src = SWIGLU ? (p.row_index ? (int64_t)p.row_index[rr] : rr) : rr;
-    s.a_off = (uint32_t)(src * K * 2 + (a_pos(rl, lane & 31) << 4));
+    s.a_off = (uint32_t)(src * K * 2 + (a_pos<F>(rl, lane % kRowLanes) << 4));
   }
-  s.a_dst = (wave & 1) * 2 * kARowB;
+  s.a_dst = (wave & 1) * (kAB / 2);
   f32x4 acc[CHAIN][2];
 #pragma unroll
   for (int b = 0; b < CHAIN; ++b) acc[b][0] = acc[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  s.template run<CHAIN>(ring, sc, K / kStepK, acc);
+  s.template run<CHAIN>(ring, sc, K / Fmt<F>::kStepK, acc);
 
   // lane holds MFMA rows 4*(lane/16) + e, column n0 + lane%16 (+16 for set 1 of down, +128 per
   // further column block); the pass's rows are MFMA rows 0 .. kPassRows-1
@@ -359,7 +475,7 @@ __device__ __forceinline__ void q4_pass(const Q4Args& p, char* const (&ring)[kD]
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int64_t row = mb + 4 * (lane >> 4) + e;
-    if ((lane >> 4) != 0 || row >= rend) continue;
+    if ((lane >> 4) >= kPassRows / 4 || row >= rend) continue;
     if constexpr (SWIGLU) {
       // h in f16, each group of 8 columns in the operand order of the down matmul
       const _Float16 v = (_Float16)swiglu_f32(acc[0][0][e], acc[0][1][e]);
@@ -441,7 +557,7 @@ struct ShStream {
       }
   }
 
-  // As Q4Stream::run, without scales.
+  // As QStream::run, without scales.
   __device__ __forceinline__ void run(char* const (&ring)[kD], int nsteps, f32x4 (&acc)[kShNP][2]) const {
     ShSlot sl[kD];
     static_for<kD>([&](auto ic) {
@@ -464,7 +580,7 @@ struct ShStream {
 
 // Work-group blk of the shared expert: output columns of 4 waves, every row of the expert.
 template <bool SWIGLU>
-__device__ __forceinline__ void shared_part(const Q4Args& p, char* const (&ring)[kD], int blk) {
+__device__ __forceinline__ void shared_part(const QArgs& p, char* const (&ring)[kD], int blk) {
   const int H = p.H, I = p.I, K = SWIGLU ? H : I;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -511,11 +627,11 @@ __device__ __forceinline__ void shared_part(const Q4Args& p, char* const (&ring)
   }
 }
 
-template <bool SWIGLU, int CHAIN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void q4_stream_kernel(Q4Args p) {
+template <QFormat F, bool SWIGLU, int CHAIN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void q_stream_kernel(QArgs p) {
   // one array per stage: the compiler then tells the stages' direct loads and LDS reads apart
   __shared__ __align__(16) char s0[kStageB], s1[kStageB], s2[kStageB], s3[kStageB];
-  __shared__ __align__(16) char sc[kWaves * kScaleWaveB];
+  __shared__ __align__(16) char sc[F == QFormat::kInt4 ? kWaves * kScaleWaveB : 16];
   static_assert(kD == 4, "one LDS array per ring stage");
   char* const ring[kD] = {s0, s1, s2, s3};
 
@@ -541,32 +657,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // rows of the two 16-row sets: gate and up rows n0.. (gate/up), or W_down rows n0.. and n0+16..
   const int64_t row0[2] = {n0, SWIGLU ? n0 : n0 + 16};
-  const uint32_t* cm[2] = {p.codes0 + (int64_t)g * N * (K / 8), (SWIGLU ? p.codes1 : p.codes0) + (int64_t)g * N * (K / 8)};
-  const uint16_t* sm[2] = {p.scales0 + (int64_t)g * N * (K / 32),
-                           (SWIGLU ? p.scales1 : p.scales0) + (int64_t)g * N * (K / 32)};
-  Q4Stream s;
+  const int64_t rowb = code_row_bytes<F>(K);  // bytes of codes per weight row
+  const char* cm[2] = {static_cast<const char*>(p.codes0) + (int64_t)g * N * rowb,
+                       static_cast<const char*>(SWIGLU ? p.codes1 : p.codes0) + (int64_t)g * N * rowb};
+  const void* sm[2] = {p.scales0, SWIGLU ? p.scales1 : p.scales0};
+  QStream<F> s;
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    s.cb[r] = cm[r] + row0[r] * (K / 8);
-    s.sb[r] = sm[r] + row0[r] * (K / 32);
-  }
+  for (int r = 0; r < 2; ++r) s.cb[r] = cm[r] + row0[r] * rowb;
   s.abase = p.a;
   s.a_bytes = p.a_bytes;
   // column block b of this wave's rows starts 128 rows (down) further on; the descriptors span all
-  s.blk_cb = (uint32_t)(128 * (K / 2));
-  s.blk_sb = (uint32_t)(128 * (K / 16));
-  s.c_bytes = (uint32_t)((CHAIN - 1) * s.blk_cb + 16 * (K / 2));
-  s.s_bytes = (uint32_t)((CHAIN - 1) * s.blk_sb + 16 * (K / 16));
+  s.blk_cb = (uint32_t)(128 * rowb);
+  s.c_bytes = (uint32_t)((CHAIN - 1) * s.blk_cb + 16 * rowb);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = 8 * i + (lane >> 3);  // lane's row in the 16-row set; its slot = chunk position
-    s.c_off[i] = (uint32_t)(row * (K / 2) + (((lane & 7) ^ code_swz(row)) << 4));
+    s.c_off[i] = (uint32_t)(row * rowb + (((lane & 7) ^ code_swz(row)) << 4));
   }
-  s.s_off = (uint32_t)((lane >> 2) * (K / 16) + (lane & 3) * 16);
+  if constexpr (F == QFormat::kInt4) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      s.sb[r] = static_cast<const uint16_t*>(sm[r]) + (int64_t)g * N * (K / 32) + row0[r] * (K / 32);
+    s.blk_sb = (uint32_t)(128 * (K / 16));
+    s.s_bytes = (uint32_t)((CHAIN - 1) * s.blk_sb + 16 * (K / 16));
+    s.s_off = (uint32_t)((lane >> 2) * (K / 16) + (lane & 3) * 16);
+  } else {
+    // the scales of the wave's rows: block row n0/128 (+ b for column block b) of [N/128, K/128],
+    // consecutive in memory, so lane b*ksteps + k reads element (n0/128) * ksteps + lane
+    const int ksteps = K / Fmt<F>::kBlock;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      s.sb[r] = static_cast<const float*>(sm[r]) + ((int64_t)g * (N / 128) + n0 / 128) * ksteps;
+    s.s_bytes = (uint32_t)(CHAIN * ksteps * 4);
+  }
   s.wave_off = wave * kWaveB;
   s.sc_wave_off = wave * kScaleWaveB;
 #if defined(__HIP_DEVICE_COMPILE__)
-  for (int64_t mb = r0; mb < r1; mb += kPassRows) q4_pass<SWIGLU, CHAIN>(p, ring, sc, s, n0, mb, r1);
+  for (int64_t mb = r0; mb < r1; mb += Fmt<F>::kPassRows) q_pass<F, SWIGLU, CHAIN>(p, ring, sc, s, n0, mb, r1);
 #else
   (void)s;
   (void)n0;
@@ -600,7 +727,7 @@ static uint32_t operand_bytes(int64_t rows, int cols) {
 }
 
 // Shared-expert fields of the launch arguments.
-static void set_shared(Q4Args& p, const SharedBf16* sh, bool swiglu, int H, int I) {
+static void set_shared(QArgs& p, const SharedBf16* sh, bool swiglu, int H, int I) {
   p.sh_blocks = 0;
   if (!sh) return;
   p.sh_blocks = swiglu ? I / 64 : H / 128;
@@ -612,27 +739,50 @@ static void set_shared(Q4Args& p, const SharedBf16* sh, bool swiglu, int H, int 
   p.sh_a_bytes = swiglu ? operand_bytes(sh->x_rows, H) : operand_bytes(sh->h_rows, I);
 }
 
-hipError_t launch_gateup_q4_stream(const Groups& g, const QWeights& w, const uint16_t* x16, int64_t x_rows,
-                                   uint16_t* h16, const SharedBf16* sh, int H, int I, hipStream_t s) {
-  Q4Args p{g.group_offsets, g.row_index, g.active, g.counters, g.max_rows, w.gate_codes, w.gate_scales,
-           w.up_codes, w.up_scales, x16, operand_bytes(x_rows, H), h16, 0, nullptr, H, I, I / 64};
+bool qshape_ok(QFormat f, int H, int I) {
+  if (f == QFormat::kInt4) return H > 0 && I > 0 && H % 256 == 0 && I % 256 == 0;
+  constexpr int kMax = Fmt<QFormat::kFp8>::kBlock * Fmt<QFormat::kFp8>::kMaxSteps;
+  return H > 0 && I > 0 && H % 128 == 0 && I % 128 == 0 && H <= kMax && I <= kMax;
+}
+
+hipError_t launch_gateup_q_stream(const Groups& g, const QWeights& w, const uint16_t* x16, int64_t x_rows,
+                                  uint16_t* h16, const SharedBf16* sh, int H, int I, hipStream_t s) {
+  if (!qshape_ok(w.format, H, I)) return hipErrorInvalidValue;
+  QArgs p{g.group_offsets, g.row_index, g.active, g.counters, g.max_rows, w.gate_codes, w.gate_scales,
+          w.up_codes, w.up_scales, x16, operand_bytes(x_rows, H), h16, 0, nullptr, H, I, I / 64};
   set_shared(p, sh, true, H, I);
-  q4_stream_kernel<true, 1><<<(unsigned)(p.sh_blocks + (int64_t)g.n_groups * p.n_wg), 256, 0, s>>>(p);
+  const unsigned grid = (unsigned)(p.sh_blocks + (int64_t)g.n_groups * p.n_wg);
+  if (w.format == QFormat::kInt4)
+    q_stream_kernel<QFormat::kInt4, true, 1><<<grid, 256, 0, s>>>(p);
+  else
+    q_stream_kernel<QFormat::kFp8, true, 1><<<grid, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
-hipError_t launch_down_q4_stream(const Groups& g, const QWeights& w, const uint16_t* h16, uint16_t* y_rows,
-                                 const SharedBf16* sh, int H, int I, hipStream_t s) {
-  // chained column blocks when they divide the columns and the K steps fill whole scale blocks
-  const bool chain = (H / 128) % kDownChain == 0 && (I / kStepK) % kD == 0;
-  Q4Args p{g.group_offsets, nullptr, g.active, g.counters, g.max_rows, w.down_codes, w.down_scales, nullptr,
-           nullptr, h16, operand_bytes(g.max_rows, I), y_rows, 1, nullptr, H, I, H / 128 / (chain ? kDownChain : 1)};
+hipError_t launch_down_q_stream(const Groups& g, const QWeights& w, const uint16_t* h16, uint16_t* y_rows,
+                                const SharedBf16* sh, int H, int I, hipStream_t s) {
+  if (!qshape_ok(w.format, H, I)) return hipErrorInvalidValue;
+  const bool q4 = w.format == QFormat::kInt4;
+  // chained column blocks when they divide the columns and the K steps fill whole 4-bit scale
+  // blocks (FP8: while the chain's scales fit one register)
+  const int ksteps = I / (q4 ? Fmt<QFormat::kInt4>::kStepK : Fmt<QFormat::kFp8>::kStepK);
+  const bool chain = (H / 128) % kDownChain == 0 && ksteps % kD == 0 &&
+                     (q4 || kDownChain * ksteps <= Fmt<QFormat::kFp8>::kMaxSteps);
+  QArgs p{g.group_offsets, nullptr, g.active, g.counters, g.max_rows, w.down_codes, w.down_scales, nullptr,
+          nullptr, h16, operand_bytes(g.max_rows, I), y_rows, 1, nullptr, H, I, H / 128 / (chain ? kDownChain : 1)};
   set_shared(p, sh, false, H, I);
   const unsigned grid = (unsigned)(p.sh_blocks + (int64_t)g.n_groups * p.n_wg);
-  if (chain)
-    q4_stream_kernel<false, kDownChain><<<grid, 256, 0, s>>>(p);
-  else
-    q4_stream_kernel<false, 1><<<grid, 256, 0, s>>>(p);
+  if (q4) {
+    if (chain)
+      q_stream_kernel<QFormat::kInt4, false, kDownChain><<<grid, 256, 0, s>>>(p);
+    else
+      q_stream_kernel<QFormat::kInt4, false, 1><<<grid, 256, 0, s>>>(p);
+  } else {
+    if (chain)
+      q_stream_kernel<QFormat::kFp8, false, kDownChain><<<grid, 256, 0, s>>>(p);
+    else
+      q_stream_kernel<QFormat::kFp8, false, 1><<<grid, 256, 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 

@@ -69,15 +69,20 @@ struct Weights {
   int32_t shared_group = -1;
 };
 
-// 4-bit routed-expert weights (w = q * s, one binary16 scale per 32 consecutive inputs): codes
-// [E, N, K/8] (q of input k in bits 4*(k % 8) of word k/8, two's complement), scales [E, N, K/32].
+// Quantized routed-expert weights, by storage format:
+//   kInt4: w = q * s, one binary16 scale per 32 consecutive inputs: codes [E, N, K/8] uint32 (q of
+//          input k in bits 4*(k % 8) of word k/8, two's complement), scales [E, N, K/32] binary16
+//   kFp8:  w = e4m3(c) * s, one fp32 scale per 128 x 128 block: codes [E, N, K] bytes (OCP E4M3),
+//          scales [E, N/128, K/128] fp32
+enum class QFormat { kInt4, kFp8 };
 struct QWeights {
-  const uint32_t* gate_codes = nullptr;  // [E, I, H/8]
-  const uint16_t* gate_scales = nullptr; // [E, I, H/32]
-  const uint32_t* up_codes = nullptr;
-  const uint16_t* up_scales = nullptr;
-  const uint32_t* down_codes = nullptr;  // [E, H, I/8]
-  const uint16_t* down_scales = nullptr; // [E, H, I/32]
+  QFormat format = QFormat::kInt4;
+  const void* gate_codes = nullptr;   // [E, I, H] inputs per row
+  const void* gate_scales = nullptr;
+  const void* up_codes = nullptr;
+  const void* up_scales = nullptr;
+  const void* down_codes = nullptr;   // [E, H, I] inputs per row
+  const void* down_scales = nullptr;
 };
 
 // ----------------------------------------------------------------------------- launchers
@@ -150,13 +155,16 @@ struct SharedBf16 {
 };
 // y16[r, c] (f16) = x[r, c] with every group of 8 columns in the order 0,4,1,5,2,6,3,7.
 hipError_t launch_f16_rows(const uint16_t* x, uint16_t* y16, int64_t rows, int cols, hipStream_t s);
+// Whether the quantized stream kernels take these sizes (4-bit: H, I multiples of 256; FP8:
+// multiples of 128, at most 8192).
+bool qshape_ok(QFormat f, int H, int I);
 // h16[r, I] (f16, same column order) = SiLU(a Wg^T) * (a Wu^T), a = x16 rows (x_rows of them) through
 // row_index; plus the shared expert's h rows (bf16) when sh is given.
-hipError_t launch_gateup_q4_stream(const Groups& g, const QWeights& w, const uint16_t* x16, int64_t x_rows,
-                                   uint16_t* h16, const SharedBf16* sh, int H, int I, hipStream_t s);
+hipError_t launch_gateup_q_stream(const Groups& g, const QWeights& w, const uint16_t* x16, int64_t x_rows,
+                                  uint16_t* h16, const SharedBf16* sh, int H, int I, hipStream_t s);
 // y_rows[r, H] (bf16) = h16[r] Wd^T, plus the shared expert's rows when sh is given.
-hipError_t launch_down_q4_stream(const Groups& g, const QWeights& w, const uint16_t* h16, uint16_t* y_rows,
-                                 const SharedBf16* sh, int H, int I, hipStream_t s);
+hipError_t launch_down_q_stream(const Groups& g, const QWeights& w, const uint16_t* h16, uint16_t* y_rows,
+                                const SharedBf16* sh, int H, int I, hipStream_t s);
 
 // grouped SwiGLU, fp32 (plain kernels) ---------------------------------------------
 hipError_t launch_gateup_f32(const Groups& g, const Weights& w, const float* x, float* h, int H, int I,

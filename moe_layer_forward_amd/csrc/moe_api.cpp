@@ -277,9 +277,9 @@ int run_after_routing(const moe_config* c, int64_t T, const void* x, const int32
   return ok();
 }
 
-// Workspace of the forward with 4-bit routed experts.  h holds f16 rows for the routed pairs and
+// Workspace of the forward with quantized routed experts.  h holds f16 rows for the routed pairs and
 // bf16 rows for the shared expert's rows after them; y_rows is bf16.
-struct Q4Ws {
+struct QuantWs {
   int32_t* ids;
   float* weights;
   float* router_part;
@@ -293,12 +293,12 @@ struct Q4Ws {
   void* y_rows;
 };
 
-Q4Ws carve_q4(Carver& cv, const moe_config* c, int64_t T) {
+QuantWs carve_quant(Carver& cv, const moe_config* c, int64_t T) {
   const int H = c->hidden_size, I = c->moe_intermediate_size, E = c->n_routed_experts, K = c->top_k;
   const bool shared = c->n_shared_experts == 1;
   const int64_t P = T * K;
   const int64_t rows = P + (shared ? T : 0);
-  Q4Ws w{};
+  QuantWs w{};
   w.ids = cv.take<int32_t>(P);
   w.weights = cv.take<float>(P);
   w.router_part = cv.take<float>((int64_t)moe::router_nsplit(T, H, E, true) * T * E);
@@ -313,10 +313,14 @@ Q4Ws carve_q4(Carver& cv, const moe_config* c, int64_t T) {
   return w;
 }
 
-int check_config_q4(const moe_config* c) {
-  if (c->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "4-bit routed experts need dtype MOE_BF16");
-  if (c->hidden_size % 256 || c->moe_intermediate_size % 256)
-    return fail(MOE_ERR_UNSUPPORTED, "4-bit routed experts need hidden_size and moe_intermediate_size multiples of 256");
+int check_config_quant(const moe_config* c, moe::QFormat f) {
+  const bool q4 = f == moe::QFormat::kInt4;
+  if (c->dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "%s routed experts need dtype MOE_BF16", q4 ? "4-bit" : "FP8");
+  if (!moe::qshape_ok(f, c->hidden_size, c->moe_intermediate_size))
+    return fail(MOE_ERR_UNSUPPORTED,
+                q4 ? "4-bit routed experts need hidden_size and moe_intermediate_size multiples of 256"
+                   : "FP8 routed experts need hidden_size and moe_intermediate_size multiples of 128, at most 8192");
   return MOE_OK;
 }
 
@@ -341,6 +345,91 @@ int check_ws(void* ws, size_t have, size_t need) {
   if (reinterpret_cast<uintptr_t>(ws) % kAlign)
     return fail(MOE_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
   return MOE_OK;
+}
+
+// The layer with quantized routed experts (either format): name prefixes the error messages.
+int forward_quant(const char* name, const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                  const float* score_bias, const float* logit_offset, const moe::QWeights& qw, const void* ws_gate,
+                  const void* ws_up, const void* ws_down, void* y, int32_t* topk_ids_out, float* topk_weights_out,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  prof_reset();
+  int st = check_config(cfg);
+  if (st) return st;
+  if ((st = check_config_quant(cfg, qw.format))) return st;
+  if ((st = check_tokens(T, cfg))) return st;
+  if (T == 0) return ok();
+  if (!x || !w_router || !qw.gate_codes || !qw.gate_scales || !qw.up_codes || !qw.up_scales || !qw.down_codes ||
+      !qw.down_scales || !y)
+    return fail(MOE_ERR_INVALID_ARG, "%s: x, w_router, expert codes and scales and y are required", name);
+  const bool shared = cfg->n_shared_experts == 1;
+  if (shared && (!ws_gate || !ws_up || !ws_down))
+    return fail(MOE_ERR_INVALID_ARG, "%s: shared expert weights are required", name);
+  if ((st = check_forward_spans(cfg, T))) return st;
+  const int H = cfg->hidden_size, I = cfg->moe_intermediate_size, E = cfg->n_routed_experts, K = cfg->top_k;
+  const int64_t P = T * K;
+  Carver cv(workspace);
+  QuantWs w = carve_quant(cv, cfg, T);
+  if ((st = check_ws(workspace, workspace_bytes, cv.used))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* ids = topk_ids_out ? topk_ids_out : w.ids;
+  float* weights = topk_weights_out ? topk_weights_out : w.weights;
+
+  hipError_t e = run_router(cfg, T, x, w_router, w.router_part, s);
+  if (e != hipSuccess) return device_status(e, "router logits");
+  e = timed("topk", s, [&] {
+    return moe::launch_topk(w.router_part, moe::router_nsplit(T, H, E, true), logit_offset, score_bias, T, E, K,
+                            cfg->routed_scaling_factor, ids, weights, s);
+  });
+  if (e != hipSuccess) return device_status(e, "top-k");
+  // routed experts: groups 0..E-1 over rows [0, P); the shared expert (bf16) runs in the same
+  // launches over rows [P, P + T) (row P + t is token t)
+  moe::Groups gr = w.routed;
+  gr.group_offsets = w.offsets;
+  gr.row_index = w.row_token;
+  const bool fused = moe::permute_plan_fused(P, E, gr.n_groups);
+  if (fused) {
+    e = timed("permute_plan", s, [&] {
+      return moe::launch_permute_plan(ids, T, K, E, w.offsets, w.row_token, w.pair_row, shared, gr,
+                                      static_cast<const uint16_t*>(x), w.x16, H, s);
+    });
+    if (e != hipSuccess) return device_status(e, "permute");
+  } else {
+    e = timed("permute", s, [&] {
+      return moe::launch_permute(ids, T, K, E, w.offsets, w.row_token, w.pair_row, w.perm_scratch, shared, s);
+    });
+    if (e != hipSuccess) return device_status(e, "permute");
+    e = timed("f16_rows", s, [&] {
+      return moe::launch_f16_rows(static_cast<const uint16_t*>(x), w.x16, T, H, s);
+    });
+    if (e != hipSuccess) return device_status(e, "f16 rows");
+  }
+  moe::SharedBf16 sh;
+  sh.offsets = w.offsets + E;
+  sh.row_index = w.row_token;
+  sh.gate = static_cast<const uint16_t*>(ws_gate);
+  sh.up = static_cast<const uint16_t*>(ws_up);
+  sh.down = static_cast<const uint16_t*>(ws_down);
+  sh.x = static_cast<const uint16_t*>(x);
+  sh.x_rows = T;
+  sh.h = w.h;
+  sh.h_rows = P + T;
+  const moe::SharedBf16* shp = shared ? &sh : nullptr;
+  uint16_t* y_rows = static_cast<uint16_t*>(w.y_rows);
+  if (!fused) e = timed("plan", s, [&] { return moe::launch_plan(gr, s); });
+  const bool q4 = qw.format == moe::QFormat::kInt4;
+  if (e == hipSuccess)
+    e = timed(q4 ? "gateup_q4" : "gateup_fp8", s,
+              [&] { return moe::launch_gateup_q_stream(gr, qw, w.x16, T, w.h, shp, H, I, s); });
+  if (e == hipSuccess)
+    e = timed(q4 ? "down_q4" : "down_fp8", s,
+              [&] { return moe::launch_down_q_stream(gr, qw, w.h, y_rows, shp, H, I, s); });
+  if (e != hipSuccess) return device_status(e, "experts");
+
+  e = timed("combine", s, [&] {
+    return moe::launch_combine(y_rows, true, w.pair_row, weights, shared ? y_rows + P * H : nullptr, y, true, T, K,
+                               H, s);
+  });
+  return device_status(e, "combine");
 }
 
 }  // namespace
@@ -380,8 +469,11 @@ size_t moe_workspace_size(const moe_config* cfg, int32_t op, int64_t rows, int32
       carve_forward(cv, cfg, rows, false);
       break;
     case MOE_OP_FORWARD_Q4:
-      if (check_config_q4(cfg) != MOE_OK || check_tokens(rows, cfg) != MOE_OK) return 0;
-      carve_q4(cv, cfg, rows);
+    case MOE_OP_FORWARD_FP8:
+      if (check_config_quant(cfg, op == MOE_OP_FORWARD_Q4 ? moe::QFormat::kInt4 : moe::QFormat::kFp8) != MOE_OK ||
+          check_tokens(rows, cfg) != MOE_OK)
+        return 0;
+      carve_quant(cv, cfg, rows);
       break;
     default:
       fail(MOE_ERR_INVALID_ARG, "unknown op %d", op);
@@ -565,81 +657,20 @@ int moe_forward_q4(const moe_config* cfg, int64_t T, const void* x, const void* 
                    const uint16_t* down_scales, const void* ws_gate, const void* ws_up, const void* ws_down, void* y,
                    int32_t* topk_ids_out, float* topk_weights_out, void* workspace, size_t workspace_bytes,
                    void* stream) {
-  prof_reset();
-  int st = check_config(cfg);
-  if (st) return st;
-  if ((st = check_config_q4(cfg))) return st;
-  if ((st = check_tokens(T, cfg))) return st;
-  if (T == 0) return ok();
-  if (!x || !w_router || !gate_codes || !gate_scales || !up_codes || !up_scales || !down_codes || !down_scales || !y)
-    return fail(MOE_ERR_INVALID_ARG, "moe_forward_q4: x, w_router, expert codes and scales and y are required");
-  const bool shared = cfg->n_shared_experts == 1;
-  if (shared && (!ws_gate || !ws_up || !ws_down))
-    return fail(MOE_ERR_INVALID_ARG, "moe_forward_q4: shared expert weights are required");
-  if ((st = check_forward_spans(cfg, T))) return st;
-  const int H = cfg->hidden_size, I = cfg->moe_intermediate_size, E = cfg->n_routed_experts, K = cfg->top_k;
-  const int64_t P = T * K;
-  Carver cv(workspace);
-  Q4Ws w = carve_q4(cv, cfg, T);
-  if ((st = check_ws(workspace, workspace_bytes, cv.used))) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  int32_t* ids = topk_ids_out ? topk_ids_out : w.ids;
-  float* weights = topk_weights_out ? topk_weights_out : w.weights;
+  const moe::QWeights qw{moe::QFormat::kInt4, gate_codes, gate_scales, up_codes, up_scales, down_codes, down_scales};
+  return forward_quant("moe_forward_q4", cfg, T, x, w_router, score_bias, logit_offset, qw, ws_gate, ws_up, ws_down,
+                       y, topk_ids_out, topk_weights_out, workspace, workspace_bytes, stream);
+}
 
-  hipError_t e = run_router(cfg, T, x, w_router, w.router_part, s);
-  if (e != hipSuccess) return device_status(e, "router logits");
-  e = timed("topk", s, [&] {
-    return moe::launch_topk(w.router_part, moe::router_nsplit(T, H, E, true), logit_offset, score_bias, T, E, K,
-                            cfg->routed_scaling_factor, ids, weights, s);
-  });
-  if (e != hipSuccess) return device_status(e, "top-k");
-  // routed experts: groups 0..E-1 over rows [0, P); the shared expert (bf16) runs in the same
-  // launches over rows [P, P + T) (row P + t is token t)
-  moe::Groups gr = w.routed;
-  gr.group_offsets = w.offsets;
-  gr.row_index = w.row_token;
-  const bool fused = moe::permute_plan_fused(P, E, gr.n_groups);
-  if (fused) {
-    e = timed("permute_plan", s, [&] {
-      return moe::launch_permute_plan(ids, T, K, E, w.offsets, w.row_token, w.pair_row, shared, gr,
-                                      static_cast<const uint16_t*>(x), w.x16, H, s);
-    });
-    if (e != hipSuccess) return device_status(e, "permute");
-  } else {
-    e = timed("permute", s, [&] {
-      return moe::launch_permute(ids, T, K, E, w.offsets, w.row_token, w.pair_row, w.perm_scratch, shared, s);
-    });
-    if (e != hipSuccess) return device_status(e, "permute");
-    e = timed("f16_rows", s, [&] {
-      return moe::launch_f16_rows(static_cast<const uint16_t*>(x), w.x16, T, H, s);
-    });
-    if (e != hipSuccess) return device_status(e, "f16 rows");
-  }
-  moe::QWeights qw{gate_codes, gate_scales, up_codes, up_scales, down_codes, down_scales};
-  moe::SharedBf16 sh;
-  sh.offsets = w.offsets + E;
-  sh.row_index = w.row_token;
-  sh.gate = static_cast<const uint16_t*>(ws_gate);
-  sh.up = static_cast<const uint16_t*>(ws_up);
-  sh.down = static_cast<const uint16_t*>(ws_down);
-  sh.x = static_cast<const uint16_t*>(x);
-  sh.x_rows = T;
-  sh.h = w.h;
-  sh.h_rows = P + T;
-  const moe::SharedBf16* shp = shared ? &sh : nullptr;
-  uint16_t* y_rows = static_cast<uint16_t*>(w.y_rows);
-  if (!fused) e = timed("plan", s, [&] { return moe::launch_plan(gr, s); });
-  if (e == hipSuccess)
-    e = timed("gateup_q4", s, [&] { return moe::launch_gateup_q4_stream(gr, qw, w.x16, T, w.h, shp, H, I, s); });
-  if (e == hipSuccess)
-    e = timed("down_q4", s, [&] { return moe::launch_down_q4_stream(gr, qw, w.h, y_rows, shp, H, I, s); });
-  if (e != hipSuccess) return device_status(e, "experts");
-
-  e = timed("combine", s, [&] {
-    return moe::launch_combine(y_rows, true, w.pair_row, weights, shared ? y_rows + P * H : nullptr, y, true, T, K,
-                               H, s);
-  });
-  return device_status(e, "combine");
+int moe_forward_fp8(const moe_config* cfg, int64_t T, const void* x, const void* w_router, const float* score_bias,
+                    const float* logit_offset, const uint8_t* gate_codes, const float* gate_scales,
+                    const uint8_t* up_codes, const float* up_scales, const uint8_t* down_codes,
+                    const float* down_scales, const void* ws_gate, const void* ws_up, const void* ws_down, void* y,
+                    int32_t* topk_ids_out, float* topk_weights_out, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  const moe::QWeights qw{moe::QFormat::kFp8, gate_codes, gate_scales, up_codes, up_scales, down_codes, down_scales};
+  return forward_quant("moe_forward_fp8", cfg, T, x, w_router, score_bias, logit_offset, qw, ws_gate, ws_up, ws_down,
+                       y, topk_ids_out, topk_weights_out, workspace, workspace_bytes, stream);
 }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }

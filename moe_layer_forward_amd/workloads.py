@@ -14,6 +14,8 @@ dense_*     64 /   7168 18432    1   1  bf16    none: the dense SwiGLU FFN of th
             8192                                 model's first layer, all tokens
 decode_int4    64  7168  2048  384   8  bf16    as decode; routed experts stored as
                                                  4-bit codes + binary16 scales
+decode_fp8     64  7168  2048  384   8  bf16    as decode; routed experts stored as
+                                                 E4M3 codes + fp32 128x128-block scales
 ==========  =====  ====  ====  ===  ==  ======  ==================================
 
 
@@ -32,6 +34,8 @@ decode_int4 has decode's tokens and weights; its routed experts are those bf16
 weights quantized per group of 32 inputs (s = f16(max|w| / 7), q = clamp(rint(w / s),
 -8, 7)) -- the checkpoint-conversion step, done on the device for the GPU and on
 the host for the oracle by two implementations of the same rule (``synth``).
+decode_fp8 likewise quantizes them per 128 x 128 block (s = max|w| / 448, c = E4M3
+round-to-nearest-even of w / s).
 
 Synthetic streams: 0 activations, 1 router, 2 gate, 3 up, 4 down, 5/6/7 shared
 gate/up/down, 11/12/13 dense gate/up/down (Philox, index = expert id); 8 skew
@@ -78,7 +82,7 @@ class Workload:
     rsf: float = RSF_K2
     sigma_x: float = 1.0
     sigma_router: float = 0.02
-    quant: str = "none"           # 'none' | 'int4' (routed experts stored as 4-bit codes + scales)
+    quant: str = "none"           # 'none' | 'int4' | 'fp8' (routed experts stored as codes + scales)
     extra: dict = field(default_factory=dict, compare=False)
 
     @property
@@ -109,6 +113,7 @@ WORKLOADS = {
     "dense_prefill": Workload("dense_prefill", 8192, 7168, DENSE_I, 1, 1, "bf16", x_seed=7, w_seed=100,
                               routing="dense", n_shared=0),
     "decode_int4": Workload("decode_int4", 64, 7168, 2048, 384, 8, "bf16", x_seed=2, w_seed=100, quant="int4"),
+    "decode_fp8": Workload("decode_fp8", 64, 7168, 2048, 384, 8, "bf16", x_seed=2, w_seed=100, quant="fp8"),
 }
 
 
@@ -179,6 +184,17 @@ def host_expert_q4(w: Workload, e: int):
     return tuple(out)
 
 
+def host_expert_fp8(w: Workload, e: int):
+    """8-bit storage of routed expert e: ((codes, scales) of W_gate, W_up, W_down), quantized on the host
+    from the expert's bf16 weights (``synth.host_quantize_fp8``)."""
+    sg, su, sd = _expert_streams(w)
+    out = []
+    for stream, shape, sigma in ((sg, (w.I, w.H), w.sigma_gate_up), (su, (w.I, w.H), w.sigma_gate_up),
+                                 (sd, (w.H, w.I), w.sigma_down)):
+        out.append(synth.host_quantize_fp8(synth.host_tensor(w.w_seed, stream, e, shape, sigma, "bf16")))
+    return tuple(out)
+
+
 def host_shared(w: Workload):
     if w.n_shared == 0:
         return None
@@ -193,7 +209,8 @@ def device_weights(w: Workload, device="cuda"):
     """Router, routed-expert and shared-expert weights of the workload (the dense FFN as expert 0 for
     'dense'), generated in HBM.  For quant 'int4' the routed experts come as gate/up/down codes
     (int32 words) and scales (int16 words holding binary16), quantized on the device
-    (``synth.device_quantize_q4``) from the same bf16 weights, a chunk of experts at a time."""
+    (``synth.device_quantize_q4``) from the same bf16 weights, a chunk of experts at a time; for
+    'fp8' as uint8 E4M3 codes and float32 block scales (``synth.device_quantize_fp8``)."""
     import torch
 
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -216,6 +233,20 @@ def device_weights(w: Workload, device="cuda"):
                 m = min(chunk, w.E - e0)
                 synth.device_fill(buf[:m], w.w_seed, stream, e0, m, n * k, sigma)
                 synth.device_quantize_q4(buf[:m], codes[e0:e0 + m], scales[e0:e0 + m])
+            t[f"{name}_codes"], t[f"{name}_scales"] = codes, scales
+            del buf
+    elif w.quant == "fp8":
+        if w.dtype != "bf16":
+            raise ValueError("FP8 experts are quantized from bf16 weights")
+        chunk = min(w.E, 32)
+        for name, stream, (n, k), sigma in mats:
+            codes = torch.empty((w.E, n, k), dtype=torch.uint8, device=device)
+            scales = torch.empty((w.E, n // 128, k // 128), dtype=torch.float32, device=device)
+            buf = torch.empty((chunk, n, k), dtype=torch.bfloat16, device=device)
+            for e0 in range(0, w.E, chunk):
+                m = min(chunk, w.E - e0)
+                synth.device_fill(buf[:m], w.w_seed, stream, e0, m, n * k, sigma)
+                synth.device_quantize_fp8(buf[:m], codes[e0:e0 + m], scales[e0:e0 + m])
             t[f"{name}_codes"], t[f"{name}_scales"] = codes, scales
             del buf
     else:

@@ -58,10 +58,13 @@ def rel_l2(y, y_ref):
 
 
 def oracle_expert(w):
-    """Expert weights (float64) as the oracle sees them: the bf16 weights, or for 4-bit workloads
-    the dequantized codes and scales (host quantizer, then ``oracle.dequant_q4``)."""
+    """Expert weights (float64) as the oracle sees them: the bf16 weights, or for 4-bit and FP8
+    workloads the dequantized codes and scales (host quantizer, then ``oracle.dequant_q4`` or
+    ``oracle.dequant_fp8``)."""
     if w.quant == "int4":
         return lambda e: tuple(oracle.dequant_q4(c, s) for c, s in wl.host_expert_q4(w, e))
+    if w.quant == "fp8":
+        return lambda e: tuple(oracle.dequant_fp8(c, s) for c, s in wl.host_expert_fp8(w, e))
     return lambda e: wl.host_expert(w, e)
 
 

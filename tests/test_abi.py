@@ -137,6 +137,32 @@ def test_q4_forward_argument_checks():
         assert lib.moe_workspace_size(ctypes.byref(bad), moe.MOE_OP_FORWARD_Q4, 64, 0) == 0
 
 
+def test_fp8_forward_argument_checks():
+    # the FP8 forward checks its config, pointers and workspace before launching anything
+    lib = moe.load_library()
+    fake = ctypes.c_void_p(0x1000)
+
+    def call(cfg, T=64, x=fake, codes=fake, scales=fake, shared=fake, ws=1 << 40):
+        return lib.moe_forward_fp8(ctypes.byref(cfg), T, x, fake, None, None, codes, scales, fake, fake, fake, fake,
+                                   shared, fake, fake, fake, None, None, fake, ws, None)
+
+    cfg = moe.make_config()
+    need = moe.moe_workspace_size(cfg, moe.MOE_OP_FORWARD_FP8, 64)
+    assert need == moe.moe_workspace_size(cfg, moe.MOE_OP_FORWARD_Q4, 64)  # the same buffers
+    assert call(cfg, x=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(cfg, codes=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(cfg, scales=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(cfg, shared=None) == moe.MOE_ERR_INVALID_ARG and "shared" in moe.moe_last_error()
+    assert call(cfg, ws=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(cfg, T=0, x=None, codes=None, shared=None, ws=0) == moe.MOE_OK
+    # multiples of 128 up to 8192 (7296 is not a multiple of 256, so the 4-bit path refuses it)
+    assert moe.moe_workspace_size(moe.make_config(hidden_size=7296), moe.MOE_OP_FORWARD_FP8, 64, 0) > 0
+    for bad in (moe.make_config(hidden_size=7168 + 64), moe.make_config(hidden_size=8192 + 128),
+                moe.make_config(moe_intermediate_size=8192 + 128), moe.make_config(dtype="f32")):
+        assert call(bad) == moe.MOE_ERR_UNSUPPORTED
+        assert lib.moe_workspace_size(ctypes.byref(bad), moe.MOE_OP_FORWARD_FP8, 64, 0) == 0
+
+
 def test_zero_tokens_is_a_no_op():
     cfg = moe.make_config()
     lib = moe.load_library()
