@@ -440,7 +440,9 @@ def profile_summary(d):
     print("| kernel | calls | average µs | min µs | max µs | total ms | % of GPU time |")
     print("|---|---|---|---|---|---|---|")
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        name = r["Name"].replace("(anonymous namespace)::", "").split("(")[0]
+        name = r["Name"].replace("(anonymous namespace)::", "")
+        if name.endswith(")"):  # drop the parameter list, keep template arguments such as (moe::QFormat)1
+            name = name[:name.rfind("(")]
         print(f"| `{name[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
               f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |")
 
