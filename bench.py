@@ -390,19 +390,14 @@ def run(w, weights, steps, warmup, graph=True):
             "kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()}}
 
 
-def cpu_baseline(w, n_tokens):
-    """The oracle as it stands, on the first n_tokens tokens of the workload, on the host cores.
-    Only the oracle's own arithmetic is timed (weight regeneration excluded)."""
+def _time_oracle(w, n_tokens):
+    """Seconds of the oracle's own arithmetic on the first n_tokens tokens of the workload, and the
+    seconds spent regenerating expert weights beside it (not counted)."""
     import numpy as np
 
     import oracle
     from moe_layer_forward_amd import workloads as wl
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
     tokens = np.arange(n_tokens)
     x = wl.host_x_rows(w, tokens)
     router = wl.host_router(w)
@@ -417,11 +412,29 @@ def cpu_baseline(w, n_tokens):
     shared = wl.host_shared(w)
     t0 = time.perf_counter()
     oracle.moe_forward(x, router, expert, shared, w.K, w.rsf, logit_offset=wl.logit_offsets(w))
-    el = time.perf_counter() - t0 - gen[0]
-    return {"value": n_tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n_tokens} tokens of the {w.name} workload (T={w.T}), all {w.K}+{w.n_shared} experts "
-                      f"each, float64 numpy; {el:.2f} s of oracle arithmetic timed, plus {gen[0]:.1f} s of "
-                      f"input (expert weight) regeneration not timed"}
+    return time.perf_counter() - t0 - gen[0], gen[0]
+
+
+def cpu_baseline(w, n_tokens, n_tokens_1t=4):
+    """The oracle as it stands, on the first n_tokens tokens of the workload, on the host cores (and
+    on the first n_tokens_1t tokens with one BLAS thread).  Only the oracle's own arithmetic is timed
+    (weight regeneration excluded)."""
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threadpool_limits, threads = None, 1
+    el, gen = _time_oracle(w, n_tokens)
+    out = {"value": n_tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"first {n_tokens} tokens of the {w.name} workload (T={w.T}), all {w.K}+{w.n_shared} experts "
+                     f"each, float64 numpy; {el:.2f} s of oracle arithmetic timed, plus {gen:.1f} s of "
+                     f"input (expert weight) regeneration not timed"}
+    if threadpool_limits is not None and n_tokens_1t > 0:
+        with threadpool_limits(limits=1, user_api="blas"):
+            el1, _ = _time_oracle(w, n_tokens_1t)
+        out["one_thread"] = {"value": n_tokens_1t / el1, "unit": "tokens/s", "cores": 1,
+                             "sample": f"first {n_tokens_1t} tokens, one BLAS thread; {el1:.2f} s timed"}
+    return out
 
 
 def _csv_rows(d, suffix):

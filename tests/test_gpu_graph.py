@@ -1,4 +1,4 @@
-"""The layer call inside a captured HIP graph (torch.cuda.CUDAGraph).
+"""The layer call inside a captured HIP graph (torch.cuda.CUDAGraph), bf16 and quantized experts.
 
 The library launches only kernels on the caller's stream (no allocation, copy, memset or
 synchronisation inside a call), so a serving loop can capture `moe_forward` once and replay it.
@@ -69,5 +69,53 @@ def test_forward_graph_replays_match_eager(T):
         assert torch.equal(ids, ids_ref), f"replay {rep}: routing differs"
         assert torch.equal(wts, w_ref), f"replay {rep}: routing weights differ"
         assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), f"replay {rep}: output differs"
+        assert torch.isfinite(scratch)
+    del g
+
+
+@pytest.mark.parametrize("quant", ["int4", "fp8"])
+def test_quantized_forward_graph_replays_match_eager(quant):
+    torch = _torch()
+    T = 24
+    w = wl.custom(f"graph_{quant}", T=T, H=512, I=256, E=40, K=4, x_seed=43, w_seed=44, quant=quant)
+    t = wl.device_inputs(w)
+    cfg = moe.config_for(w)
+    fwd, op = ((moe.moe_forward_q4, moe.MOE_OP_FORWARD_Q4) if quant == "int4"
+               else (moe.moe_forward_fp8, moe.MOE_OP_FORWARD_FP8))
+    ws = moe.alloc_workspace(cfg, op, T)
+    y = torch.empty((T, w.H), dtype=torch.bfloat16, device="cuda")
+    q = {k: t[k] for k in moe.QUANT_KEYS}
+
+    def call():
+        fwd(cfg, t["x"], t["w_router"], q, t["ws_gate"], t["ws_up"], t["ws_down"], workspace=ws, out=y)
+
+    x0 = t["x"].clone()
+    x1 = torch.flip(x0, dims=[0]).contiguous()
+    refs = []
+    for xin in (x0, x1):
+        t["x"].copy_(xin)
+        call()
+        torch.cuda.synchronize()
+        refs.append(y.clone())
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+
+    for rep in range(4):
+        which = rep % 2
+        t["x"].copy_(x1 if which else x0)
+        y.zero_()
+        g.replay()
+        scratch = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), refs[which].view(torch.int16)), f"replay {rep}: output differs"
         assert torch.isfinite(scratch)
     del g
