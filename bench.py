@@ -17,6 +17,9 @@ under profiles/):
     rocprofv3 --pmc FETCH_SIZE -d FDIR -o run --output-format csv -- python bench.py --pmc-calibrate ...
     rocprofv3 --pmc WRITE_SIZE -d WDIR -o run --output-format csv -- python bench.py --pmc-calibrate ...
     python bench.py --traffic-summary WORKLOAD FDIR WDIR   # HBM bytes per dispatch, copy-calibrated
+    rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 \
+              SQ_INSTS_VALU_MFMA_MOPS_F16 -d DIR -o run --output-format csv -- python bench.py ...
+    python bench.py --mfma-summary WORKLOAD DIR            # matrix-core busy % per dispatch
 """
 import argparse
 import csv
@@ -500,11 +503,54 @@ def traffic_summary(workload, fdir, wdir):
     print("\n```json\n" + json.dumps(recs, indent=1) + "\n```")
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F16")
+SIMDS = 256 * 4            # MI355X: 256 CUs x 4 SIMDs
+XCDS = 8                   # GRBM_GUI_ACTIVE has one instance per XCD, all counting the same cycles
+
+
+def mfma_summary(workload, d):
+    """Matrix-core busy time of the library's kernels from one rocprofv3 --pmc pass over
+    MFMA_COUNTERS.  busy % = SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) / (GPU cycles x SIMDs), the
+    expression of rocprofv3's MfmaUtil metric, whose GPU cycles are the largest GRBM_GUI_ACTIVE
+    instance; the CSV holds the sum over the XCDs' instances, hence / XCDS.  The cycles per µs give
+    the clock the kernel ran at.  MFMA work from the MOPS counters (one count per 512 FLOP)."""
+    per = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if r["Counter_Name"] not in MFMA_COUNTERS:
+            continue
+        rec = per.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"],
+                                                "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        rec[r["Counter_Name"]] = float(r["Counter_Value"])
+    print("| kernel | dispatches | µs | clock MHz | MFMA busy % of cycles | MFMA TFLOP / dispatch | TFLOP/s | "
+          "% of 2.5 PFLOP/s |")
+    print("|---|---|---|---|---|---|---|---|")
+    recs = []
+    for name, (sym, _) in KERNEL_SYMBOLS.items():
+        hits = [v for v in per.values() if sym in v["name"] and all(c in v for c in MFMA_COUNTERS)]
+        if not hits:
+            continue
+        n = len(hits)
+        mean = {c: sum(h[c] for h in hits) / n for c in MFMA_COUNTERS}
+        us = sum(h["ns"] for h in hits) / n / 1e3
+        cycles = mean["GRBM_GUI_ACTIVE"] / XCDS
+        busy = 100 * mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * SIMDS)
+        tflop = (mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] + mean["SQ_INSTS_VALU_MFMA_MOPS_F16"]) * 512 / 1e12
+        rate = tflop / (us * 1e-6)
+        print(f"| {name} | {n} | {us:.1f} | {cycles / us:.0f} | {busy:.1f} | {tflop:.4g} | {rate:.0f} | "
+              f"{100 * rate * 1e12 / BF16_PEAK:.1f} |")
+        recs.append({"workload": workload, "kernel": name, "dispatches": n, "us": us, "clock_mhz": cycles / us,
+                     "mfma_busy_pct": busy, "mfma_tflop": tflop, **{c: mean[c] for c in MFMA_COUNTERS}})
+    print("\n```json\n" + json.dumps(recs, indent=1) + "\n```")
+
+
 def main():
     if len(sys.argv) >= 2 and sys.argv[1] == "--profile-summary":
         return profile_summary(sys.argv[2])
     if len(sys.argv) >= 2 and sys.argv[1] == "--traffic-summary":
         return traffic_summary(*sys.argv[2:5])
+    if len(sys.argv) >= 2 and sys.argv[1] == "--mfma-summary":
+        return mfma_summary(*sys.argv[2:4])
     from moe_layer_forward_amd import workloads as wl
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
