@@ -40,6 +40,7 @@ struct StreamArgs {
   int out_bf16;
   const float* row_scale;
   int H, I, n_nblk;
+  int small_only;  // only the groups active[counters[2] ..) (the tile kernels take the others)
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(256) void stream_kernel(StreamArgs p) {
     (void)s3;
   }
 
-  const int slot = blockIdx.x / p.n_nblk, nb = blockIdx.x % p.n_nblk;
+  const int slot = (p.small_only ? p.counters[2] : 0) + (int)blockIdx.x / p.n_nblk, nb = blockIdx.x % p.n_nblk;
   if (slot >= p.counters[0]) return;
   const int g = p.active[slot];
   int64_t r0 = p.group_offsets[g], r1 = p.group_offsets[g + 1];
@@ -299,17 +300,18 @@ constexpr int kDepthDown = 2;
 }  // namespace
 
 hipError_t launch_gateup_stream_bf16(const Groups& g, const Weights& w, const uint16_t* x, uint16_t* h, int H, int I,
-                                     hipStream_t s) {
-  StreamArgs p{g.group_offsets, g.row_index, g.active, g.counters, g.max_rows, w, x, h, 1, nullptr, H, I, I / 64};
+                                     bool small_only, hipStream_t s) {
+  StreamArgs p{g.group_offsets, g.row_index, g.active, g.counters, g.max_rows, w, x, h, 1, nullptr, H, I, I / 64,
+               small_only ? 1 : 0};
   const int64_t blocks = (int64_t)g.n_groups * p.n_nblk;
   stream_kernel<true, kDepthGateUp><<<(unsigned)blocks, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
 hipError_t launch_down_stream_bf16(const Groups& g, const Weights& w, const uint16_t* h, void* y_rows, bool y_bf16,
-                                   const float* row_scale, int H, int I, hipStream_t s) {
+                                   const float* row_scale, int H, int I, bool small_only, hipStream_t s) {
   StreamArgs p{g.group_offsets, nullptr, g.active, g.counters, g.max_rows, w, h, y_rows, y_bf16 ? 1 : 0, row_scale,
-               H, I, H / 128};
+               H, I, H / 128, small_only ? 1 : 0};
   const int64_t blocks = (int64_t)g.n_groups * p.n_nblk;
   stream_kernel<false, kDepthDown><<<(unsigned)blocks, 256, 0, s>>>(p);
   return hipGetLastError();

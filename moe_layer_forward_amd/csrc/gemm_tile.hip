@@ -485,18 +485,36 @@ unsigned grid_for(int64_t max_tiles, int n_ntiles, int n_ksplit = 1) {
   return (unsigned)n;
 }
 
+// Whether row r belongs to a group of the tile list, i.e. of more than stream_rows rows counted as
+// the plan counts them (clamped to max_rows); the smaller groups' rows come from the weight-stream
+// kernels, and rows before offsets[0] belong to no group.  Binary search over offsets[0 .. G].
+__device__ __forceinline__ bool row_in_tile_list(const int32_t* __restrict__ offsets, int G, int64_t max_rows,
+                                                 int stream_rows, int64_t r) {
+  if (r < offsets[0]) return false;
+  if (stream_rows == 0) return true;
+  int lo = 0, hi = G;  // offsets[lo] <= r < offsets[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (offsets[mid] <= r) lo = mid; else hi = mid;
+  }
+  const int64_t a = offsets[lo] < max_rows ? offsets[lo] : max_rows;
+  const int64_t b = offsets[lo + 1] < max_rows ? offsets[lo + 1] : max_rows;
+  return b - a > stream_rows;
+}
+
 // y[r, :] = sum over the K ranges of part[ks, r, :] (in ks order), rows [0, offsets[G]) clamped to
-// max_rows; 8 columns per thread.
+// max_rows that belong to groups of the tile list; 8 columns per thread.
 __global__ __launch_bounds__(256) void ksplit_reduce_kernel(const float* __restrict__ part, int n_ksplit,
                                                             const int32_t* __restrict__ offsets, int G,
-                                                            int64_t max_rows, int H, void* __restrict__ out,
-                                                            int out_bf16) {
+                                                            int64_t max_rows, int stream_rows, int H,
+                                                            void* __restrict__ out, int out_bf16) {
   int64_t rows = offsets[G];
   if (rows > max_rows) rows = max_rows;
   const int64_t n = rows * (H / 8);
   const int64_t plane = max_rows * H;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t e = 8 * i;  // row e / H, columns e % H .. +7
+    if (!row_in_tile_list(offsets, G, max_rows, stream_rows, e / H)) continue;
     f32x4 lo = *reinterpret_cast<const f32x4*>(part + e), hi = *reinterpret_cast<const f32x4*>(part + e + 4);
     for (int ks = 1; ks < n_ksplit; ++ks) {
       lo += *reinterpret_cast<const f32x4*>(part + ks * plane + e);
@@ -572,8 +590,8 @@ hipError_t launch_down_tile_bf16(const Groups& g, const Weights& w, const uint16
   const int64_t n = g.max_rows * (H / 8);
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  ksplit_reduce_kernel<<<(unsigned)blocks, 256, 0, s>>>(part, split, g.group_offsets, g.n_groups, g.max_rows, H,
-                                                        y_rows, y_bf16 ? 1 : 0);
+  ksplit_reduce_kernel<<<(unsigned)blocks, 256, 0, s>>>(part, split, g.group_offsets, g.n_groups, g.max_rows,
+                                                        g.stream_rows, H, y_rows, y_bf16 ? 1 : 0);
   return hipGetLastError();
 }
 

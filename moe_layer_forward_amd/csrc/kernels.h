@@ -51,11 +51,19 @@ struct Groups {
   const int32_t* row_index = nullptr;      // [max_rows] device or null
   // Plan (workspace), written by launch_plan.
   int32_t* active = nullptr;               // [G] ids of groups with rows
-  int32_t* counters = nullptr;             // [0] n_active, [1] n_tiles
+  int32_t* counters = nullptr;             // [0] n_active, [1] n_tiles, [2] n_large
   int32_t* tiles = nullptr;                // [2 * max_tiles] (group, first row in group)
   int32_t max_tiles = 0;
   int32_t tile_m = 0;                      // rows per tile in the tile list
+  int32_t stream_rows = 0;                 // 0, or kStreamRows: groups of at most this many rows stay
+                                           // out of the tile list (see below)
 };
+// With many groups, groups of at most kStreamRows rows (one pass of the weight-stream kernels) stay
+// out of the tile list and go to the stream kernels: active[0 .. n_large) are the larger groups,
+// active[n_large .. n_active) the small ones.  Calls with fewer than kStreamMinGroups groups keep
+// every group in the tile list (two more launches would cost more than the few small groups gain).
+constexpr int kStreamRows = 32;
+constexpr int kStreamMinGroups = 16;
 
 // Expert weights by group: group g < shared_group uses the stacked tensors at index g; the group
 // equal to shared_group uses the s_* tensors.
@@ -123,14 +131,17 @@ hipError_t launch_gather_rows(const void* x, const int32_t* row_token, void* x_p
 hipError_t launch_plan(const Groups& g, hipStream_t s);
 
 // grouped SwiGLU, bf16 ------------------------------------------------------------
-// h[r, I] (bf16) = SiLU(a Wg^T) * (a Wu^T) for every row of every active group.
+// h[r, I] (bf16) = SiLU(a Wg^T) * (a Wu^T) for every row of every active group (the stream kernels:
+// of the small groups only, active[n_large ..), when small_only; the tile kernels: of the groups in
+// the tile list).
 hipError_t launch_gateup_stream_bf16(const Groups& g, const Weights& w, const uint16_t* x, uint16_t* h, int H,
-                                     int I, hipStream_t s);
+                                     int I, bool small_only, hipStream_t s);
 hipError_t launch_gateup_tile_bf16(const Groups& g, const Weights& w, const uint16_t* x, uint16_t* h, int H,
                                    int I, hipStream_t s);
 // y_rows[r, H] = row_scale[r] * h[r] Wd^T   (y fp32 when y_bf16 == false)
 hipError_t launch_down_stream_bf16(const Groups& g, const Weights& w, const uint16_t* h, void* y_rows,
-                                   bool y_bf16, const float* row_scale, int H, int I, hipStream_t s);
+                                   bool y_bf16, const float* row_scale, int H, int I, bool small_only,
+                                   hipStream_t s);
 // With few row tiles the K dimension is split (down_tile_ksplit ranges, partial sums in part,
 // [split, max_rows, H] fp32, then a reduction into y_rows).
 hipError_t launch_down_tile_bf16(const Groups& g, const Weights& w, const uint16_t* h, void* y_rows,

@@ -152,9 +152,10 @@ moe::Groups carve_plan(Carver& cv, int G, int64_t max_rows) {
   g.n_groups = G;
   g.max_rows = max_rows;
   g.tile_m = moe::kTileM;
+  g.stream_rows = G >= moe::kStreamMinGroups ? moe::kStreamRows : 0;
   g.max_tiles = (int32_t)((max_rows + moe::kTileM - 1) / moe::kTileM + G);
   g.active = cv.take<int32_t>(G);
-  g.counters = cv.take<int32_t>(2);
+  g.counters = cv.take<int32_t>(3);
   g.tiles = cv.take<int32_t>(2LL * g.max_tiles);
   return g;
 }
@@ -187,19 +188,33 @@ hipError_t run_swiglu(const moe_config* c, const moe::Groups& g, const moe::Weig
       return moe::launch_down_f32(g, w, static_cast<const float*>(h), static_cast<float*>(y_rows), row_scale, H, I, s);
     });
   }
-  if (use_stream_kernels(g.max_rows, g.n_groups)) {
+  // decode-like: every group on the weight-stream kernels; otherwise the groups in the tile list on
+  // the tile kernels and, when the plan leaves the small ones out of it, those on the stream kernels
+  const bool all_stream = use_stream_kernels(g.max_rows, g.n_groups);
+  const bool small_stream = !all_stream && g.stream_rows > 0;
+  if (all_stream || small_stream) {
     e = timed("gateup_stream", s, [&] {
-      return moe::launch_gateup_stream_bf16(g, w, static_cast<const uint16_t*>(x), static_cast<uint16_t*>(h), H, I, s);
+      return moe::launch_gateup_stream_bf16(g, w, static_cast<const uint16_t*>(x), static_cast<uint16_t*>(h), H, I,
+                                            small_stream, s);
     });
     if (e != hipSuccess) return e;
-    return timed("down_stream", s, [&] {
-      return moe::launch_down_stream_bf16(g, w, static_cast<const uint16_t*>(h), y_rows, y_bf16, row_scale, H, I, s);
-    });
   }
+  if (all_stream)
+    return timed("down_stream", s, [&] {
+      return moe::launch_down_stream_bf16(g, w, static_cast<const uint16_t*>(h), y_rows, y_bf16, row_scale, H, I,
+                                          false, s);
+    });
   e = timed("gateup_tile", s, [&] {
     return moe::launch_gateup_tile_bf16(g, w, static_cast<const uint16_t*>(x), static_cast<uint16_t*>(h), H, I, s);
   });
   if (e != hipSuccess) return e;
+  if (small_stream) {
+    e = timed("down_stream", s, [&] {
+      return moe::launch_down_stream_bf16(g, w, static_cast<const uint16_t*>(h), y_rows, y_bf16, row_scale, H, I,
+                                          true, s);
+    });
+    if (e != hipSuccess) return e;
+  }
   return timed("down_tile", s, [&] {
     return moe::launch_down_tile_bf16(g, w, static_cast<const uint16_t*>(h), y_rows, y_bf16, row_scale, part, H, I,
                                       s);

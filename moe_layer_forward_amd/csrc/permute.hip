@@ -142,9 +142,12 @@ __device__ int32_t block_excl_scan(int32_t v, int32_t* sh, int32_t* total) {
 constexpr int kBuckets = 64;     // size classes for largest-first ordering (16-row passes, capped)
 constexpr int kPlanPerThread = 4;  // groups per thread -> at most 4096 groups
 
-// The plan of G groups (one 1024-thread work-group): active groups largest first, and their tiles.
+// The plan of G groups (one 1024-thread work-group): active groups largest first, and the tiles of
+// those with more than stream_rows rows (0 or kStreamRows; the smaller ones, a suffix of the active
+// list since the size classes are 16 rows wide, go to the weight-stream kernels).
 __device__ void plan_block(const int32_t* __restrict__ off, int G, int64_t max_rows, int tile_m, int max_tiles,
-                           int32_t* __restrict__ active, int32_t* __restrict__ counters, int32_t* __restrict__ tiles) {
+                           int stream_rows, int32_t* __restrict__ active, int32_t* __restrict__ counters,
+                           int32_t* __restrict__ tiles) {
   __shared__ int32_t bucket_cnt[kBuckets];
   __shared__ int32_t bucket_cur[kBuckets];
   __shared__ int32_t scan_buf[1024];
@@ -175,13 +178,17 @@ __device__ void plan_block(const int32_t* __restrict__ off, int G, int64_t max_r
     }
   }
   __syncthreads();
+  static_assert(kStreamRows % 16 == 0, "small groups fill whole size classes");
   if (tid == 0) {
-    int32_t run = 0;
+    const int small_b = kBuckets - stream_rows / 16;  // the size classes of the small groups start here
+    int32_t run = 0, n_large = 0;
     for (int b = 0; b < kBuckets; ++b) {
+      if (b == small_b) n_large = run;
       bucket_cur[b] = run;
       run += bucket_cnt[b];
     }
     counters[0] = run;
+    counters[2] = stream_rows > 0 ? n_large : run;
     n_active_sh = run;
   }
   __syncthreads();
@@ -203,7 +210,7 @@ __device__ void plan_block(const int32_t* __restrict__ off, int G, int64_t max_r
 #pragma unroll
   for (int j = 0; j < kPlanPerThread; ++j) {
     const int pos = tid * kPlanPerThread + j;
-    ntl[j] = pos < n_active ? (pos_of[pos] + tile_m - 1) / tile_m : 0;
+    ntl[j] = pos < n_active && pos_of[pos] > stream_rows ? (pos_of[pos] + tile_m - 1) / tile_m : 0;
     mine += ntl[j];
   }
   int32_t total;
@@ -224,9 +231,10 @@ __device__ void plan_block(const int32_t* __restrict__ off, int G, int64_t max_r
 }
 
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ off, int G, int64_t max_rows,
-                                                    int tile_m, int max_tiles, int32_t* __restrict__ active,
-                                                    int32_t* __restrict__ counters, int32_t* __restrict__ tiles) {
-  plan_block(off, G, max_rows, tile_m, max_tiles, active, counters, tiles);
+                                                    int tile_m, int max_tiles, int stream_rows,
+                                                    int32_t* __restrict__ active, int32_t* __restrict__ counters,
+                                                    int32_t* __restrict__ tiles) {
+  plan_block(off, G, max_rows, tile_m, max_tiles, stream_rows, active, counters, tiles);
 }
 
 // Few pairs (P <= kChunk): histogram, scan, stable scatter and (when plan.n_groups > 0) the plan in
@@ -300,8 +308,8 @@ __global__ __launch_bounds__(1024) void permute_plan_small_kernel(
   if (plan.n_groups == 0) return;  // permutation only
   __threadfence_block();
   __syncthreads();  // offsets written above are read back by the plan
-  plan_block(offsets, plan.n_groups, plan.max_rows, plan.tile_m, plan.max_tiles, plan.active, plan.counters,
-             plan.tiles);
+  plan_block(offsets, plan.n_groups, plan.max_rows, plan.tile_m, plan.max_tiles, plan.stream_rows, plan.active,
+             plan.counters, plan.tiles);
 }
 
 __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ row_token,
@@ -360,8 +368,8 @@ hipError_t launch_gather_rows(const void* x, const int32_t* row_token, void* x_p
 }
 
 hipError_t launch_plan(const Groups& g, hipStream_t s) {
-  plan_kernel<<<1, 1024, 0, s>>>(g.group_offsets, g.n_groups, g.max_rows, g.tile_m, g.max_tiles, g.active, g.counters,
-                                 g.tiles);
+  plan_kernel<<<1, 1024, 0, s>>>(g.group_offsets, g.n_groups, g.max_rows, g.tile_m, g.max_tiles, g.stream_rows,
+                                 g.active, g.counters, g.tiles);
   return hipGetLastError();
 }
 

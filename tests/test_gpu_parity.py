@@ -62,6 +62,17 @@ def test_small_bf16_every_token(T):
     _check_full(w, wl.device_inputs(w))
 
 
+def test_mixed_group_sizes_every_token():
+    # skewed routing: groups of a few rows (weight-stream kernels) beside groups of hundreds of rows
+    # (tile kernels) in the same layer call; few row tiles, so the down GEMM splits K and its
+    # reduction must leave the stream kernels' rows alone
+    _torch()
+    w = wl.custom("mixed", T=512, H=512, I=512, E=48, K=4, routing="skew")
+    y, ids, _ = _check_full(w, wl.device_inputs(w))
+    counts = np.bincount(to_np(ids).ravel(), minlength=w.E)
+    assert ((counts > 0) & (counts <= 32)).sum() >= 5 and (counts > 32).sum() >= 5, counts
+
+
 def test_single_token_and_no_shared_expert():
     _torch()
     w = wl.custom("one", T=1, H=256, I=128, E=16, K=3)
