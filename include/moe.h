@@ -25,6 +25,11 @@
  *     is a host struct read during the call only.
  *   - Tensors are row-major and contiguous.  Weights use the nn.Linear
  *     [out, in] layout: w_gate/w_up [E, I, H], w_down [E, H, I].
+ *   - Alignment: token rows, weights, 4-bit and FP8 codes, 4-bit scales and
+ *     outputs start on a 16-byte boundary; id, offset, routing-weight, row-
+ *     scale, bias and FP8-scale vectors on a 4-byte one (fresh allocations and
+ *     slices along the first dimension of these tensors are).  A misaligned
+ *     pointer returns MOE_ERR_INVALID_ARG.
  *   - dtype (config) is the element type of x, y, the router weight and the
  *     expert weights: MOE_BF16 (fp32 accumulation, the intermediate h rounded
  *     to bf16) or MOE_F32.  Routing scores/weights are always fp32, ids int32.

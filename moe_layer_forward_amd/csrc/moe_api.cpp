@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 
 #include "kernels.h"
@@ -339,6 +340,21 @@ int check_config_quant(const moe_config* c, moe::QFormat f) {
   return MOE_OK;
 }
 
+// Operands the kernels move 16 bytes at a time (token rows, weights, codes, 4-bit scales, outputs)
+// must start on a 16-byte boundary, index, weight and fp32-scale vectors on a 4-byte one.  NULL
+// pointers pass (their presence is checked separately).
+struct Aligned {
+  const void* p;
+  size_t bytes;
+  const char* what;
+};
+int check_aligned(const char* fn, std::initializer_list<Aligned> list) {
+  for (const Aligned& a : list)
+    if (a.p && reinterpret_cast<uintptr_t>(a.p) % a.bytes)
+      return fail(MOE_ERR_INVALID_ARG, "%s: %s must be %zu-byte aligned", fn, a.what, a.bytes);
+  return MOE_OK;
+}
+
 hipError_t run_router(const moe_config* c, int64_t T, const void* x, const void* w_router, float* part,
                       hipStream_t s) {
   const int H = c->hidden_size, E = c->n_routed_experts;
@@ -379,6 +395,15 @@ int forward_quant(const char* name, const moe_config* cfg, int64_t T, const void
   const bool shared = cfg->n_shared_experts == 1;
   if (shared && (!ws_gate || !ws_up || !ws_down))
     return fail(MOE_ERR_INVALID_ARG, "%s: shared expert weights are required", name);
+  const size_t sa = qw.format == moe::QFormat::kInt4 ? 16 : 4;  // 4-bit scales are read 16 bytes at a time
+  if ((st = check_aligned(name, {{x, 16, "x"}, {w_router, 16, "w_router"}, {qw.gate_codes, 16, "gate_codes"},
+                                 {qw.up_codes, 16, "up_codes"}, {qw.down_codes, 16, "down_codes"},
+                                 {qw.gate_scales, sa, "gate_scales"}, {qw.up_scales, sa, "up_scales"},
+                                 {qw.down_scales, sa, "down_scales"}, {ws_gate, 16, "ws_gate"}, {ws_up, 16, "ws_up"},
+                                 {ws_down, 16, "ws_down"}, {y, 16, "y"}, {score_bias, 4, "score_bias"},
+                                 {logit_offset, 4, "logit_offset"}, {topk_ids_out, 4, "topk_ids_out"},
+                                 {topk_weights_out, 4, "topk_weights_out"}})))
+    return st;
   if ((st = check_forward_spans(cfg, T))) return st;
   const int H = cfg->hidden_size, I = cfg->moe_intermediate_size, E = cfg->n_routed_experts, K = cfg->top_k;
   const int64_t P = T * K;
@@ -508,6 +533,10 @@ int moe_route(const moe_config* cfg, int64_t T, const void* x, const void* w_rou
   if (T == 0) return ok();
   if (!x || !w_router || !topk_ids || !topk_weights)
     return fail(MOE_ERR_INVALID_ARG, "moe_route: x, w_router, topk_ids and topk_weights are required");
+  if ((st = check_aligned("moe_route", {{x, 16, "x"}, {w_router, 16, "w_router"}, {score_bias, 4, "score_bias"},
+                                        {logit_offset, 4, "logit_offset"}, {topk_ids, 4, "topk_ids"},
+                                        {topk_weights, 4, "topk_weights"}})))
+    return st;
   const int H = cfg->hidden_size, E = cfg->n_routed_experts, K = cfg->top_k;
   const bool bf16 = cfg->dtype == MOE_BF16;
   if (bf16 && ((st = check_span("x [T, H]", T * H * 2)) || (st = check_span("w_router [E, H]", (int64_t)E * H * 2))))
@@ -538,6 +567,10 @@ int moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_ids, int32
     return fail(MOE_ERR_INVALID_ARG, "moe_permute: topk_ids, expert_offsets, row_token and pair_row are required");
   if ((x == nullptr) != (x_perm == nullptr))
     return fail(MOE_ERR_INVALID_ARG, "moe_permute: x and x_perm must both be given or both be NULL");
+  if ((st = check_aligned("moe_permute", {{topk_ids, 4, "topk_ids"}, {expert_offsets, 4, "expert_offsets"},
+                                          {row_token, 4, "row_token"}, {pair_row, 4, "pair_row"}, {x, 16, "x"},
+                                          {x_perm, 16, "x_perm"}})))
+    return st;
   const int E = cfg->n_routed_experts, K = cfg->top_k;
   Carver cv(workspace);
   int32_t* scratch = cv.take<int32_t>(moe::permute_scratch_ints(T * K, E));
@@ -573,6 +606,11 @@ int moe_grouped_swiglu(const moe_config* cfg, int32_t n_groups, const int32_t* g
   if (!group_offsets || !x || !w_gate || !w_up || !w_down || !y_rows)
     return fail(MOE_ERR_INVALID_ARG, "moe_grouped_swiglu: group_offsets, x, weights and y_rows are required");
   if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "y_dtype %d", y_dtype);
+  if ((st = check_aligned("moe_grouped_swiglu", {{group_offsets, 4, "group_offsets"}, {x, 16, "x"},
+                                                 {row_index, 4, "row_index"}, {w_gate, 16, "w_gate"},
+                                                 {w_up, 16, "w_up"}, {w_down, 16, "w_down"},
+                                                 {row_scale, 4, "row_scale"}, {y_rows, 16, "y_rows"}})))
+    return st;
   if (cfg->dtype == MOE_F32 && y_dtype != MOE_F32)
     return fail(MOE_ERR_UNSUPPORTED, "fp32 layers produce fp32 y_rows");
   if (cfg->dtype == MOE_BF16) {
@@ -604,6 +642,10 @@ int moe_combine(const moe_config* cfg, int64_t T, const void* y_rows, int32_t y_
   if (T == 0) return ok();
   if (!y_rows || !pair_row || !topk_weights || !y)
     return fail(MOE_ERR_INVALID_ARG, "moe_combine: y_rows, pair_row, topk_weights and y are required");
+  if ((st = check_aligned("moe_combine", {{y_rows, 16, "y_rows"}, {pair_row, 4, "pair_row"},
+                                          {topk_weights, 4, "topk_weights"}, {y_shared, 16, "y_shared"},
+                                          {y, 16, "y"}})))
+    return st;
   if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "y_dtype %d", y_dtype);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = timed("combine", s, [&] {
@@ -626,6 +668,13 @@ int moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_r
     return fail(MOE_ERR_INVALID_ARG, "moe_forward: x, w_router, expert weights and y are required");
   if (cfg->n_shared_experts == 1 && (!ws_gate || !ws_up || !ws_down))
     return fail(MOE_ERR_INVALID_ARG, "moe_forward: shared expert weights are required");
+  if ((st = check_aligned("moe_forward", {{x, 16, "x"}, {w_router, 16, "w_router"}, {w_gate, 16, "w_gate"},
+                                          {w_up, 16, "w_up"}, {w_down, 16, "w_down"}, {ws_gate, 16, "ws_gate"},
+                                          {ws_up, 16, "ws_up"}, {ws_down, 16, "ws_down"}, {y, 16, "y"},
+                                          {score_bias, 4, "score_bias"}, {logit_offset, 4, "logit_offset"},
+                                          {topk_ids_out, 4, "topk_ids_out"},
+                                          {topk_weights_out, 4, "topk_weights_out"}})))
+    return st;
   if ((st = check_forward_spans(cfg, T))) return st;
   const int H = cfg->hidden_size, E = cfg->n_routed_experts, K = cfg->top_k;
   const bool bf16 = cfg->dtype == MOE_BF16;
@@ -658,6 +707,12 @@ int moe_forward_routed(const moe_config* cfg, int64_t T, const void* x, const in
     return fail(MOE_ERR_INVALID_ARG, "moe_forward_routed: x, routing, expert weights and y are required");
   if (cfg->n_shared_experts == 1 && (!ws_gate || !ws_up || !ws_down))
     return fail(MOE_ERR_INVALID_ARG, "moe_forward_routed: shared expert weights are required");
+  if ((st = check_aligned("moe_forward_routed", {{x, 16, "x"}, {topk_ids, 4, "topk_ids"},
+                                                 {topk_weights, 4, "topk_weights"}, {w_gate, 16, "w_gate"},
+                                                 {w_up, 16, "w_up"}, {w_down, 16, "w_down"},
+                                                 {ws_gate, 16, "ws_gate"}, {ws_up, 16, "ws_up"},
+                                                 {ws_down, 16, "ws_down"}, {y, 16, "y"}})))
+    return st;
   if ((st = check_forward_spans(cfg, T))) return st;
   Carver cv(workspace);
   ForwardWs w = carve_forward(cv, cfg, T, false);

@@ -163,6 +163,31 @@ def test_fp8_forward_argument_checks():
         assert lib.moe_workspace_size(ctypes.byref(bad), moe.MOE_OP_FORWARD_FP8, 64, 0) == 0
 
 
+def test_misaligned_pointers_are_refused():
+    # checked on the host before anything is launched
+    lib = moe.load_library()
+    cfg = moe.make_config()
+    fake, odd8, odd2 = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1008), ctypes.c_void_p(0x1002)
+    ws = 1 << 40
+    rc = lib.moe_forward(ctypes.byref(cfg), 64, odd8, fake, None, None, fake, fake, fake, fake, fake, fake, fake,
+                         None, None, fake, ws, None)
+    assert rc == moe.MOE_ERR_INVALID_ARG and "x must be 16-byte aligned" in moe.moe_last_error()
+    rc = lib.moe_forward(ctypes.byref(cfg), 64, fake, fake, None, None, fake, fake, fake, fake, fake, fake, fake,
+                         odd2, None, fake, ws, None)
+    assert rc == moe.MOE_ERR_INVALID_ARG and "topk_ids_out must be 4-byte aligned" in moe.moe_last_error()
+
+    def fp8(codes=fake, scales=fake, ws=ws):
+        return lib.moe_forward_fp8(ctypes.byref(cfg), 64, fake, fake, None, None, codes, scales, fake, fake, fake,
+                                   fake, fake, fake, fake, fake, None, None, fake, ws, None)
+
+    assert fp8(codes=odd8) == moe.MOE_ERR_INVALID_ARG and "gate_codes" in moe.moe_last_error()
+    assert fp8(scales=odd2) == moe.MOE_ERR_INVALID_ARG and "gate_scales" in moe.moe_last_error()
+    # FP8 scales need 4 bytes only: with too small a workspace the call then stops at that check
+    assert fp8(scales=ctypes.c_void_p(0x1004), ws=16) == moe.MOE_ERR_WORKSPACE
+    rc = lib.moe_combine(ctypes.byref(cfg), 8, fake, 1, fake, fake, None, odd8, None)
+    assert rc == moe.MOE_ERR_INVALID_ARG and "y must be 16-byte aligned" in moe.moe_last_error()
+
+
 def test_zero_tokens_is_a_no_op():
     cfg = moe.make_config()
     lib = moe.load_library()
