@@ -30,16 +30,17 @@ def _torch():
     return torch
 
 
-def _check(w, t, tokens=None):
+def _check(w, t, tokens=None, bias=None):
     torch = _torch()
     cfg = moe.config_for(w)
     y, ids, wts = moe.moe_forward_fp8(cfg, t["x"], t["w_router"], {k: t[k] for k in moe.QUANT_KEYS},
                                       t.get("ws_gate"), t.get("ws_up"), t.get("ws_down"),
+                                      score_bias=None if bias is None else torch.from_numpy(bias).cuda(),
                                       logit_offset=t.get("logit_offset"), return_routing=True)
     torch.cuda.synchronize()
     tokens = np.arange(w.T) if tokens is None else np.asarray(tokens)
     ids_g, w_g, y_g = to_np(ids)[tokens], to_np(wts)[tokens], to_np(y)[tokens]
-    y_ref, ids_ref, w_ref, gap = oracle_forward_tokens(w, tokens, ids_gpu=ids_g)
+    y_ref, ids_ref, w_ref, gap = oracle_forward_tokens(w, tokens, ids_gpu=ids_g, score_bias=bias)
     differ = check_routing(ids_g, w_g, ids_ref, w_ref, gap)
     err = rel_l2(y_g, y_ref)
     print(f"{w.name}: T={w.T} checked {len(tokens)} tokens, near-tie swaps {len(differ)}, "
@@ -62,6 +63,15 @@ def test_fp8_small_every_token(T, H, I, E, K, shared):
     _torch()
     w = wl.custom(f"fp8_{T}", T, H, I, E, K, x_seed=41, w_seed=42, n_shared=shared, quant="fp8")
     _check(w, wl.device_inputs(w))
+
+
+def test_fp8_skewed_routing_with_bias():
+    # Zipf-shaped logit offsets (a few experts with many rows, many with one or two) and a score bias
+    # that enters the selection only
+    _torch()
+    w = wl.custom("fp8_skew", 200, 512, 256, 32, 4, x_seed=46, w_seed=47, routing="skew", quant="fp8")
+    bias = (np.random.default_rng(48).standard_normal(w.E) * 0.1).astype(np.float32)
+    _check(w, wl.device_inputs(w), bias=bias)
 
 
 def test_fp8_single_token():
