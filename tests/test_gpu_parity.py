@@ -252,10 +252,14 @@ def test_permute_call_integer_exact():
 
 
 @pytest.mark.parametrize("y_bf16", [False, True])
-@pytest.mark.parametrize("sizes", [[30, 0, 55, 0, 95], [3, 0, 5, 1, 0]], ids=["tile_kernels", "stream_kernels"])
+@pytest.mark.parametrize("sizes", [[30, 0, 55, 0, 95], [3, 0, 5, 1, 0],
+                                   [2, 40, 0, 7, 300, 1, 33, 32, 0, 5, 17, 64, 3, 0, 9, 120, 1, 31, 0, 2, 8, 0, 50, 4]],
+                         ids=["tile_kernels", "stream_kernels", "many_groups_both"])
 def test_grouped_swiglu_and_combine_calls(y_bf16, sizes):
+    # many_groups_both: 24 groups, so the groups of at most 32 rows go to the weight-stream kernels and
+    # the others (33 .. 300 rows) to the tile kernels in the same call
     torch = _torch()
-    w = wl.custom("gs", T=90, H=256, I=384, E=5, K=2)
+    w = wl.custom("gs", T=90, H=256, I=384, E=len(sizes), K=2)
     t = wl.device_inputs(w)
     # groups with 0 rows in the middle and at the end; rows gathered through row_index
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
@@ -270,7 +274,7 @@ def test_grouped_swiglu_and_combine_calls(y_bf16, sizes):
     torch.cuda.synchronize()
     x = wl.host_x(w)
     ref = np.zeros((rows, w.H))
-    for g in range(5):
+    for g in range(len(sizes)):
         a, b = off[g], off[g + 1]
         if b > a:
             ref[a:b] = scale[a:b, None] * oracle.swiglu_expert(x[row_index[a:b]], *wl.host_expert(w, g))
