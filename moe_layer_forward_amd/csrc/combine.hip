@@ -33,8 +33,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                                                       const float* __restrict__ weights,
                                                       const void* __restrict__ y_shared, void* __restrict__ y,
                                                       int64_t T, int K, int H) {
-  // one thread per (token, 8 columns); the K row loads are issued four at a time, the sum keeps
-  // k order
+  // one thread per (token, 8 columns); the row loads of up to 8 k (and the shared row) are issued
+  // before any of them is added, and the sum keeps k order, then adds the shared row
   const int cpr = H / 8;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= T * cpr) return;
@@ -43,7 +43,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   const int32_t* pr = pair_row + t * K;
   const float* wt = weights + t * K;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float sh[8];
+  if (y_shared) load8<ROWS_BF16>(y_shared, t * H + c, sh);
   int k = 0;
+  for (; k + 8 <= K; k += 8) {
+    float v[8][8], w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      w[u] = wt[k + u];
+      load8<ROWS_BF16>(y_rows, (int64_t)pr[k + u] * H + c, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w[u], v[u][e], acc[e]);
+  }
   for (; k + 4 <= K; k += 4) {
     float v[4][8], w[4];
 #pragma unroll
@@ -64,10 +78,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, v[e], acc[e]);
   }
   if (y_shared) {
-    float v[8];
-    load8<ROWS_BF16>(y_shared, t * H + c, v);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += v[e];
+    for (int e = 0; e < 8; ++e) acc[e] += sh[e];
   }
   if (Y_BF16) {
     uint32_t w[4];
