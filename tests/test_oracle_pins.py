@@ -454,3 +454,20 @@ def test_fp8_quantizer_round_trip_bound():
     np.testing.assert_array_equal(t32.to(torch.float8_e4m3fn).view(torch.uint8).numpy(), codes)
     zc, zs = synth.host_quantize_fp8(np.zeros((128, 128), dtype=np.uint16))
     assert zs[0, 0] == 0 and zc.sum() == 0 and np.all(oracle.dequant_fp8(zc, zs) == 0)
+
+
+def test_logit_offsets_force_selection():
+    """Offsets of +100 on exactly K experts select them whatever the router says, each with score
+    sigma(l + 100) = 1 in float64, so each weight is rsf / K; offsets of -100 on every other expert
+    leave the choice unchanged."""
+    x = _rng(11).standard_normal((16, 64))
+    wr = _rng(12).standard_normal((24, 64)) * 0.02
+    forced = np.array([3, 7, 19, 22])
+    off = np.zeros(24, np.float32)
+    off[forced] = 100.0
+    for rest in (0.0, -100.0):
+        o = off.copy()
+        o[np.setdiff1d(np.arange(24), forced)] = rest
+        ids, w, gap, s = oracle.route(x, wr, 4, RSF, logit_offset=o)
+        np.testing.assert_array_equal(np.sort(ids, axis=1), np.tile(forced, (16, 1)))
+        np.testing.assert_array_equal(w, np.full((16, 4), RSF / 4))
