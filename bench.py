@@ -50,6 +50,9 @@ KERNEL_SYMBOLS = {
     "down_tile": ("::down_tile_kernel", ["gemm_tile.hip", "tile_core.h", "kernels.h"]),
     "router_logits": ("::router_logits_kernel", ["route.hip", "tile_core.h", "kernels.h"]),
     "combine": ("::combine_kernel", ["combine.hip", "kernels.h"]),
+    "router_logits_f32": ("::router_logits_f32_kernel", ["route.hip", "tile_core.h", "kernels.h"]),
+    "gateup_f32": ("::gateup_f32_kernel", ["gemm_simple.hip", "kernels.h"]),
+    "down_f32": ("::down_f32_kernel", ["gemm_simple.hip", "kernels.h"]),
     "gateup_q4": ("::q_stream_kernel<(moe::QFormat)0, true", ["gemm_quant.hip", "tile_core.h", "kernels.h"]),
     "down_q4": ("::q_stream_kernel<(moe::QFormat)0, false", ["gemm_quant.hip", "tile_core.h", "kernels.h"]),
     "gateup_fp8": ("::q_stream_kernel<(moe::QFormat)1, true", ["gemm_quant.hip", "tile_core.h", "kernels.h"]),
