@@ -19,7 +19,10 @@
 // K loop is unrolled by the stage count, so the compiler can tell which LDS reads depend on which
 // direct loads.
 // Work-groups = 4 waves (64 h columns, or 128 output columns of down) of one group; groups come from
-// the plan's active list, largest first, so the long-running many-row groups start early.
+// the plan's active list, largest first, so the long-running many-row groups start early.  Besides
+// decode-like calls (every group here), the kernels take the groups of at most kStreamRows rows of
+// calls with many groups whose larger groups go to the tile kernels (small_only: the plan's active
+// list from counters[2] on).
 #include <type_traits>
 
 #include "kernels.h"
