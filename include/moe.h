@@ -231,7 +231,7 @@ int moe_forward_q4(const moe_config* cfg, int64_t T, const void* x, const void* 
  * y_rows to bf16.  The shared expert and the combine are as in moe_forward.
  * Shapes: as moe_forward, with hidden_size and moe_intermediate_size multiples of 128 and at
  * most 8192 (else MOE_ERR_UNSUPPORTED).
- * Each routed expert that received tokens has its codes read once per 8 of its rows (the kernels
+ * Each routed expert that received tokens has its codes read once per 16 of its rows (the kernels
  * stream weights; they are built for decode-sized T, about one row per expert).
  * Workspace: moe_workspace_size(cfg, MOE_OP_FORWARD_FP8, T, 0). */
 int moe_forward_fp8(const moe_config* cfg, int64_t T, const void* x, const void* w_router,

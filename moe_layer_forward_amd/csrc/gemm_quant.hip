@@ -33,7 +33,7 @@
 // contiguous bytes (whole lines) with the streaming policy; the 16-byte chunk c of a 128-byte row r
 // sits at c ^ ((r >> 1) & 7) so the 16 rows of one B-operand read hit different banks.  A step
 // covers 128 bytes of codes per row (256 inputs of 4-bit codes, 128 of FP8).  The token rows of a
-// pass (4 rows of 256 inputs, or 8 rows of 128) are shared by the work-group's 4 waves through the
+// pass (4 rows of 256 inputs, or 16 rows of 128) are shared by the work-group's 4 waves through the
 // same ring (a barrier per step); the 4-bit scales come a 4-step block at a time through LDS, the
 // FP8 scales of a wave's whole rows sit one per lane in a register.
 // Work-groups = 4 waves; groups from the plan's active list, largest first; the first work-groups
@@ -57,8 +57,6 @@ constexpr int kCodeRowB = 128;          // bytes of codes per row per step
 constexpr int kSetCodeB = 16 * kCodeRowB;
 constexpr int kWaveB = 2 * kSetCodeB;   // one wave's part of the codes of one ring stage
 constexpr int kCodesB = kWaves * kWaveB;
-constexpr int kAB = 2048;               // a pass's token rows of one step, shared by the waves
-constexpr int kStageB = kCodesB + kAB;
 constexpr int kD = 4;                   // ring stages = steps in flight = steps per 4-bit scale block
 constexpr int kScaleRowB = kD * 16;     // a row's binary16 scales for the kD steps of a block
 constexpr int kScaleSetB = 16 * kScaleRowB;  // = one 64-lane 16-byte store
@@ -75,7 +73,7 @@ struct Fmt<QFormat::kInt4> {
 template <>
 struct Fmt<QFormat::kFp8> {
   static constexpr int kStepK = 128;
-  static constexpr int kPassRows = 8;
+  static constexpr int kPassRows = 16;
   static constexpr int kBlock = 128;   // scale block edge
   static constexpr int kMaxSteps = 64; // a wave's row of scales fits one register of 64 lanes
 };
@@ -88,8 +86,19 @@ template <QFormat F>
 constexpr int64_t code_row_bytes(int64_t K) {
   return K * kCodeRowB / Fmt<F>::kStepK;
 }
-static_assert(Fmt<QFormat::kInt4>::kPassRows * a_row_bytes<QFormat::kInt4>() == kAB, "token rows of a step");
-static_assert(Fmt<QFormat::kFp8>::kPassRows * a_row_bytes<QFormat::kFp8>() == kAB, "token rows of a step");
+// a pass's token rows of one step (in the ring stage, shared by the waves), and the whole stage
+template <QFormat F>
+constexpr int a_stage_bytes() {
+  return Fmt<F>::kPassRows * a_row_bytes<F>();
+}
+template <QFormat F>
+constexpr int stage_bytes() {
+  return kCodesB + a_stage_bytes<F>();
+}
+static_assert(a_stage_bytes<QFormat::kInt4>() == 2048 && a_stage_bytes<QFormat::kFp8>() == 4096, "token rows");
+// two work-groups per CU: 4 stages each, plus the 4-bit scale buffer, within the 160 KiB of LDS
+static_assert(2 * (4 * stage_bytes<QFormat::kFp8>()) <= 160 * 1024, "LDS");
+static_assert(2 * (4 * stage_bytes<QFormat::kInt4>() + kWaves * kScaleWaveB) <= 160 * 1024, "LDS");
 
 // Compile-time loop: f(integral_constant<int, I>) for I = 0 .. N-1.
 template <int N, int I = 0, class F>
@@ -187,7 +196,7 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
 typedef __attribute__((address_space(3))) void* LdsPtr;
 
 // Token rows in a ring stage: row r of the pass at r * a_row_bytes, its 16-byte piece g at a
-// position xor-ed with the row (4-bit: 4 rows of 32 pieces, g ^ 4r; FP8: 8 rows of 16 pieces,
+// position xor-ed with the row (4-bit: 4 rows of 32 pieces, g ^ 4r; FP8: 16 rows of 16 pieces,
 // g ^ r), so the rows one A-operand read touches fall in different banks.
 template <QFormat F>
 __device__ __forceinline__ int a_pos(int r, int g) {
@@ -245,9 +254,9 @@ struct QStream {
     }
   }
 
-  // Half of the pass's token rows of step k (1 KiB) into ring stage d (the same rows for every
-  // column block).  Waves w and w + 2 load the same half: identical bytes to the same place, and
-  // every wave issues the same loads.
+  // This wave's 1 KiB part of the pass's token rows of step k into ring stage d (the same rows for
+  // every column block): a quarter for FP8; a half for 4-bit, which waves w and w + 2 both load
+  // (identical bytes to the same place), so that every wave issues the same loads.
   __device__ __forceinline__ void issue_rows(char* const (&ring)[kD], int d, int b, int k, int nblk) const {
     b = __builtin_amdgcn_readfirstlane(b);
     k = __builtin_amdgcn_readfirstlane(k);
@@ -451,18 +460,21 @@ __device__ __forceinline__ void q_pass(const QArgs& p, char* const (&ring)[kD], 
   constexpr int kPassRows = Fmt<F>::kPassRows;
   constexpr int kARowB = a_row_bytes<F>();
   constexpr int kRowLanes = kARowB / 16;  // lanes per token row of a wave's load
+  constexpr int kParts = a_stage_bytes<F>() / 1024;  // 1 KiB parts of a step's rows (2 or 4 waves' loads)
+  constexpr int kPartRows = kPassRows / kParts;
   const int H = p.H, I = p.I, K = SWIGLU ? H : I;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int part = wave % kParts;  // with 2 parts, waves w and w + 2 load the same one
   QStream<F> s = base;
-  {  // this wave's row (kPassRows/2)(w % 2) + lane/kRowLanes, piece position lane % kRowLanes
-    const int rl = (kPassRows / 2) * (wave & 1) + lane / kRowLanes;
+  {  // this wave's row kPartRows * part + lane/kRowLanes, piece position lane % kRowLanes
+    const int rl = kPartRows * part + lane / kRowLanes;
     const int64_t r = mb + rl;
     const int64_t rr = r < r1 ? r : mb;  // rows past the group end repeat its first row, never stored
     const int64_t src = SWIGLU ? (p.row_index ? (int64_t)p.row_index[rr] : rr) : rr;
     s.a_off = (uint32_t)(src * K * 2 + (a_pos<F>(rl, lane % kRowLanes) << 4));
   }
-  s.a_dst = (wave & 1) * (kAB / 2);
+  s.a_dst = part * 1024;
   f32x4 acc[CHAIN][2];
 #pragma unroll
   for (int b = 0; b < CHAIN; ++b) acc[b][0] = acc[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -627,11 +639,25 @@ __device__ __forceinline__ void shared_part(const QArgs& p, char* const (&ring)[
   }
 }
 
+// The 4-bit scale buffer (LDS); FP8 has none, so that two FP8 work-groups fit a CU's LDS.
+template <QFormat F>
+struct ScaleBuf {
+  __device__ static char* get() {
+    __shared__ __align__(16) char sc[kWaves * kScaleWaveB];
+    return sc;
+  }
+};
+template <>
+struct ScaleBuf<QFormat::kFp8> {
+  __device__ static char* get() { return nullptr; }
+};
+
 template <QFormat F, bool SWIGLU, int CHAIN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void q_stream_kernel(QArgs p) {
   // one array per stage: the compiler then tells the stages' direct loads and LDS reads apart
+  constexpr int kStageB = stage_bytes<F>();
   __shared__ __align__(16) char s0[kStageB], s1[kStageB], s2[kStageB], s3[kStageB];
-  __shared__ __align__(16) char sc[F == QFormat::kInt4 ? kWaves * kScaleWaveB : 16];
+  char* const sc = ScaleBuf<F>::get();
   static_assert(kD == 4, "one LDS array per ring stage");
   char* const ring[kD] = {s0, s1, s2, s3};
 

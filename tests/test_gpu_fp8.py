@@ -3,7 +3,7 @@
 The oracle evaluates the layer in float64 on the dequantized weights (E4M3 value times its 128 x 128
 block scale, from the host quantizer's codes and scales); the GPU multiplies in binary16 with fp32
 accumulation, so the bf16 output bar (per-row relative L2 <= 2e-2) applies.  Cases: small sizes on
-every token (several 8-row passes per expert and a ragged tail; no shared expert; odd numbers of
+every token (several 16-row passes per expert and a ragged tail; no shared expert; odd numbers of
 128-blocks, where the down kernel runs one column block per work-group and the K loops end on
 padded steps; a long W_down row whose scales do not fit the chained down kernel; hidden_size at
 its 8192 limit; more than 4096 (token, expert) pairs), and the full decode shape on sampled tokens.
@@ -51,7 +51,7 @@ def _check(w, t, tokens=None, bias=None):
 
 
 @pytest.mark.parametrize("T,H,I,E,K,shared", [
-    (70, 512, 256, 8, 2, 1),     # ~17.5 rows per expert: three 8-row passes, ragged
+    (70, 512, 256, 8, 2, 1),     # ~17.5 rows per expert: two 16-row passes, ragged
     (5, 768, 512, 40, 4, 0),     # one or two rows per expert, no shared expert; chained down blocks
     (40, 384, 640, 12, 3, 1),    # 3 x 5 blocks: one down column block per work-group, padded K steps
     (8, 256, 4608, 8, 2, 1),     # W_down rows of 36 blocks: scales too many for the chained down kernel
