@@ -32,6 +32,8 @@ import re
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -134,7 +136,8 @@ def measure_peaks():
 
     lib = ctypes.CDLL(os.path.join(ROOT, "moe_layer_forward_amd", "libmoe_peaks.so"))
     i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32
-    lib.peaks_read.argtypes = [vp, i64, vp, vp]
+    lib.peaks_read.argtypes = [vp, i64, i32, vp]
+    lib.peaks_read_vgpr.argtypes = [vp, i64, vp, vp]
     lib.peaks_copy.argtypes = [vp, vp, i64, vp]
     lib.peaks_mfma.argtypes = [i32, i32, vp, vp]
     stream = torch.cuda.current_stream().cuda_stream
@@ -157,7 +160,8 @@ def measure_peaks():
     rd = 4 << 30
     buf = torch.empty(rd, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
-    t_read = best(lambda: lib.peaks_read(buf.data_ptr(), rd, sink.data_ptr(), stream))
+    t_read = best(lambda: lib.peaks_read(buf.data_ptr(), rd, 512, stream))
+    t_read_v = best(lambda: lib.peaks_read_vgpr(buf.data_ptr(), rd, sink.data_ptr(), stream))
     half = rd // 2
     t_copy = best(lambda: lib.peaks_copy(buf.data_ptr(), buf.data_ptr() + half, half, stream))
     del buf
@@ -165,9 +169,11 @@ def measure_peaks():
     blocks, iters = 256 * 4, 2000
     t_mfma = best(lambda: lib.peaks_mfma(blocks, iters, sink.data_ptr(), stream))
     flops = blocks * 4 * 4 * iters * 32768
-    return {"hbm_read_GB_s": rd / t_read / 1e9, "hbm_copy_GB_s": 2 * half / t_copy / 1e9,
+    return {"hbm_read_GB_s": max(rd / t_read, rd / t_read_v) / 1e9, "hbm_read_lds_GB_s": rd / t_read / 1e9,
+            "hbm_read_vgpr_GB_s": rd / t_read_v / 1e9, "hbm_copy_GB_s": 2 * half / t_copy / 1e9,
             "mfma_bf16_TFLOP_s": flops / t_mfma / 1e12,
-            "how": "streaming read of 4 GiB; 2 GiB copy counted as read + write; 4 independent "
+            "how": "streaming read of 4 GiB (the better of direct-to-LDS non-temporal 1 KiB loads, 8 waves per "
+                   "CU, and 16-byte register loads); 2 GiB copy counted as read + write; 4 independent "
                    "v_mfma_f32_32x32x16_bf16 chains per wave, 16 waves per CU; best of 5"}
 
 
@@ -198,9 +204,39 @@ def vendor_gemm(E=385, M=192, H=7168, I=2048, reps=10):
     return out
 
 
-def kernel_work(name, w, n_touched):
-    """Algorithmic (bytes, flops) of one launch of a grouped GEMM kernel: the weights of every group
-    with rows read once, the token rows / h read once, the outputs written once."""
+STREAM_ROWS, STREAM_MIN_GROUPS = 32, 16   # the device plan's split (kStreamRows, kStreamMinGroups)
+
+
+def plan_families(w, ids):
+    """Which groups the library's plan hands to the weight-stream kernels and which to the tile
+    kernels, from the realised routing (host mirror of moe_api.cpp's kernel choice and the device
+    plan's split at kStreamRows).  Returns {family: [(group, rows, tokens)]}, tokens being the set of
+    token ids whose rows the group reads (None = every token)."""
+    if w.routing == "dense":
+        groups = [(0, w.T, None)]
+    else:
+        ids = np.asarray(ids)
+        groups = []
+        for e in range(w.E):
+            t_idx = np.nonzero((ids == e).any(axis=1))[0]
+            rows = int((ids == e).sum())
+            if rows:
+                groups.append((e, rows, t_idx))
+        if w.n_shared:
+            groups.append((w.E, w.T, None))
+    n_groups = (1 if w.routing == "dense" else w.E + w.n_shared)
+    max_rows = w.T if w.routing == "dense" else w.T * w.K + w.T * w.n_shared
+    if max_rows <= 4 * n_groups:
+        return {"stream": groups, "tile": []}
+    cut = STREAM_ROWS if n_groups >= STREAM_MIN_GROUPS else 0
+    return {"stream": [g for g in groups if g[1] <= cut], "tile": [g for g in groups if g[1] > cut]}
+
+
+def kernel_work(name, w, fams, n_touched):
+    """Algorithmic (bytes, flops) of one launch of a grouped-GEMM kernel: the weights of the groups the
+    plan gives that kernel, once each; the token rows those groups read (each token's row once), or
+    their h rows; the outputs written once.  Weight re-reads (per 32-row pass of the stream kernels,
+    per row tile of the tile kernels) are traffic, not algorithmic bytes."""
     eb = 2 if w.dtype == "bf16" else 4
     if name in ("gateup_q4", "down_q4", "gateup_fp8", "down_fp8"):
         # routed experts with quantized weights (f16 token rows and h), plus the shared expert's bf16
@@ -212,17 +248,41 @@ def kernel_work(name, w, n_touched):
             return wbytes + w.T * w.H * 2 * (1 + w.n_shared) + rows * w.I * 2, rows * 2 * 2 * w.I * w.H
         wbytes = (n_touched * qb + w.n_shared * 2) * w.H * w.I
         return wbytes + rows * w.I * 2 + rows * w.H * 2, rows * 2 * w.H * w.I
-    n_groups_active = n_touched + w.n_shared
-    rows = w.T * w.K + w.T * w.n_shared
-    if w.quant != "none":  # the bf16 kernels run the shared expert alone
-        n_groups_active, rows = 1, w.T
+    fam = "stream" if name.endswith("_stream") else "tile" if name.endswith("_tile") else None
+    if fam is None or fams is None:
+        return None, None
+    groups = fams[fam]
+    if not groups:
+        return None, None
+    rows = sum(g[1] for g in groups)
+    if any(g[2] is None for g in groups):
+        tokens = w.T
+    else:
+        tokens = len(np.unique(np.concatenate([g[2] for g in groups])))
     if name.startswith("gateup"):
-        wbytes = n_groups_active * 2 * w.I * w.H * eb
-        return wbytes + w.T * w.H * eb + rows * w.I * eb, rows * 2 * 2 * w.I * w.H
+        return (len(groups) * 2 * w.I * w.H * eb + tokens * w.H * eb + rows * w.I * eb,
+                rows * 2 * 2 * w.I * w.H)
     if name.startswith("down"):
-        wbytes = n_groups_active * w.H * w.I * eb
-        return wbytes + rows * w.I * eb + rows * w.H * eb, rows * 2 * w.H * w.I
+        return len(groups) * w.H * w.I * eb + rows * w.I * eb + rows * w.H * eb, rows * 2 * w.H * w.I
     return None, None
+
+
+def roofline_of(name, w, kb, kf, us):
+    """Roofline of one kernel launch: bound by HBM when its algorithmic flops per byte sit below the
+    ridge of the published peaks, else by the matrix cores."""
+    peak_flops = BF16_PEAK if w.dtype == "bf16" else F32_PEAK
+    s = us * 1e-6
+    if kf / kb < peak_flops / HBM_PEAK:
+        r = {"bound": "hbm", "achieved": kb / s / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+             "frac": kb / s / HBM_PEAK}
+    else:
+        r = {"bound": "mfma", "achieved": kf / s / 1e12, "peak": peak_flops / 1e12, "unit": "TFLOP/s",
+             "frac": kf / s / peak_flops}
+    r.update({"traffic": load_traffic(w.name, name), "kernel": name, "bytes_per_launch": kb,
+              "flops_per_launch": kf, "avg_launch_us": us})
+    if r["frac"] > 1.0:
+        log(f"warning: {w.name} {name}: roofline fraction {r['frac']:.3f} > 1 -- the algorithmic count is wrong")
+    return r
 
 
 def layer_work(w, n_touched):
@@ -356,6 +416,7 @@ def run(w, weights, steps, warmup, graph=True):
         del flush
 
     # routing actually realised (counts touched experts for the byte accounting)
+    ids_np = None
     if w.routing == "dense":
         counts = np.array([T])
     else:
@@ -363,23 +424,19 @@ def run(w, weights, steps, warmup, graph=True):
             ids = acts["topk_ids"]
         else:
             ids, _ = moe.moe_route(cfg, acts["x"], weights["w_router"], logit_offset=acts.get("logit_offset"))
-        counts = np.bincount(ids.cpu().numpy().ravel(), minlength=w.E)
+        ids_np = ids.cpu().numpy()
+        counts = np.bincount(ids_np.ravel(), minlength=w.E)
     n_touched = int((counts > 0).sum())
     lb, lf = layer_work(w, n_touched)
+    fams = plan_families(w, None if w.routing == "dense" else ids_np) if w.quant == "none" else None
+    per_kernel = {}
+    for n, us in kern.items():
+        kb, kf = kernel_work(n, w, fams, n_touched)
+        if kb:
+            per_kernel[n] = roofline_of(n, w, kb, kf, us * 1e3)
     dom = max(kern, key=kern.get)
-    kb, kf = kernel_work(dom, w, n_touched)
-    dom_s = kern[dom] * 1e-3
+    roof = per_kernel.get(dom)
     peak_flops = BF16_PEAK if w.dtype == "bf16" else F32_PEAK
-    if kb is not None and kf / kb < peak_flops / HBM_PEAK:
-        roof = {"bound": "hbm", "achieved": kb / dom_s / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                "frac": kb / dom_s / HBM_PEAK, "traffic": load_traffic(w.name, dom), "kernel": dom,
-                "bytes_per_launch": kb, "flops_per_launch": kf, "avg_launch_us": kern[dom] * 1e3}
-    elif kb is not None:
-        roof = {"bound": "mfma", "achieved": kf / dom_s / 1e12, "peak": peak_flops / 1e12, "unit": "TFLOP/s",
-                "frac": kf / dom_s / peak_flops, "traffic": load_traffic(w.name, dom), "kernel": dom,
-                "bytes_per_launch": kb, "flops_per_launch": kf, "avg_launch_us": kern[dom] * 1e3}
-    else:
-        roof = None
     s = ms * 1e-3
     layer = {"GB_s": lb / s / 1e9, "TFLOP_s": lf / s / 1e12, "hbm_frac": lb / s / HBM_PEAK,
              "mfma_frac": lf / s / peak_flops, "alg_bytes": lb, "alg_flops": lf, "touched_experts": n_touched,
@@ -392,8 +449,14 @@ def run(w, weights, steps, warmup, graph=True):
     if flushed_ms is not None:
         layer["flushed_ms_median"] = flushed_ms
         layer["flushed_mfma_frac"] = lf / (flushed_ms * 1e-3) / peak_flops
+    if fams is not None:
+        layer["groups_on_stream_kernels"] = len(fams["stream"])
+        layer["groups_on_tile_kernels"] = len(fams["tile"])
     return {"tokens_per_s": T / s, "ms_per_step": ms, "roofline": roof, "layer": layer,
-            "kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()}}
+            "kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
+            "kernels_roofline": {k: {f: v[f] for f in ("bound", "achieved", "unit", "frac", "bytes_per_launch",
+                                                       "flops_per_launch")}
+                                 for k, v in per_kernel.items()}}
 
 
 def _time_oracle(w, n_tokens):
@@ -441,6 +504,59 @@ def cpu_baseline(w, n_tokens, n_tokens_1t=4):
         out["one_thread"] = {"value": n_tokens_1t / el1, "unit": "tokens/s", "cores": 1,
                              "sample": f"first {n_tokens_1t} tokens, one BLAS thread; {el1:.2f} s timed"}
     return out
+
+
+def cpu_baseline_sampled(w, n_experts=8, n_shared_rows=512, seed=7):
+    """The oracle on a bounded sample of a large workload, extrapolated to the whole batch and labelled
+    "sampled": the routing of every token (oracle.route), the SwiGLU of n_experts routed experts
+    (drawn at random among the touched ones) over all of their rows, scaled to all routed rows by row
+    count, and the shared expert on n_shared_rows rows, scaled to T rows (oracle.swiglu_expert).
+    Only the oracle's arithmetic is timed (input regeneration is not); the combine is not timed."""
+    import oracle
+    from moe_layer_forward_amd import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    rng = np.random.default_rng(seed)
+    x = wl.host_x(w)
+    t_route = 0.0
+    if w.routing == "preassigned":
+        ids = wl.preassigned(w)[0]
+    else:
+        t0 = time.perf_counter()
+        ids = oracle.route(x, wl.host_router(w), w.K, w.rsf, logit_offset=wl.logit_offsets(w))[0]
+        t_route = time.perf_counter() - t0
+    counts = np.bincount(ids.ravel(), minlength=w.E)
+    touched = np.nonzero(counts)[0]
+    pick = np.sort(rng.choice(touched, min(n_experts, len(touched)), replace=False))
+    t_exp, rows_exp = 0.0, 0
+    for e in pick:
+        t_idx = np.nonzero((ids == e).any(axis=1))[0]
+        if w.routing == "preassigned" and len(t_idx) > n_shared_rows:
+            t_idx = t_idx[:n_shared_rows]
+        wts = wl.host_expert(w, int(e))
+        t0 = time.perf_counter()
+        oracle.swiglu_expert(x[t_idx], *wts)
+        t_exp += time.perf_counter() - t0
+        rows_exp += len(t_idx)
+    t_routed = t_exp / rows_exp * ids.size
+    t_shared = 0.0
+    if w.n_shared:
+        sh = wl.host_shared(w)
+        m = min(n_shared_rows, w.T)
+        t0 = time.perf_counter()
+        oracle.swiglu_expert(x[:m], *sh)
+        t_shared = (time.perf_counter() - t0) * w.T / m
+    total = t_route + t_routed + t_shared
+    return {"value": w.T / total, "unit": "tokens/s", "cores": threads, "kind": "oracle", "sampled": True,
+            "sample": f"{w.name} (T={w.T}): "
+                      + (f"routing of all {w.T} tokens ({t_route:.2f} s), " if t_route else "routing given, ")
+                      + f"SwiGLU of {len(pick)} of {len(touched)} touched routed experts over all their "
+                        f"{rows_exp} rows ({t_exp:.2f} s, scaled by rows to {ids.size} routed rows), shared "
+                        f"expert on {min(n_shared_rows, w.T)} rows (scaled to {w.T}); float64 numpy; "
+                        f"combine not timed; extrapolated total {total:.1f} s"}
 
 
 def _csv_rows(d, suffix):
@@ -600,12 +716,19 @@ def main():
         if key not in weights_cache:
             src = wl.WORKLOADS["decode"] if shared_moe else w
             log(f"generating weights for {src.name} ...")
+            t0 = time.perf_counter()
             weights_cache[key] = wl.device_weights(src)
             torch.cuda.synchronize()
+            phases["weights"] = round(phases["weights"] + time.perf_counter() - t0, 2)
         return weights_cache[key]
 
+    phases = {"weights": 0.0, "workloads": {}, "cpu_baseline": {}}
+    t_start = time.perf_counter()
+    wt = weights_for(main_w)
     log(f"running {main_w.name} ...")
-    res = run(main_w, weights_for(main_w), args.steps, args.warmup, graph=not args.no_graph)
+    t0 = time.perf_counter()
+    res = run(main_w, wt, args.steps, args.warmup, graph=not args.no_graph)
+    phases["workloads"][main_w.name] = round(time.perf_counter() - t0, 2)
     out = {
         "metric": METRIC, "value": res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
@@ -614,29 +737,55 @@ def main():
                    "K": main_w.K, "n_shared": main_w.n_shared, "routed_scaling_factor": main_w.rsf,
                    "parallelism": "1 GPU"},
         "roofline": res["roofline"], "layer": res["layer"], "kernels_us": res["kernels_us"],
+        "kernels_roofline": res["kernels_roofline"],
     }
     for name in [n for n in args.also.split(",") if n and n not in ("none", args.workload)]:
         w2 = wl.WORKLOADS[name]
+        wt2 = weights_for(w2)
         log(f"running {w2.name} ...")
-        r2 = run(w2, weights_for(w2), args.steps, args.warmup, graph=not args.no_graph)
+        t0 = time.perf_counter()
+        r2 = run(w2, wt2, args.steps, args.warmup, graph=not args.no_graph)
+        phases["workloads"][w2.name] = round(time.perf_counter() - t0, 2)
         out[w2.name] = {"value": r2["tokens_per_s"], "unit": "tokens/s", "ms_per_step": r2["ms_per_step"],
                         "config": {"workload": w2.name, "T": w2.T},
                         "dtype": {"int4": "f16 x int4 (routed), bf16 (shared)",
                                   "fp8": "f16 x e4m3 (routed), bf16 (shared)"}.get(w2.quant, w2.dtype),
                         "roofline": r2["roofline"],
-                        "layer": r2["layer"], "kernels_us": r2["kernels_us"]}
+                        "layer": r2["layer"], "kernels_us": r2["kernels_us"],
+                        "kernels_roofline": r2["kernels_roofline"]}
     weights_cache.clear()
     torch.cuda.empty_cache()
     if not args.no_peaks:
         log("measuring this GPU's peaks ...")
+        t0 = time.perf_counter()
         pk = measure_peaks()
+        # the best HBM-bound kernel of this run, beside the read kernels: the "measured read" roof is
+        # the highest of them, so no fraction of it exceeds 1
+        best = max(((r["achieved"], f"{wn}/{kn}") for wn, kr in
+                    [(out["config"]["workload"], out["kernels_roofline"])] +
+                    [(k, v["kernels_roofline"]) for k, v in out.items() if isinstance(v, dict) and
+                     "kernels_roofline" in v]
+                    for kn, r in kr.items() if r["bound"] == "hbm"), default=(0.0, None))
+        pk["hbm_read_best_GB_s"] = max(pk["hbm_read_GB_s"], best[0])
+        pk["hbm_read_best_of"] = "read kernels" if pk["hbm_read_GB_s"] >= best[0] else f"kernel {best[1]}"
         out["measured_peaks"] = pk
         for layer in [out["layer"]] + [v["layer"] for v in out.values() if isinstance(v, dict) and "layer" in v]:
-            layer["hbm_frac_of_measured_read"] = layer["GB_s"] / pk["hbm_read_GB_s"]
+            layer["hbm_frac_of_measured_read"] = layer["GB_s"] / pk["hbm_read_best_GB_s"]
             layer["mfma_frac_of_measured"] = layer["TFLOP_s"] / pk["mfma_bf16_TFLOP_s"]
+        phases["peaks"] = round(time.perf_counter() - t0, 2)
     if args.cpu_tokens > 0:
         log("timing the oracle on the host ...")
+        t0 = time.perf_counter()
         out["cpu_baseline"] = cpu_baseline(main_w, min(args.cpu_tokens, main_w.T))
+        phases["cpu_baseline"][main_w.name] = round(time.perf_counter() - t0, 2)
+        for name in ("prefill", "skew", "ep_share"):
+            if name in out and isinstance(out[name], dict):
+                log(f"timing the oracle on a sample of {name} ...")
+                t0 = time.perf_counter()
+                out[name]["cpu_baseline"] = cpu_baseline_sampled(wl.WORKLOADS[name])
+                phases["cpu_baseline"][name] = round(time.perf_counter() - t0, 2)
+    phases["total"] = round(time.perf_counter() - t_start, 2)
+    out["phases_s"] = phases
     print(json.dumps(out), flush=True)
 
 

@@ -208,7 +208,9 @@ struct QStream {
   static constexpr bool kQ4 = F == QFormat::kInt4;
   static constexpr int kPassRows = Fmt<F>::kPassRows;
   static constexpr int kARowB = a_row_bytes<F>();
-  static constexpr int kLoads = 2 * 2 + 1;  // per step: codes, and this wave's half of the token rows
+  // per step: codes (2 sets x 2 direct loads), and this wave's part of the pass's token rows (FP8: a
+  // quarter, one per wave; 4-bit: a half, loaded by waves w and w + 2 alike)
+  static constexpr int kLoads = 2 * 2 + 1;
   static constexpr int kScaleLoads = kQ4 ? 2 : 0;  // per block of kD steps: 4-bit scales (into registers)
   static_assert(2 * kLoads + kScaleLoads <= 63, "vmcnt");
 
@@ -220,7 +222,7 @@ struct QStream {
   uint32_t s_off;           // 4-bit: lane offset of the scale load (row lane/4, piece lane%4 of a block)
   uint32_t a_off;           // lane offset of this wave's token-row load (row, swizzled piece)
   uint32_t blk_cb, blk_sb;  // bytes between consecutive column blocks of the codes / the scales
-  int wave_off, sc_wave_off, a_dst;  // this wave's codes, scale buffer, and token-row half
+  int wave_off, sc_wave_off, a_dst;  // this wave's codes, scale buffer, and its part of the token rows
 
   // Position (b, k) + off steps, where a column block has ksteps steps: one carry is enough to
   // tell live steps (b < the chain length) from the padded ones past the end.
@@ -295,7 +297,7 @@ struct QStream {
   __device__ __forceinline__ void compute_q4(char* const (&ring)[kD], int d, const char* sc, f32x4 (&acc)[2]) const {
     const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
     const char* src = ring[d] + wave_off + c * kCodeRowB + 4 * q;
-    const int ar = c & (kPassRows - 1);  // MFMA rows kPassRows.. repeat the pass's rows (never stored)
+    const int ar = c & (kPassRows - 1);  // FP8 passes fill all 16 MFMA rows: no padding rows
     const char* arow = ring[d] + kCodesB + ar * kARowB;
     u32x4 sv[2];  // the step's 8 scales of row c of each set
 #pragma unroll
@@ -350,7 +352,7 @@ struct QStream {
                                               f32x4 (&acc)[2]) const {
     const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
     const char* src = ring[d] + wave_off + c * kCodeRowB + 8 * (q & 1);
-    const int ar = c & (kPassRows - 1);  // MFMA rows kPassRows.. repeat the pass's rows (never stored)
+    const int ar = c & (kPassRows - 1);  // FP8 passes fill all 16 MFMA rows: no padding rows
     const char* arow = ring[d] + kCodesB + ar * kARowB;
     u32x2 wd[4][2];
     u32x4 af[4];

@@ -96,8 +96,12 @@ def philox4x32_10(counter, key):
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
-    """Exact widening of bf16 bit patterns (uint16) to float32."""
-    return (bits.astype(np.uint32) << 16).view(np.float32)
+    """Exact widening of bf16 bit patterns (uint16) to float32: the pattern becomes the upper 16 bits
+    of the float32 (little-endian, so the second uint16 of each pair), the lower 16 bits are zero."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    pairs = np.zeros(bits.shape + (2,), dtype=np.uint16)
+    pairs[..., 1] = bits
+    return pairs.view(np.float32)[..., 0]
 
 
 def host_tensor(seed: int, stream: int, index: int, shape, sigma: float, dtype: str,

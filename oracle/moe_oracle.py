@@ -200,16 +200,18 @@ def dequant_q4(codes, scales):
     """
     codes = np.asarray(codes, dtype=np.uint32)
     n, words = codes.shape
-    nib = (codes[:, :, None] >> (4 * np.arange(8, dtype=np.uint32))) & np.uint32(0xF)
-    q = nib.astype(np.int64)
-    q = np.where(q >= 8, q - 16, q).reshape(n, words * 8)
+    nib = ((codes[:, :, None] >> (4 * np.arange(8, dtype=np.uint32))) & np.uint32(0xF)).astype(np.uint8)
+    # 4-bit two's complement: fields 0..7 are 0..7, fields 8..15 are -8..-1
+    twos = np.array([0, 1, 2, 3, 4, 5, 6, 7, -8, -7, -6, -5, -4, -3, -2, -1], dtype=np.float64)
+    q = twos[nib].reshape(n, words * 8)
     sc = np.asarray(scales)
     if sc.dtype == np.uint16:
         sc = sc.view(np.float16)
     sc = sc.astype(np.float64)
     if sc.shape != (n, words * 8 // 32):
         raise ValueError("scales must be [N, K/32]")
-    return q * np.repeat(sc, 32, axis=1)
+    # group j of row r holds inputs 32j .. 32j+31, all times sc[r, j]
+    return (q.reshape(n, words * 8 // 32, 32) * sc[:, :, None]).reshape(n, words * 8)
 
 
 def e4m3_value(codes):
@@ -234,4 +236,8 @@ def dequant_fp8(codes, scales, block=128):
     sc = np.asarray(scales, dtype=np.float64)
     if n % block or k % block or sc.shape != (n // block, k // block):
         raise ValueError("scales must be [N/block, K/block]")
-    return e4m3_value(codes) * np.repeat(np.repeat(sc, block, axis=0), block, axis=1)
+    # every code's value, looked up in the 256 values e4m3_value gives; then weight (n, k) times the
+    # scale of block (n // block, k // block)
+    vals = e4m3_value(np.arange(256, dtype=np.uint8))[codes]
+    w = vals.reshape(n // block, block, k // block, block) * sc[:, None, :, None]
+    return w.reshape(n, k)

@@ -68,6 +68,72 @@ def oracle_expert(w):
     return lambda e: wl.host_expert(w, e)
 
 
+class PrefetchExperts:
+    """expert(e) for the oracle, with the weights of the next experts in ``order`` regenerated ahead on
+    a few host threads (the oracle visits experts in ascending id order; regeneration, not the
+    oracle's arithmetic, is what costs time at the full shape).  At most ``ahead`` experts are held."""
+
+    def __init__(self, fn, order, workers=4, ahead=6):
+        from concurrent.futures import ThreadPoolExecutor
+
+        self.fn = fn
+        self.order = [int(e) for e in order]
+        self.pos = {e: i for i, e in enumerate(self.order)}
+        self.pool = ThreadPoolExecutor(max_workers=workers)
+        self.ahead = ahead
+        self.pending = {}
+        self.next = 0
+
+    def _fill(self, upto):
+        while self.next < len(self.order) and self.next <= upto:
+            e = self.order[self.next]
+            self.pending[e] = self.pool.submit(self.fn, e)
+            self.next += 1
+
+    def __call__(self, e):
+        e = int(e)
+        if e not in self.pos:
+            return self.fn(e)
+        self._fill(self.pos[e] + self.ahead)
+        fut = self.pending.pop(e, None)
+        return fut.result() if fut is not None else self.fn(e)
+
+    def close(self):
+        for f in self.pending.values():
+            f.cancel()
+        self.pool.shutdown(wait=True)
+
+
+def oracle_outputs_shared_weights(cases):
+    """Oracle outputs for several workloads that share one weight set (same H, I, E, K, weight seed
+    and storage): ``cases`` = [(w, tokens, ids_gpu)], ids_gpu the GPU's ids of those tokens.  Each
+    case is routed by the oracle (near-ties re-evaluated with the GPU's ids, as in
+    ``oracle_forward_tokens``); then all rows go through one ``moe_forward_given_routing`` call
+    (rows are independent), so each expert is regenerated once.  Returns [(y, ids, wts, gap)]."""
+    xs, idss, wtss, gaps, sizes = [], [], [], [], []
+    for w, tokens, ids_gpu in cases:
+        x, ids, wts, gap, scores = oracle_route(w, tokens)
+        for t in range(len(tokens)):
+            if set(ids_gpu[t].tolist()) != set(ids[t].tolist()) and gap[t] < NEAR_TIE:
+                ids[t] = ids_gpu[t]
+                s = scores[t, ids_gpu[t]]
+                wts[t] = w.rsf * s / s.sum()
+        xs.append(x), idss.append(ids), wtss.append(wts), gaps.append(gap), sizes.append(len(tokens))
+    w0 = cases[0][0]
+    ids_all = np.concatenate(idss)
+    expert = PrefetchExperts(oracle_expert(w0), np.unique(ids_all))
+    try:
+        y = oracle.moe_forward_given_routing(np.concatenate(xs), ids_all, np.concatenate(wtss), expert,
+                                             wl.host_shared(w0))
+    finally:
+        expert.close()
+    out, a = [], 0
+    for n, ids, wts, gap in zip(sizes, idss, wtss, gaps):
+        out.append((y[a:a + n], ids, wts, gap))
+        a += n
+    return out
+
+
 def oracle_forward_tokens(w, tokens, ids_gpu=None, score_bias=None):
     """Oracle output for the given tokens.  Where ids_gpu differs from the oracle's choice on a
     near-tie, the oracle is evaluated with the GPU's ids (weights from the oracle's scores)."""
@@ -79,7 +145,11 @@ def oracle_forward_tokens(w, tokens, ids_gpu=None, score_bias=None):
                 s = scores[t, ids_gpu[t]]
                 wts[t] = w.rsf * s / s.sum()
     shared = wl.host_shared(w)
-    y = oracle.moe_forward_given_routing(x, ids, wts, oracle_expert(w), shared)
+    expert = PrefetchExperts(oracle_expert(w), np.unique(ids))
+    try:
+        y = oracle.moe_forward_given_routing(x, ids, wts, expert, shared)
+    finally:
+        expert.close()
     return y, ids, wts, gap
 
 
@@ -88,3 +158,7 @@ def oracle_forward_preassigned(w, tokens):
     x = wl.host_x_rows(w, tokens)
     return oracle.moe_forward_given_routing(x, ids[tokens], wts[tokens].astype(np.float64),
                                             lambda e: wl.host_expert(w, e), wl.host_shared(w))
+
+
+def near_tie_count(gap):
+    return int((np.asarray(gap) < NEAR_TIE).sum())

@@ -120,12 +120,13 @@ def test_fp8_rejects_f32_and_unsupported_sizes():
         assert e.value.status == moe.MOE_ERR_UNSUPPORTED
 
 
+@pytest.mark.timeout(900)
 def test_decode_fp8_full_size():
     torch = _torch()
     w = wl.WORKLOADS["decode_fp8"]
     t = wl.device_inputs(w)
     torch.cuda.synchronize()
-    y, ids, wts = _check(w, t, tokens=[0, 17, 38, 63])
+    y, ids, wts = _check(w, t)  # every token
     x, ids_ref, w_ref, gap, _ = oracle_route(w, np.arange(w.T))
     check_routing(to_np(ids), to_np(wts), ids_ref, w_ref, gap)
     del t

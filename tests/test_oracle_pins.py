@@ -297,6 +297,33 @@ def test_combine_equals_loop():
         np.testing.assert_allclose(y[t], expect, rtol=1e-14)
 
 
+@pytest.mark.parametrize("name", ["tiny", "noshared"])
+def test_combine_of_permuted_expert_rows_is_the_layer(name):
+    """[DEEP] §10.2 Steps 5-7 as the GPU path runs them: rows grouped per expert by
+    ``oracle.permute``, each row through its expert's SwiGLU, then ``oracle.combine`` with the
+    routing weights and the shared expert.  That must equal ``moe_forward_given_routing`` (which the
+    dense masked brute force above pins), so a wrong row index, a transposed pair_row, weights
+    applied by row instead of by pair, or a dropped shared term in ``combine`` fails here."""
+    w = wl.WORKLOADS["tiny"] if name == "tiny" else wl.custom("noshared", T=40, H=64, I=32, E=10, K=3,
+                                                              dtype="f32", n_shared=0)
+    x = wl.host_x(w)
+    experts = [wl.host_expert(w, e) for e in range(w.E)]
+    shared = wl.host_shared(w)
+    ids, wts, _, _ = oracle.route(x, wl.host_router(w), w.K, w.rsf)
+    offsets, row_token, pair_row = oracle.permute(ids, w.E)
+    rows = np.zeros((w.T * w.K, w.H))
+    for e in range(w.E):
+        a, b = offsets[e], offsets[e + 1]
+        if b > a:
+            rows[a:b] = oracle.swiglu_expert(x[row_token[a:b]], *experts[e])
+    shared_out = oracle.swiglu_expert(x, *shared) if shared is not None else None
+    y = oracle.combine(rows, pair_row, wts, shared_out)
+    y_ref = oracle.moe_forward_given_routing(x, ids, wts, lambda e: experts[e], shared)
+    np.testing.assert_allclose(y, y_ref, rtol=1e-12, atol=1e-14)
+    # the pairing is not trivially the identity: rows are really reordered
+    assert not np.array_equal(pair_row.ravel(), np.arange(w.T * w.K))
+
+
 # ----------------------------------------------------------------- equivariance and poison
 def test_token_permutation_and_expert_relabelling():
     x, wr, experts, shared = _random_layer(11, T=20, E=10)
