@@ -176,6 +176,26 @@ int moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_r
                 int32_t* topk_ids_out, float* topk_weights_out, void* workspace, size_t workspace_bytes,
                 void* stream);
 
+/* The whole layer, as moe_forward, with no workspace argument and no allocation: for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Scratch comes from a fixed array of MOE_NOALLOC_SCRATCH_BYTES in the library's
+ * device code, one per GPU, held until the process ends; its address is looked up on the first call
+ * on each device (the device current at the call; `stream` must belong to it).  The call allocates
+ * nothing and frees nothing.
+ *   Arguments, layouts and results: as moe_forward.
+ *   Limit: the call's workspace (moe_workspace_size(cfg, MOE_OP_FORWARD, T, 0)) must fit the array,
+ *   otherwise MOE_ERR_WORKSPACE and nothing is launched; at the K2 shape (H = 7168, I = 2048,
+ *   E = 384, K = 8, one shared expert) that is T <= 176.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one GPU (concurrent streams,
+ *   threads) race and give undefined results; calls ordered on one stream do not.  No part of the
+ *   array needs to start at zero. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_forward_noalloc(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                        const float* score_bias, const float* logit_offset, const void* w_gate,
+                        const void* w_up, const void* w_down, const void* ws_gate, const void* ws_up,
+                        const void* ws_down, void* y, int32_t* topk_ids_out, float* topk_weights_out,
+                        void* stream);
+
 /* The layer for tokens that arrive already routed (one expert-parallel rank's share:
  * [ZH-INFRA] §2.1 places 3 routed + 1 shared expert per rank at EP = 128): Steps 5-7 of
  * [DEEP] §10.2 with topk_ids [T, K] int32 and topk_weights [T, K] fp32 given.

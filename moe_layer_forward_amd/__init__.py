@@ -24,8 +24,9 @@ MOE_F32, MOE_BF16 = 0, 1
  MOE_OP_FORWARD_ROUTED, MOE_OP_FORWARD_Q4, MOE_OP_FORWARD_FP8) = range(8)
 
 EXPORTED = ("moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "moe_forward",
-            "moe_forward_routed", "moe_forward_q4", "moe_forward_fp8", "moe_last_error", "moe_profile_events",
-            "moe_profile_count", "moe_profile_kernel")
+            "moe_forward_noalloc", "moe_forward_routed", "moe_forward_q4", "moe_forward_fp8", "moe_last_error",
+            "moe_profile_events", "moe_profile_count", "moe_profile_kernel")
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20  # the fixed scratch of moe_forward_noalloc (include/moe.h)
 
 
 class MoeConfig(ctypes.Structure):
@@ -75,6 +76,7 @@ def load_library():
         lib.moe_grouped_swiglu.argtypes = [cfgp, i32, vp, i64, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
         lib.moe_combine.argtypes = [cfgp, i64, vp, i32, vp, vp, vp, vp, vp]
         lib.moe_forward.argtypes = [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.moe_forward_noalloc.argtypes = [cfgp, i64] + [vp] * 14
         lib.moe_forward_routed.argtypes = [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.moe_forward_q4.argtypes = [cfgp, i64] + [vp] * 17 + [sz, vp]
         lib.moe_forward_fp8.argtypes = [cfgp, i64] + [vp] * 17 + [sz, vp]
@@ -238,6 +240,29 @@ def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, ws_gate=None, ws_up=None
                                       _ptr(ws_up), _ptr(ws_down), _ptr(y), _ptr(ids), _ptr(wts), _ptr(ws),
                                       ws.numel(), stream))
     return (y, ids, wts) if (return_routing or routing_out is not None) else y
+
+
+def moe_forward_noalloc(cfg, x, w_router, w_gate, w_up, w_down, ws_gate=None, ws_up=None, ws_down=None,
+                        score_bias=None, logit_offset=None, out=None, routing_out=None):
+    """The whole layer with the library's fixed per-GPU scratch instead of a workspace: the C call
+    allocates nothing (with ``out`` given and ``routing_out`` for the routing, neither does this
+    wrapper).  Returns y [T, H] (and the routing tensors when routing_out is given)."""
+    import torch
+
+    T = x.shape[0]
+    dev, stream = _dev(x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, score_bias, logit_offset)
+    y = out if out is not None else torch.empty((T, cfg.hidden_size), dtype=_elem(cfg), device=dev)
+    ids = wts = None
+    if routing_out is not None:
+        ids, wts = routing_out
+        if (ids.dtype != torch.int32 or wts.dtype != torch.float32 or tuple(ids.shape) != (T, cfg.top_k)
+                or tuple(wts.shape) != (T, cfg.top_k) or not ids.is_contiguous() or not wts.is_contiguous()):
+            raise ValueError("routing_out must be contiguous (int32 [T, K], float32 [T, K]) tensors")
+    _check(load_library().moe_forward_noalloc(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(score_bias),
+                                              _ptr(logit_offset), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                              _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(y), _ptr(ids),
+                                              _ptr(wts), stream))
+    return (y, ids, wts) if routing_out is not None else y
 
 
 def moe_forward_routed(cfg, x, topk_ids, topk_weights, w_gate, w_up, w_down, ws_gate=None, ws_up=None, ws_down=None,

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
@@ -472,6 +473,39 @@ int forward_quant(const char* name, const moe_config* cfg, int64_t T, const void
   return device_status(e, "combine");
 }
 
+// ----------------------------------------------------------------------------- no-allocation forward
+// Scratch of moe_forward_noalloc: a file-scope device array that every GPU the library runs on holds
+// (its own copy, at its own address) until the process ends.  In host code `scratch` names a host
+// stand-in, not device memory: host code uses only the per-device address hipGetSymbolAddress gives.
+constexpr size_t kNoAllocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up once per device (with that device
+// current) and kept.
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "moe_forward_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_forward_noalloc: device %d beyond the %d the library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_DEVICE, "moe_forward_noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -692,6 +726,28 @@ int moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* w_r
   });
   if (e != hipSuccess) return device_status(e, "top-k");
   return run_after_routing(cfg, T, x, ids, weights, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y, w, s);
+}
+
+int moe_forward_noalloc(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                        const float* score_bias, const float* logit_offset, const void* w_gate, const void* w_up,
+                        const void* w_down, const void* ws_gate, const void* ws_up, const void* ws_down, void* y,
+                        int32_t* topk_ids_out, float* topk_weights_out, void* stream) {
+  prof_reset();
+  int st = check_config(cfg);
+  if (st) return st;
+  if ((st = check_tokens(T, cfg))) return st;
+  if (T == 0) return ok();
+  Carver cv(nullptr);
+  carve_forward(cv, cfg, T, true);
+  if (cv.used > kNoAllocScratchBytes)
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_forward_noalloc: T=%lld needs %zu bytes of scratch, above its fixed %zu bytes "
+                "(use moe_forward with a workspace)",
+                (long long)T, cv.used, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws))) return st;
+  return moe_forward(cfg, T, x, w_router, score_bias, logit_offset, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,
+                     topk_ids_out, topk_weights_out, ws, kNoAllocScratchBytes, stream);
 }
 
 int moe_forward_routed(const moe_config* cfg, int64_t T, const void* x, const int32_t* topk_ids,

@@ -43,6 +43,34 @@ def test_workspace_sizes():
     assert moe.moe_workspace_size(cfg, moe.MOE_OP_PERMUTE, 64) > 0
 
 
+def test_noalloc_scratch_limit_at_the_k2_shape():
+    """The no-allocation forward's fixed scratch holds the K2 layer's forward workspace up to T = 176
+    (the limit include/moe.h states), and its size matches the header's MOE_NOALLOC_SCRATCH_BYTES."""
+    import re
+
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == moe.MOE_NOALLOC_SCRATCH_BYTES
+    cfg = moe.make_config()
+    assert moe.moe_workspace_size(cfg, moe.MOE_OP_FORWARD, 176) <= moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert moe.moe_workspace_size(cfg, moe.MOE_OP_FORWARD, 177) > moe.MOE_NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_checks_arguments_before_any_device_call():
+    """Config errors come back synchronously from the no-allocation forward too (no GPU needed)."""
+    cfg = moe.make_config()
+    cfg.n_group = 8
+    lib = moe.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    rc = lib.moe_forward_noalloc(ctypes.byref(cfg), 64, fake, fake, None, None, fake, fake, fake, fake, fake, fake,
+                                 fake, None, None, None)
+    assert rc == moe.MOE_ERR_UNSUPPORTED and moe.moe_last_error()
+    cfg = moe.make_config()
+    rc = lib.moe_forward_noalloc(ctypes.byref(cfg), 100000, fake, fake, None, None, fake, fake, fake, fake, fake,
+                                 fake, fake, None, None, None)
+    assert rc == moe.MOE_ERR_WORKSPACE and "scratch" in moe.moe_last_error()
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("n_group", 8, moe.MOE_ERR_UNSUPPORTED),
     ("topk_group", 4, moe.MOE_ERR_UNSUPPORTED),
