@@ -7,33 +7,29 @@
 // Work item = (row tile of one group, column slab; for down with few row tiles also a K range,
 // whose fp32 partial sums a second kernel adds in K order).  Row tiles come from the device-side plan
 // (largest groups first, kTileM = 256 rows each, so a K2 expert's ~170 prefill rows are one tile
-// and every weight byte is read from HBM once).  With ~170 rows per expert the layer moves ~170
-// FLOP per weight byte, below the MI355X ridge (~310), so these kernels are weight streams first
-// and matrix-core loops second:
+// and every weight byte is read from HBM once).  A tile is up to 256 token rows x 256 weight rows
+// (gate/up: the gate and up rows of 128 h columns; down: 256 output columns), K in steps of 64.
 //
-//   * B (weights) never touches LDS.  Each wave owns 32 weight rows (output columns) and loads them
-//     straight into v_mfma_f32_16x16x32_bf16 B-operand registers: one load instruction covers 64
-//     contiguous bytes of each of 16 rows, and kDepth K steps of it are in flight per wave (a
-//     register ring).  8 waves, two per SIMD (up to 128 accumulators
-//     and the 64-register ring fit a wave's 256 registers), so one wave's MFMAs cover the other's
-//     waits.
-//   * A (token rows) is shared by the 8 waves and staged through a kStages-deep LDS ring with
-//     gfx950's direct global -> LDS loads (no register round trip).  Each stage is its own
-//     __shared__ array and every access names its stage statically (the K loop is unrolled by
-//     kStages), so the compiler can tell which LDS reads depend on which direct loads; with a
-//     single array it would make every LDS read wait for the newest direct load, i.e. for all
-//     loads in flight, weights included.  Rows are gathered straight
-//     from x through row_index, so no permuted copy of x is written.  LDS rows are unpadded;
-//     16-byte chunk c of row r sits at c ^ swz(r), so the 16 rows one 16-lane group reads land in
-//     16 different bank groups.
-//   * Every wave multiplies all rows of the tile, in 32-row steps up to the group's end: the K loop
-//     is instantiated per row count (chosen outside the loop), so padding rows cost no MFMA and
-//     the A rows past the last 32-row step are not even loaded.
-//   * One barrier per K step (LDS traffic only; the loads in flight stay in flight).
-//
-//   gate/up: wave w owns h columns n0 + 16w .. +16 of the tile's 128: column sub-tile 0 is their
-//            gate rows, sub-tile 1 their up rows, so h = SiLU(g) * u is formed in registers.
-//   down:    wave w owns 32 rows of W_down; y_rows (fp32 or bf16), times row_scale if given.
+// Both operands reach the matrix cores through LDS, loaded with gfx950's direct global -> LDS
+// loads (global_load_lds_dwordx4): one instruction moves 8 rows x 128 contiguous bytes (whole
+// cache lines).  On MI355X that form moves ~54 B/clk per CU from L2, against ~16 B/clk for loads
+// straight into MFMA operand registers (16 rows x 64 bytes per instruction, the operand layout),
+// which would spend as long on a step's 32 KiB of weights as the step's MFMAs take.
+//   * LDS: two stages of token rows (A) and three of weight rows (B), 5 x 32 KiB = 160 KiB, each
+//     stage its own __shared__ array, the K loop unrolled by 6 so every access names its stage
+//     statically (the compiler can then tell which LDS reads depend on which direct loads).  A is
+//     loaded one step ahead (it comes from L2), B two steps ahead (it streams from HBM).
+//   * 8 waves in a 2 (rows) x 4 (columns) grid; a wave owns 64 weight rows and every other 16-row
+//     block of the token rows (blocks wr, wr+2, ...), so the two wave rows split any row count
+//     evenly.  Each A fragment read from LDS feeds 4 v_mfma_f32_16x16x32_bf16 and each B fragment
+//     up to 8; accumulators stay in VGPRs (at most 128), two waves per SIMD.
+//   * LDS rows are 128 bytes, unpadded; 16-byte chunk c of row r sits at c ^ ((r >> 1) & 7), so the
+//     16 rows one 16-lane group reads fall in 16 different bank groups.  A load lane picks the
+//     global chunk that belongs in its LDS slot, so every load still reads whole row segments.
+//   * The K loop is instantiated per (16-row blocks of this wave, A loads per wave), chosen outside
+//     the loop: padding rows cost no MFMA and A rows past the group's last 16-row block are not
+//     loaded.  One barrier per K step (LDS traffic only; the loads in flight stay in flight).
+//   * Outputs leave through LDS (the free rings), as whole 16-byte chunks of contiguous rows.
 // Work items are dealt XCD-major, so the column slabs of one row tile run on the same XCD at the
 // same time and share its rows of A in that XCD's L2.
 #include <type_traits>
@@ -47,21 +43,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512, kWaves = 8;
-constexpr int kBK = 64;                                // k per step
-constexpr int kRowBytes = kBK * 2;                     // one A row of one step in LDS
-constexpr int kStages = 4;                             // LDS ring of A (one __shared__ array per stage)
-constexpr int kDepth = kStages;                        // K steps of weights in flight per wave
-constexpr int kADist = kStages - 1;                    // A is loaded this many steps ahead
-constexpr int kStageBytes = kTileM * kRowBytes;        // 32 KiB
-constexpr int kSmemBytes = kStages * kStageBytes;      // 128 KiB
-constexpr int kALoads = kStageBytes / 1024 / kWaves;   // direct-to-LDS loads per wave per step (at most)
-constexpr int kNSub = 2;                               // 16-column sub-tiles per wave
-constexpr int kBLoads = 2 * kNSub;                     // 2 k-substeps x 2 column sub-tiles
-constexpr int kLoads = kALoads + kBLoads;              // vector-memory ops per wave per step
-constexpr int kSub = kTileM / 16;                      // 16-row sub-tiles of a tile
-static_assert(kALoads * kWaves * 1024 == kStageBytes && kRowBytes == 128 && kTileM % 32 == 0, "A staging");
-static_assert(kSmemBytes <= 160 * 1024, "LDS");
-static_assert(3 * kBLoads + 2 * kALoads <= 63, "vmcnt");
+constexpr int kBK = 64;                              // k per step
+constexpr int kRowBytes = kBK * 2;                   // one row of one step in LDS
+constexpr int kTileN = 256;                          // weight rows per tile
+constexpr int kStageBytes = 256 * kRowBytes;         // 32 KiB: 256 rows of one step
+constexpr int kBLoads = kTileN * kRowBytes / 1024 / kWaves;  // B pieces (8 rows) per wave per step: 4
+constexpr int kMaxBlk = kTileM / 32;                 // 16-row blocks per wave row: 8
+static_assert(kTileM == 256 && kRowBytes == 128 && kBLoads == 4, "tile shape");
 
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
@@ -107,239 +95,192 @@ __device__ __forceinline__ bool tile_of(const TileArgs& p, int& nt, int& ks, Til
   return t.rbeg < t.rend;
 }
 
-// Operand addressing: uniform bases plus 32-bit per-lane byte offsets (operands stay below 4 GiB).
-struct Operands {
-  const char* a_base;          // A rows; lane offsets a_off[j] include the row and the LDS chunk
-  uint32_t a_off[kALoads];
-  const char* b[kNSub];        // first weight row of each 16-column sub-tile of this wave
-  uint32_t b_off;              // row (lane % 16) and 16-byte quarter (lane / 16) of a 64-byte piece
-  int skew, nk;                // step kt loads K step (kt + skew) mod nk (uniform over the work-group)
+// The two LDS rings.
+struct Rings {
+  char* a[2];
+  char* b[3];
 };
 
-// Byte offset along K of the step loaded as step kt (kt < nk).
-__device__ __forceinline__ uint32_t kbytes(const Operands& o, int kt) {
-  int ks = kt + o.skew;
-  if (ks >= o.nk) ks -= o.nk;
-  return (uint32_t)ks * kRowBytes;
-}
-
-// B fragments of one K step: [k-substep][column sub-tile].
-struct BFrag {
-  u32x4 v[2][kNSub];
+// Direct-load addressing: uniform bases plus 32-bit per-lane byte offsets (operands stay below 4 GiB);
+// a lane offset already names the row and the chunk that belongs in the lane's LDS slot.
+struct Loads {
+  const char* a_base;
+  uint32_t a_off[4];         // A pieces w, w + 8, ... (the first NAL of them are loaded)
+  const char* b_base[kBLoads];  // B piece w + 8j: its weight tensor (uniform)
+  uint32_t b_off[kBLoads];
+  int skew, nk;              // step kt loads K step (kt + skew) mod nk (uniform over the work-group)
 };
 
-__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
-
-__device__ __forceinline__ void load_b(BFrag& f, const Operands& o, uint32_t kb) {
-  const uint32_t off = o.b_off + kb;
-#pragma unroll
-  for (int s = 0; s < kNSub; ++s) {
-    f.v[0][s] = *reinterpret_cast<const u32x4*>(o.b[s] + off);
-    f.v[1][s] = *reinterpret_cast<const u32x4*>(o.b[s] + off + 64);
-  }
+__device__ __forceinline__ uint32_t kbytes(const Loads& o, int kt) {
+  int k = kt + o.skew;
+  if (k >= o.nk) k -= o.nk;
+  return (uint32_t)k * kRowBytes;
 }
 
-// A loads per wave per step when only the first 32*NP rows are multiplied.
-template <int NP>
-constexpr int a_loads() { return (4 * NP + kWaves - 1) / kWaves; }
-
-// Direct global -> LDS loads of step kt's A block: 1 KiB piece g (rows 8g .. 8g+7) is loaded by
-// wave g % kWaves; only the pieces under the first 32*NP rows are loaded.
-template <int NP>
-__device__ __forceinline__ void issue_a(const Operands& o, uint32_t kb, char* stage) {
+template <int NAL>
+__device__ __forceinline__ void issue_a(const Loads& o, int kt, char* stage) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t kb = kbytes(o, kt);
 #pragma unroll
-  for (int j = 0; j < a_loads<NP>(); ++j)
-    __builtin_amdgcn_global_load_lds(o.a_base + (o.a_off[j] + kb), stage + (j * kWaves + w) * 1024, 16, 0, 0);
+  for (int j = 0; j < NAL; ++j)
+    __builtin_amdgcn_global_load_lds(o.a_base + (o.a_off[j] + kb), stage + (w + kWaves * j) * 1024, 16, 0, 0);
 }
 
-// MFMAs of one K step over the first 2*NP 16-row sub-tiles.  acc[i][s]: rows 16i.., column
-// sub-tile s; lane l, element e holds row 16i + 4*(l/16) + e, column 16s + l%16 of this wave.
-// The A fragments of the step (2 k-substeps x 2*NP sub-tiles) are read from LDS two ahead of the
-// MFMAs that use them, in a fixed order (a scheduling barrier after each fragment's MFMAs), so
-// only three are live at a time and each read has 8 MFMAs to land behind.
-template <int NP>
-__device__ __forceinline__ void compute_step(const char* stage, const BFrag& b, f32x4 (&acc)[2 * NP][kNSub]) {
-  constexpr int kFrags = 2 * (2 * NP);
-  const int lane = threadIdx.x & 63, r16 = lane & 15, q = lane >> 4;
-  // swz(16i + r16) == swz(r16): the lane's chunk position is the same in every sub-tile
-  const char* ap0 = stage + r16 * kRowBytes + ((q ^ swz(r16)) << 4);
-  const char* ap1 = stage + r16 * kRowBytes + (((4 + q) ^ swz(r16)) << 4);
-  auto read = [&](int f) {
-    const int kk = f / (2 * NP), i = f % (2 * NP);
-    return *reinterpret_cast<const bf16x8*>((kk ? ap1 : ap0) + i * 16 * kRowBytes);
-  };
-  bf16x8 a[kFrags];
-  a[0] = read(0);
-  a[1] = read(1);
+__device__ __forceinline__ void issue_b(const Loads& o, int kt, char* stage) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t kb = kbytes(o, kt);
 #pragma unroll
-  for (int f = 0; f < kFrags; ++f) {
-    if (f + 2 < kFrags) a[f + 2] = read(f + 2);
-    const int kk = f / (2 * NP), i = f % (2 * NP);
+  for (int j = 0; j < kBLoads; ++j)
+    __builtin_amdgcn_global_load_lds(o.b_base[j] + (o.b_off[j] + kb), stage + (w + kWaves * j) * 1024, 16, 0, 0);
+}
+
+// Per-wave LDS read geometry: lane l reads row (l & 15) of a 16-row block at logical chunk
+// 4 kk + (l >> 4); the chunk's position is the same in every 16-row block.
+struct Frag {
+  uint32_t off[2];      // byte offset inside a block for k-substep kk = 0, 1
+  uint32_t a_row0;      // byte offset of this wave's first A block (blocks wr, wr + 2, ...)
+  uint32_t b_row0[4];   // byte offset of B column block s of this wave
+};
+
+// MFMAs of one K step: NBW 16-row blocks x 4 column blocks x 2 k-substeps.  acc[i][s]: lane l,
+// element e = row 16 (wr + 2i) + 4 (l >> 4) + e, column block s, column l & 15.  B fragments of a
+// k-substep are read first (4 reads feed 4 NBW MFMAs), then A fragments two ahead of their MFMAs,
+// in a fixed order (a scheduling barrier after each fragment's MFMAs).
+template <int NBW>
+__device__ __forceinline__ void compute_step(const char* As, const char* Bs, const Frag& f, f32x4 (&acc)[NBW > 0 ? NBW : 1][4]) {
+  if constexpr (NBW > 0) {
 #pragma unroll
-    for (int s = 0; s < kNSub; ++s)
-      acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[f], as_bf16x8(b.v[kk][s]), acc[i][s], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 b[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) b[s] = *reinterpret_cast<const bf16x8*>(Bs + f.b_row0[s] + f.off[kk]);
+      const char* ap = As + f.a_row0 + f.off[kk];
+      bf16x8 a[NBW];
+      a[0] = *reinterpret_cast<const bf16x8*>(ap);
+      if constexpr (NBW > 1) a[1] = *reinterpret_cast<const bf16x8*>(ap + 2 * 16 * kRowBytes);
+#pragma unroll
+      for (int i = 0; i < NBW; ++i) {
+        if (i + 2 < NBW) a[i + 2] = *reinterpret_cast<const bf16x8*>(ap + (i + 2) * 2 * 16 * kRowBytes);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[s], acc[i][s], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else {
+    (void)As;
+    (void)Bs;
+    (void)f;
+    (void)acc;
   }
 }
 
-// The A ring: stage d of step kt is array kt % kStages.
-struct Ring {
-  char* st[kStages];
-};
-
-// One K step (kt % kStages == D): wait for this wave's A block of step kt, then for every wave's
-// (barrier, which also frees the stage of step kt-1), refill that stage with step kt+kADist,
-// multiply, and refill this step's register slot with the weights of step kt+kDepth.
-// Vector-memory order per wave: ..., A(j), B(j+1), A(j+1), B(j+2), ...  so when step kt starts,
-// the operations issued after A(kt) are B(kt+1), A(kt+1), B(kt+2), A(kt+2), B(kt+3) (those that
-// exist), kBLoads or a_loads<NP>() each.
-template <int NP, int D, bool kTail>
-__device__ __forceinline__ void kstep(const Operands& o, int kt, int nk, const Ring& ring, BFrag (&b)[kDepth],
-                                      f32x4 (&acc)[2 * NP][kNSub]) {
-  constexpr int kA = a_loads<NP>();
-  const int ahead = kTail ? nk - 1 - kt : 3;
-  if (ahead >= 3)
-    wait_vmcnt<3 * kBLoads + 2 * kA>();
-  else if (ahead == 2)
-    wait_vmcnt<2 * kBLoads + 2 * kA>();
-  else if (ahead == 1)
-    wait_vmcnt<kBLoads + kA>();
+// One K step kt (kt % 6 == D): wait for this wave's loads of A(kt) and B(kt), barrier (everyone's
+// have landed; everyone is done with step kt-1's stages), load A(kt+1) into the A stage step kt-1
+// used and B(kt+2) into the B stage step kt-1 used, multiply.  Per wave the vector-memory order is
+// B(0) A(0) B(1) | A(1) B(2) | A(2) B(3) | ...: when step kt starts, only B(kt+1) (kBLoads ops, when it
+// exists) may still be in flight.
+template <int NBW, int NAL, int D, bool kTail>
+__device__ __forceinline__ void kstep(const Loads& o, int kt, int nk, const Rings& r, const Frag& f,
+                                      f32x4 (&acc)[NBW > 0 ? NBW : 1][4]) {
+  if (!kTail || kt + 1 < nk)
+    wait_vmcnt<kBLoads>();
   else
     wait_vmcnt<0>();
   block_sync_lds();
-  if (!kTail || kt + kADist < nk) issue_a<NP>(o, kbytes(o, kt + kADist), ring.st[(D + kADist) % kStages]);
-  compute_step<NP>(ring.st[D], b[D], acc);
-  if (!kTail || kt + kDepth < nk) load_b(b[D], o, kbytes(o, kt + kDepth));
+  if (!kTail || kt + 1 < nk) issue_a<NAL>(o, kt + 1, r.a[(D + 1) % 2]);
+  if (!kTail || kt + 2 < nk) issue_b(o, kt + 2, r.b[(D + 2) % 3]);
+  __builtin_amdgcn_sched_barrier(0);
+  compute_step<NBW>(r.a[D % 2], r.b[D % 3], f, acc);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int NP>
-__device__ __forceinline__ void kloop(const Operands& o, int nk, const Ring& ring, f32x4 (&acc)[2 * NP][kNSub]) {
-  static_assert(kStages == 4 && kDepth == 4 && kADist == 3, "the unrolling below");
-  BFrag b[kDepth];
-  int kt = 0;
-  if (nk >= 8) {
-    // prologue in the steady-state order B(0), A(0), B(1), A(1), B(2), A(2), B(3); unconditional,
-    // and fenced against reordering, so the compiler's own wait for B(kt) at the loop head sees the
-    // full count of later loads (a reordered prologue makes it drain every load once per 4 steps)
-#pragma unroll
-    for (int s = 0; s < kDepth; ++s) {
-      load_b(b[s], o, kbytes(o, s));
-      __builtin_amdgcn_sched_barrier(0);
-      if (s < kADist) issue_a<NP>(o, kbytes(o, s), ring.st[s]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // steady state: every refill of these four steps exists (kt + 7 < nk), no conditions
-    for (; kt + 8 <= nk; kt += 4) {
-      kstep<NP, 0, false>(o, kt, nk, ring, b, acc);
-      kstep<NP, 1, false>(o, kt + 1, nk, ring, b, acc);
-      kstep<NP, 2, false>(o, kt + 2, nk, ring, b, acc);
-      kstep<NP, 3, false>(o, kt + 3, nk, ring, b, acc);
-    }
-  } else {
-#pragma unroll
-    for (int s = 0; s < kDepth; ++s) {
-      if (s < nk) load_b(b[s], o, kbytes(o, s));
-      if (s < kADist && s < nk) issue_a<NP>(o, kbytes(o, s), ring.st[s]);
-    }
+template <int NBW, int NAL>
+__device__ __forceinline__ void kloop(const Loads& o, int nk, const Rings& r, const Frag& f,
+                                      f32x4 (&acc)[NBW > 0 ? NBW : 1][4]) {
+  // prologue in the steady state's issue order (the loads into b0, a0, b1 in that order, as the two
+  // steps before the loop head issue them), fenced against reordering: with another order the
+  // compiler's wait before the loop head's first LDS read drains every load in flight
+  issue_b(o, 0, r.b[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_a<NAL>(o, 0, r.a[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  if (nk > 1) issue_b(o, 1, r.b[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  // step 0 is peeled off: with the loop head at a step that the prologue does not lead into, the
+  // compiler's wait before the head's first LDS read no longer drains every load in flight
+  kstep<NBW, NAL, 0, true>(o, 0, nk, r, f, acc);
+  int kt = 1;
+  // steady state: every load these six steps issue exists (kt + 7 < nk)
+  for (; kt + 8 <= nk; kt += 6) {
+    kstep<NBW, NAL, 1, false>(o, kt, nk, r, f, acc);
+    kstep<NBW, NAL, 2, false>(o, kt + 1, nk, r, f, acc);
+    kstep<NBW, NAL, 3, false>(o, kt + 2, nk, r, f, acc);
+    kstep<NBW, NAL, 4, false>(o, kt + 3, nk, r, f, acc);
+    kstep<NBW, NAL, 5, false>(o, kt + 4, nk, r, f, acc);
+    kstep<NBW, NAL, 0, false>(o, kt + 5, nk, r, f, acc);
   }
-  // the last 2 to 6 steps (K is a multiple of 128, so nk is even)
-  if (kt + 4 <= nk) {
-    kstep<NP, 0, true>(o, kt, nk, ring, b, acc);
-    kstep<NP, 1, true>(o, kt + 1, nk, ring, b, acc);
-    kstep<NP, 2, true>(o, kt + 2, nk, ring, b, acc);
-    kstep<NP, 3, true>(o, kt + 3, nk, ring, b, acc);
-    kt += 4;
+  // the last 0 .. 6 steps (or all of a short loop); kt % 6 == 1 here
+  while (kt < nk) {
+    kstep<NBW, NAL, 1, true>(o, kt, nk, r, f, acc);
+    if (++kt == nk) break;
+    kstep<NBW, NAL, 2, true>(o, kt, nk, r, f, acc);
+    if (++kt == nk) break;
+    kstep<NBW, NAL, 3, true>(o, kt, nk, r, f, acc);
+    if (++kt == nk) break;
+    kstep<NBW, NAL, 4, true>(o, kt, nk, r, f, acc);
+    if (++kt == nk) break;
+    kstep<NBW, NAL, 5, true>(o, kt, nk, r, f, acc);
+    if (++kt == nk) break;
+    kstep<NBW, NAL, 0, true>(o, kt, nk, r, f, acc);
+    ++kt;
   }
-  if (kt < nk) kstep<NP, 0, true>(o, kt, nk, ring, b, acc);
-  if (kt + 1 < nk) kstep<NP, 1, true>(o, kt + 1, nk, ring, b, acc);
 }
 
-// The tile's product over the full K (a multiple of kBK) for its first 2*NP 16-row sub-tiles,
-// then the epilogue on the accumulators.
-template <int NP, class Epilogue>
-__device__ __forceinline__ void tile_body(const Operands& o, int K, const Ring& smem, const Epilogue& epilogue) {
-  f32x4 acc[2 * NP][kNSub];
+template <int NBW, int NAL, class Epilogue>
+__device__ __forceinline__ void tile_body(const Loads& o, const Rings& r, const Frag& f, const Epilogue& epilogue) {
+  f32x4 acc[NBW > 0 ? NBW : 1][4];
 #pragma unroll
-  for (int i = 0; i < 2 * NP; ++i)
+  for (int i = 0; i < (NBW > 0 ? NBW : 1); ++i)
 #pragma unroll
-    for (int s = 0; s < kNSub; ++s) acc[i][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-  kloop<NP>(o, K / kBK, smem, acc);
-  epilogue(acc);
+    for (int s = 0; s < 4; ++s) acc[i][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  kloop<NBW, NAL>(o, o.nk, r, f, acc);
+  epilogue(std::integral_constant<int, NBW>{}, acc);
 }
 
-// One instance of the whole tile body per 32-row count of the tile (1..8): the accumulators of
-// each instance are sized to its rows, and nothing is merged across instances.  Device pass
+// One instance per (16-row blocks of this wave, A loads per wave) pair that a row count of
+// 1 .. 256 produces: nblk = ceil(rows / 16) blocks, wave row wr takes ceil((nblk - wr) / 2) of them,
+// and the 2 nblk A pieces of 8 rows are spread over the 8 waves, ceil(nblk / 4) each.  Device pass
 // only: these instances are device code.
 template <class Epilogue>
-__device__ __forceinline__ void run_tile(const Operands& o, int m_valid, int K, const Ring& smem, const Epilogue& epilogue) {
-  static_assert(kSub == 16, "dispatch below covers 1..8 row pairs");
-  const int np = (m_valid + 31) / 32;
+__device__ __forceinline__ void run_tile(const Loads& o, int nblk, int wr, const Rings& r, const Frag& f,
+                                         const Epilogue& epilogue) {
+  const int nbw = (nblk - wr + 1) / 2;
+  const int nal = (nblk + 3) / 4;
 #if defined(__HIP_DEVICE_COMPILE__)
-  switch (np) {
-    case 8: tile_body<8>(o, K, smem, epilogue); break;
-    case 7: tile_body<7>(o, K, smem, epilogue); break;
-    case 6: tile_body<6>(o, K, smem, epilogue); break;
-    case 5: tile_body<5>(o, K, smem, epilogue); break;
-    case 4: tile_body<4>(o, K, smem, epilogue); break;
-    case 3: tile_body<3>(o, K, smem, epilogue); break;
-    case 2: tile_body<2>(o, K, smem, epilogue); break;
-    default: tile_body<1>(o, K, smem, epilogue); break;
-  }
+#define MOE_TILE_CASE(B, A) \
+  if (nbw == B && nal == A) return tile_body<B, A>(o, r, f, epilogue);
+  MOE_TILE_CASE(8, 4)
+  MOE_TILE_CASE(7, 4)
+  MOE_TILE_CASE(6, 4)
+  MOE_TILE_CASE(6, 3)
+  MOE_TILE_CASE(5, 3)
+  MOE_TILE_CASE(4, 3)
+  MOE_TILE_CASE(4, 2)
+  MOE_TILE_CASE(3, 2)
+  MOE_TILE_CASE(2, 2)
+  MOE_TILE_CASE(2, 1)
+  MOE_TILE_CASE(1, 1)
+  MOE_TILE_CASE(0, 1)
+#undef MOE_TILE_CASE
 #else
-  (void)np;
   (void)o;
-  (void)K;
-  (void)smem;
+  (void)r;
+  (void)f;
   (void)epilogue;
+  (void)nbw;
+  (void)nal;
 #endif
 }
-
-// Output tiles leave through LDS so that global stores are whole 16-byte chunks of contiguous rows
-// (the MFMA layout would give 2-byte stores, 32 bytes per row per instruction).  After the K loop
-// the A ring is free; a bf16 tile of kCols columns is staged there, row r in stage r / kRowsPerStage,
-// and 16-byte chunk c of row r at position c ^ out_swz(r) (the four row groups one MFMA result
-// register spans land in different banks).
-__device__ __forceinline__ int out_swz(int r) { return ((r >> 2) & 3) << 1; }
-
-template <int kCols>
-struct OutTile {
-  static constexpr int kRowB = kCols * 2;                 // bytes per staged row
-  static constexpr int kRowsPerStage = kStageBytes / kRowB;
-  static constexpr int kChunks = kRowB / 16;              // 16-byte chunks per row
-  static_assert(kRowsPerStage % 16 == 0 && kRowsPerStage * kStages >= kTileM, "staging");
-
-  // Write one bf16 value of row r (tile-relative), column col (tile-relative).  i is the 16-row
-  // sub-tile of r, so the stage index is a compile-time constant.
-  template <int I>
-  __device__ static __forceinline__ void put(const Ring& ring, int r, int col, float v) {
-    char* st = ring.st[(16 * I) / kRowsPerStage];
-    *reinterpret_cast<uint16_t*>(st + (r % kRowsPerStage) * kRowB + (((col >> 3) ^ out_swz(r)) << 4) +
-                                 (col & 7) * 2) = f32_to_bf16(v);
-  }
-
-  // Store rows [0, m_valid) of the staged tile to out[(rbeg + r) * ld + col0 + c], columns below
-  // col_end only; every thread of the work-group takes part.
-  __device__ static __forceinline__ void store(const Ring& ring, int m_valid, uint16_t* out, int64_t ld,
-                                               int64_t rbeg, int col0, int col_end) {
-    constexpr int kPerThread = kRowsPerStage * kChunks / kThreads;
-    static_assert(kPerThread * kThreads == kRowsPerStage * kChunks, "chunks per thread");
-#pragma unroll
-    for (int st = 0; st < kStages; ++st) {
-      if (st * kRowsPerStage >= m_valid) break;
-#pragma unroll
-      for (int j = 0; j < kPerThread; ++j) {
-        const int ch = j * kThreads + threadIdx.x;
-        const int rl = ch / kChunks, c = ch % kChunks;
-        const int r = st * kRowsPerStage + rl;
-        if (r < m_valid && col0 + 8 * c < col_end) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(ring.st[st] + rl * kRowB + ((c ^ out_swz(r)) << 4));
-          *reinterpret_cast<u32x4*>(out + (rbeg + r) * ld + col0 + 8 * c) = v;
-        }
-      }
-    }
-  }
-};
 
 // Compile-time loop helper: f(integral_constant<int, I>) for I = 0 .. N-1.
 template <int N, int I = 0, class F>
@@ -350,131 +291,204 @@ __device__ __forceinline__ void static_for(const F& f) {
   }
 }
 
-// Lane offsets of the A loads: row rl of the tile is source row src(rl) of a [*, K] matrix.
+// Output tiles leave through LDS so that global stores are whole 16-byte chunks of contiguous rows.
+// A bf16 tile of kCols columns is staged over the free ring arrays in order (a0, a1, b0, b1, b2),
+// kRowsPer rows each; 16-byte chunk c of row r at position c ^ out_swz(r).
+__device__ __forceinline__ int out_swz(int r) { return ((r >> 2) & 3) << 1; }
+
+template <int kCols>
+struct OutTile {
+  static constexpr int kRowB = kCols * 2;
+  static constexpr int kRowsPer = kStageBytes / kRowB;
+  static constexpr int kChunks = kRowB / 16;
+  static_assert(kRowsPer % 16 == 0 && kRowsPer * 5 >= kTileM, "staging");
+
+  __device__ static __forceinline__ char* stage(const Rings& r, int i) {
+    return i == 0 ? r.a[0] : i == 1 ? r.a[1] : i == 2 ? r.b[0] : i == 3 ? r.b[1] : r.b[2];
+  }
+  __device__ static __forceinline__ void put(const Rings& r, int row, int col, float v) {
+    char* st = stage(r, row / kRowsPer);
+    *reinterpret_cast<uint16_t*>(st + (row % kRowsPer) * kRowB + (((col >> 3) ^ out_swz(row)) << 4) + (col & 7) * 2) =
+        f32_to_bf16(v);
+  }
+  // rows [0, m_valid) of the staged tile -> out[(rbeg + r) * ld + col0 + ...], columns below col_end
+  __device__ static __forceinline__ void store(const Rings& r, int m_valid, uint16_t* out, int64_t ld, int64_t rbeg,
+                                               int col0, int col_end) {
+    const int n = m_valid * kChunks;
+    for (int ch = threadIdx.x; ch < n; ch += kThreads) {
+      const int row = ch / kChunks, c = ch % kChunks;
+      if (col0 + 8 * c >= col_end) continue;
+      const char* st = stage(r, row / kRowsPer);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + (row % kRowsPer) * kRowB + ((c ^ out_swz(row)) << 4));
+      *reinterpret_cast<u32x4*>(out + (rbeg + row) * ld + col0 + 8 * c) = v;
+    }
+  }
+};
+
+// Lane offsets of this wave's A pieces: piece p = w + 8 j holds tile rows 8p .. 8p + 7; row rl of the
+// tile is source row src(rl) of a [*, K] matrix.
 template <class RowOf>
-__device__ __forceinline__ void a_offsets(Operands& o, int K, RowOf row_of) {
+__device__ __forceinline__ void a_offsets(Loads& o, int K, RowOf row_of) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-  for (int j = 0; j < kALoads; ++j) {
-    const int rl = (j * kWaves + w) * 8 + (lane >> 3);  // 8 rows of 128 bytes per 1 KiB load
-    const int chunk = (lane & 7) ^ swz(rl);              // the chunk that belongs in this lane's slot
+  for (int j = 0; j < 4; ++j) {
+    const int rl = (w + kWaves * j) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(rl);  // the chunk that belongs in this lane's LDS slot
     o.a_off[j] = (uint32_t)((row_of(rl) * K + 8 * chunk) * 2);
   }
 }
 
+// Lane offset of B piece j (tile rows 8p .. 8p + 7, p = w + 8 j) inside its weight tensor, whose row
+// rl sits at weight row wrow(rl) (rows K elements long).
+__device__ __forceinline__ uint32_t b_offset(int j, int64_t wrow, int K) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rl = (w + kWaves * j) * 8 + (lane >> 3);
+  const int chunk = (lane & 7) ^ swz(rl);
+  return (uint32_t)((wrow * K + 8 * chunk) * 2);
+}
+
+__device__ __forceinline__ Frag make_frag(int wr, const int (&b_rows)[4]) {
+  const int lane = threadIdx.x & 63, x = lane & 15, g = lane >> 4;
+  Frag f;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) f.off[kk] = (uint32_t)(x * kRowBytes + (((4 * kk + g) ^ swz(x)) << 4));
+  f.a_row0 = (uint32_t)(wr * 16 * kRowBytes);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) f.b_row0[s] = (uint32_t)(b_rows[s] * kRowBytes);
+  return f;
+}
+
+#define MOE_TILE_SMEM                                                                                          \
+  __shared__ __align__(16) char a0_[kStageBytes], a1_[kStageBytes], b0_[kStageBytes], b1_[kStageBytes], \
+      b2_[kStageBytes];                                                                                        \
+  const Rings rings{{a0_, a1_}, {b0_, b1_, b2_}};
+
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gateup_tile_kernel(TileArgs p) {
-  __shared__ __align__(16) char a0[kStageBytes], a1[kStageBytes], a2[kStageBytes], a3[kStageBytes];
-  const Ring smem{{a0, a1, a2, a3}};
+  MOE_TILE_SMEM
   int nt, ks;
   TileRows t;
   if (!tile_of(p, nt, ks, t)) return;
   const int H = p.H, I = p.I;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = w >> 2, wc = w & 3;  // wave row (token-row blocks wr, wr + 2, ...), wave column
   const bool sh = t.g == p.w.shared_group;
   const uint16_t* wg = sh ? (const uint16_t*)p.w.s_gate : (const uint16_t*)p.w.gate + (int64_t)t.g * I * H;
   const uint16_t* wu = sh ? (const uint16_t*)p.w.s_up : (const uint16_t*)p.w.up + (int64_t)t.g * I * H;
-  const int c0 = nt * 128 + 16 * w;  // first h column of this wave
+  const int h0 = nt * 128;  // first h column of the tile; B tile rows 0-127 gate, 128-255 up
 
-  Operands o;
+  Loads o;
   o.a_base = reinterpret_cast<const char*>(p.a);
   a_offsets(o, H, [&](int rl) -> int64_t {
     const int64_t r = t.rbeg + rl;
     const int64_t rr = r < t.rend ? r : t.rbeg;  // rows past the group end re-read its first row
     return p.row_index ? (int64_t)p.row_index[rr] : rr;
   });
-  o.b[0] = reinterpret_cast<const char*>(wg + (int64_t)c0 * H);  // gate rows of the wave's 16 columns
-  o.b[1] = reinterpret_cast<const char*>(wu + (int64_t)c0 * H);  // their up rows
-  o.b_off = (uint32_t)((lane & 15) * H * 2 + 16 * (lane >> 4));
+#pragma unroll
+  for (int j = 0; j < kBLoads; ++j) {  // pieces w, w + 8 are gate rows, w + 16, w + 24 up rows
+    const int rl = (w + kWaves * j) * 8 + (lane >> 3);
+    o.b_base[j] = reinterpret_cast<const char*>(j < 2 ? wg : wu);
+    o.b_off[j] = b_offset(j, h0 + (rl & 127), H);
+  }
   o.nk = H / kBK;
   o.skew = 0;  // 14,336-byte rows (K2) spread over the channels on their own
 
+  // wave column wc: gate rows 32 wc .. +32 (blocks 0, 1) and the up rows of the same h columns
+  const int b_rows[4] = {32 * wc, 32 * wc + 16, 128 + 32 * wc, 128 + 32 * wc + 16};
+  const Frag f = make_frag(wr, b_rows);
   uint16_t* h = static_cast<uint16_t*>(p.out);
   const int64_t rbeg = t.rbeg;
   const int m_valid = (int)(t.rend - t.rbeg);
-  run_tile(o, m_valid, H, smem, [&](const auto& acc) {
-    constexpr int n16 = sizeof(acc) / sizeof(acc[0]);
+  run_tile(o, (m_valid + 15) / 16, wr, rings, f, [&](auto nbw_c, const auto& acc) {
+    constexpr int NBW = decltype(nbw_c)::value;
     using Out = OutTile<128>;
-    block_sync_lds();  // every wave is done reading the A ring
-    static_for<n16>([&](auto ic) {
+    block_sync_lds();  // every wave is done reading the rings
+    static_for<NBW>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        Out::put<i>(smem, 16 * i + 4 * (lane >> 4) + e, 16 * w + (lane & 15),
-                    swiglu_f32(acc[i][0][e], acc[i][1][e]));
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * (wr + 2 * i) + 4 * (lane >> 4) + e;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          Out::put(rings, row, 32 * wc + 16 * s + (lane & 15), swiglu_f32(acc[i][s][e], acc[i][s + 2][e]));
+      }
     });
     block_sync_lds();
-    Out::store(smem, m_valid, h, I, rbeg, nt * 128, I);
+    Out::store(rings, m_valid, h, I, rbeg, h0, I);
   });
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void down_tile_kernel(TileArgs p) {
-  __shared__ __align__(16) char a0[kStageBytes], a1[kStageBytes], a2[kStageBytes], a3[kStageBytes];
-  const Ring smem{{a0, a1, a2, a3}};
+  MOE_TILE_SMEM
   int nt, ks;
   TileRows t;
   if (!tile_of(p, nt, ks, t)) return;
   const int H = p.H, I = p.I;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = w >> 2, wc = w & 3;
   const uint16_t* wd = t.g == p.w.shared_group ? (const uint16_t*)p.w.s_down
                                                 : (const uint16_t*)p.w.down + (int64_t)t.g * H * I;
-  const int c0 = nt * 256 + 32 * w;  // first output column of this wave (H is a multiple of 32)
-  const bool cols_ok = c0 < H;       // the last slab of an H that is not a multiple of 256
+  const int n0 = nt * 256;  // first output column of the tile
 
   // this item's K range [k0, k0 + kc) of the h rows and of W_down's rows
   const int kc = I / p.n_ksplit, k0 = ks * kc;
-  Operands o;
+  Loads o;
   o.a_base = reinterpret_cast<const char*>(p.a + k0);
   a_offsets(o, I, [&](int rl) -> int64_t {
     const int64_t r = t.rbeg + rl;
     return r < t.rend ? r : t.rbeg;
   });
 #pragma unroll
-  for (int s = 0; s < kNSub; ++s)  // idle waves re-read the first rows
-    o.b[s] = reinterpret_cast<const char*>(wd + (int64_t)((cols_ok ? c0 : 0) + 16 * s) * I + k0);
-  o.b_off = (uint32_t)((lane & 15) * I * 2 + 16 * (lane >> 4));
+  for (int j = 0; j < kBLoads; ++j) {  // output columns past H (the last slab of an H that is not a
+    const int rl = (w + kWaves * j) * 8 + (lane >> 3);  // multiple of 256) re-read row n0, never stored
+    o.b_base[j] = reinterpret_cast<const char*>(wd + k0);
+    o.b_off[j] = b_offset(j, n0 + rl < H ? n0 + rl : n0, I);
+  }
   // W_down rows a multiple of 4 KiB apart put the same K step of all 256 rows on few HBM channels:
   // the column slabs then start their K loops at different steps (and wrap around).  Only while the
   // tile's h block is small (I <= 4096: at most 2 MiB): the slabs of a tile share it through L2 only
-  // while they walk K together (the dense layer's I = 18432 measured 7% slower with the skew).
+  // while they walk K together.
   o.nk = kc / kBK;
   o.skew = (I * 2) % 4096 == 0 && I <= 4096 ? nt * 5 % o.nk : 0;
 
+  const int b_rows[4] = {64 * wc, 64 * wc + 16, 64 * wc + 32, 64 * wc + 48};
+  const Frag f = make_frag(wr, b_rows);
   const int64_t rbeg = t.rbeg, rend = t.rend;
   const int m_valid = (int)(rend - rbeg);
   const float* row_scale = p.row_scale;
   const bool split = p.n_ksplit > 1;
   void* out = split ? static_cast<void*>(p.part + (int64_t)ks * p.max_rows * H) : p.out;
-  run_tile(o, m_valid, kc, smem, [&](const auto& acc) {
-    constexpr int n16 = sizeof(acc) / sizeof(acc[0]);
+  run_tile(o, (m_valid + 15) / 16, wr, rings, f, [&](auto nbw_c, const auto& acc) {
+    constexpr int NBW = decltype(nbw_c)::value;
     if (p.out_bf16 && !split) {
       using Out = OutTile<256>;
-      block_sync_lds();  // every wave is done reading the A ring
-      static_for<n16>([&](auto ic) {
+      block_sync_lds();  // every wave is done reading the rings
+      static_for<NBW>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 16 * i + 4 * (lane >> 4) + e;
-          const float sc = row_scale && r < m_valid ? row_scale[rbeg + r] : 1.f;
+          const int row = 16 * (wr + 2 * i) + 4 * (lane >> 4) + e;
+          const float sc = row_scale && row < m_valid ? row_scale[rbeg + row] : 1.f;
 #pragma unroll
-          for (int s = 0; s < kNSub; ++s) Out::put<i>(smem, r, 32 * w + 16 * s + (lane & 15), acc[i][s][e] * sc);
+          for (int s = 0; s < 4; ++s) Out::put(rings, row, 64 * wc + 16 * s + (lane & 15), acc[i][s][e] * sc);
         }
       });
       block_sync_lds();
-      Out::store(smem, m_valid, static_cast<uint16_t*>(out), H, rbeg, nt * 256, H);
+      Out::store(rings, m_valid, static_cast<uint16_t*>(out), H, rbeg, n0, H);
       return;
     }
     // fp32 rows (a caller's choice in moe_grouped_swiglu, or a K range's partial sums): direct stores
-    if (!cols_ok) return;
 #pragma unroll
-    for (int i = 0; i < n16; ++i)
+    for (int i = 0; i < NBW; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t r = rbeg + 16 * i + 4 * (lane >> 4) + e;
+        const int64_t r = rbeg + 16 * (wr + 2 * i) + 4 * (lane >> 4) + e;
         if (r >= rend) continue;
         const float sc = row_scale ? row_scale[r] : 1.f;
 #pragma unroll
-        for (int s = 0; s < kNSub; ++s)
-          static_cast<float*>(out)[r * H + c0 + 16 * s + (lane & 15)] = acc[i][s][e] * sc;
+        for (int s = 0; s < 4; ++s) {
+          const int col = n0 + 64 * wc + 16 * s + (lane & 15);
+          if (col < H) static_cast<float*>(out)[r * H + col] = acc[i][s][e] * sc;
+        }
       }
   });
 }
@@ -538,16 +552,15 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(const float* __restr
 constexpr int kCUs = 256;  // MI355X compute units; one tile work-group per CU
 
 // K ranges per work item for a launch of `items` items over nk K steps: with fewer items than CUs,
-// the divisor s of nk (s <= 16, an even number of at least 4 steps per range, as the K loop's tail
-// expects) with the smallest ceil(items * s / CUs) / s, i.e. the fewest rounds of work per range,
-// each range's partial sums (part_frac of an item's weight bytes, written and read back once)
-// counted against it.
+// the divisor s of nk (s <= 16, at least 4 steps per range) with the smallest ceil(items * s / CUs) / s,
+// i.e. the fewest rounds of work per range, each range's partial sums (part_frac of an item's weight
+// bytes, written and read back once) counted against it.
 int tile_ksplit(int64_t items, int nk, double part_frac) {
   if (items <= 0 || items >= kCUs) return 1;
   int best = 1;
   double best_cost = 1.0;
   for (int sp = 2; sp <= 16; ++sp) {
-    if (nk % sp || nk / sp < 4 || (nk / sp) % 2) continue;
+    if (nk % sp || nk / sp < 4) continue;
     const int64_t rounds = (items * sp + kCUs - 1) / kCUs;
     const double cost = (double)rounds / sp * (1.0 + sp * part_frac);
     if (cost < best_cost - 1e-9) {
