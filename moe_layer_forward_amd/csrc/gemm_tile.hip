@@ -11,7 +11,7 @@
 // (gate/up: the gate and up rows of 128 h columns; down: 256 output columns), K in steps of 64.
 //
 // Both operands reach the matrix cores through LDS, loaded with gfx950's direct global -> LDS
-// loads (global_load_lds_dwordx4): one instruction moves 8 rows x 128 contiguous bytes (whole
+// loads (buffer_load_dwordx4 ... lds): one instruction moves 8 rows x 128 contiguous bytes (whole
 // cache lines).  On MI355X that form moves ~54 B/clk per CU from L2, against ~16 B/clk for loads
 // straight into MFMA operand registers (16 rows x 64 bytes per instruction, the operand layout),
 // which would spend as long on a step's 32 KiB of weights as the step's MFMAs take.
@@ -111,6 +111,17 @@ struct Loads {
   int skew, nk;              // step kt loads K step (kt + skew) mod nk (uniform over the work-group)
 };
 
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef __attribute__((address_space(3))) void* LdsPtr;
+
+// Buffer descriptor over an operand (a uniform base; the byte offsets stay below 4 GiB).  The direct
+// loads go through buffer descriptors rather than global addresses: the compiler counts a
+// global -> LDS load as possibly touching LDS through the flat path as well, and then waits for every
+// LDS read in flight (lgkmcnt(0)) wherever it needs one of them.
+__device__ __forceinline__ Rsrc operand_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xffffffffu, 0x00020000);
+}
+
 __device__ __forceinline__ uint32_t kbytes(const Loads& o, int kt) {
   int k = kt + o.skew;
   if (k >= o.nk) k -= o.nk;
@@ -121,9 +132,11 @@ template <int NAL>
 __device__ __forceinline__ void issue_a(const Loads& o, int kt, char* stage) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t kb = kbytes(o, kt);
+  const Rsrc rs = operand_rsrc(o.a_base);
 #pragma unroll
   for (int j = 0; j < NAL; ++j)
-    __builtin_amdgcn_global_load_lds(o.a_base + (o.a_off[j] + kb), stage + (w + kWaves * j) * 1024, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LdsPtr)(stage + (w + kWaves * j) * 1024), 16, o.a_off[j] + kb, 0, 0,
+                                             0);
 }
 
 __device__ __forceinline__ void issue_b(const Loads& o, int kt, char* stage) {
@@ -131,7 +144,8 @@ __device__ __forceinline__ void issue_b(const Loads& o, int kt, char* stage) {
   const uint32_t kb = kbytes(o, kt);
 #pragma unroll
   for (int j = 0; j < kBLoads; ++j)
-    __builtin_amdgcn_global_load_lds(o.b_base[j] + (o.b_off[j] + kb), stage + (w + kWaves * j) * 1024, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(operand_rsrc(o.b_base[j]), (LdsPtr)(stage + (w + kWaves * j) * 1024), 16,
+                                             o.b_off[j] + kb, 0, 0, 0);
 }
 
 // Per-wave LDS read geometry: lane l reads row (l & 15) of a 16-row block at logical chunk
@@ -142,29 +156,37 @@ struct Frag {
   uint32_t b_row0[4];   // byte offset of B column block s of this wave
 };
 
-// MFMAs of one K step: NBW 16-row blocks x 4 column blocks x 2 k-substeps.  acc[i][s]: lane l,
-// element e = row 16 (wr + 2i) + 4 (l >> 4) + e, column block s, column l & 15.  B fragments of a
-// k-substep are read first (4 reads feed 4 NBW MFMAs), then A fragments two ahead of their MFMAs,
-// in a fixed order (a scheduling barrier after each fragment's MFMAs).
+// MFMAs of one K step: NBW 16-row blocks x 4 column blocks x 2 k-substeps, as one sequence of 2 NBW
+// fragments (fragment fi: k-substep fi / NBW, row block fi % NBW).  acc[i][s]: lane l, element e =
+// row 16 (wr + 2i) + 4 (l >> 4) + e, column block s, column l & 15.  Each A fragment is read from LDS
+// two fragments ahead of its MFMAs and the second k-substep's 4 B fragments two fragments before
+// that substep starts, in a fixed order (a scheduling barrier after each fragment's MFMAs), so each
+// LDS read has 8 MFMAs to land behind.
 template <int NBW>
 __device__ __forceinline__ void compute_step(const char* As, const char* Bs, const Frag& f, f32x4 (&acc)[NBW > 0 ? NBW : 1][4]) {
   if constexpr (NBW > 0) {
+    constexpr int NF = 2 * NBW;
+    constexpr int kB1 = NBW >= 2 ? NBW - 2 : 0;  // fragment before whose MFMAs the second B set is read
+    auto read_a = [&](int fi) {
+      return *reinterpret_cast<const bf16x8*>(As + f.a_row0 + f.off[fi / NBW] + (fi % NBW) * 2 * 16 * kRowBytes);
+    };
+    bf16x8 b[2][4];
+    bf16x8 a[NF];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 b[4];
+    for (int s = 0; s < 4; ++s) b[0][s] = *reinterpret_cast<const bf16x8*>(Bs + f.b_row0[s] + f.off[0]);
+    a[0] = read_a(0);
+    a[1] = read_a(1);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) b[s] = *reinterpret_cast<const bf16x8*>(Bs + f.b_row0[s] + f.off[kk]);
-      const char* ap = As + f.a_row0 + f.off[kk];
-      bf16x8 a[NBW];
-      a[0] = *reinterpret_cast<const bf16x8*>(ap);
-      if constexpr (NBW > 1) a[1] = *reinterpret_cast<const bf16x8*>(ap + 2 * 16 * kRowBytes);
+    for (int fi = 0; fi < NF; ++fi) {
+      if (fi + 2 < NF) a[fi + 2] = read_a(fi + 2);
+      if (fi == kB1) {
 #pragma unroll
-      for (int i = 0; i < NBW; ++i) {
-        if (i + 2 < NBW) a[i + 2] = *reinterpret_cast<const bf16x8*>(ap + (i + 2) * 2 * 16 * kRowBytes);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[s], acc[i][s], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int s = 0; s < 4; ++s) b[1][s] = *reinterpret_cast<const bf16x8*>(Bs + f.b_row0[s] + f.off[1]);
       }
+      const int kk = fi / NBW, i = fi % NBW;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fi], b[kk][s], acc[i][s], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
     (void)As;
