@@ -30,8 +30,8 @@
 //     the loop: padding rows cost no MFMA and A rows past the group's last 16-row block are not
 //     loaded.  One barrier per K step (LDS traffic only; the loads in flight stay in flight).
 //   * Outputs leave through LDS (the free rings), as whole 16-byte chunks of contiguous rows.
-// Work items are dealt XCD-major, so the column slabs of one row tile run on the same XCD at the
-// same time and share its rows of A in that XCD's L2.
+// Row tiles are dealt round-robin to the XCDs; the column slabs of one row tile run on the same XCD at
+// the same time and share its rows of A in that XCD's L2.
 #include <type_traits>
 
 #include "tile_core.h"
@@ -74,14 +74,18 @@ struct TileRows {
   int64_t rbeg, rend;
 };
 
-// Work item -> (row tile, column slab nt, K range ks); consecutive items (one XCD's share) walk the
-// slabs and K ranges of one row tile.
+// Work-group -> (row tile, column slab nt, K range ks).  The hardware hands work-group b to XCD b % 8;
+// row tiles are dealt to the XCDs round-robin (tile t to XCD t % 8, from the plan's largest-first
+// list, so every XCD gets the same mix of large and small groups), and each XCD walks the slabs and
+// K ranges of one row tile after another, so the work-groups sharing a tile's rows of A run on one
+// XCD together and share them in its L2.
 __device__ __forceinline__ bool tile_of(const TileArgs& p, int& nt, int& ks, TileRows& t) {
-  int64_t L;
   const int per_tile = p.n_ntiles * p.n_ksplit;
-  if (!xcd_work_item((int64_t)p.counters[1] * per_tile, L)) return false;
-  const int tile = (int)(L / per_tile);
-  const int rem = (int)(L % per_tile);
+  const int64_t b = blockIdx.x, local = b / kXcds;
+  const int64_t tile64 = (local / per_tile) * kXcds + b % kXcds;
+  if (tile64 >= p.counters[1]) return false;
+  const int tile = (int)tile64;
+  const int rem = (int)(local % per_tile);
   nt = rem / p.n_ksplit;
   ks = rem % p.n_ksplit;
   t.g = p.tiles[2 * tile];
@@ -515,10 +519,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   });
 }
 
+// Work-groups for up to max_tiles row tiles dealt round-robin to the XCDs: ceil(max_tiles / 8) tiles
+// per XCD, each n_ntiles * n_ksplit work-groups.
 unsigned grid_for(int64_t max_tiles, int n_ntiles, int n_ksplit = 1) {
-  int64_t n = max_tiles * n_ntiles * n_ksplit;
-  n = (n + kXcds - 1) / kXcds * kXcds;
-  return (unsigned)n;
+  const int64_t per_xcd = (max_tiles + kXcds - 1) / kXcds;
+  return (unsigned)(per_xcd * n_ntiles * n_ksplit * kXcds);
 }
 
 // Whether row r belongs to a group of the tile list, i.e. of more than stream_rows rows counted as
