@@ -76,16 +76,39 @@ struct TileRows {
 
 // Work-group -> (row tile, column slab nt, K range ks).  The hardware hands work-group b to XCD b % 8;
 // row tiles are dealt to the XCDs round-robin (tile t to XCD t % 8, from the plan's largest-first
-// list, so every XCD gets the same mix of large and small groups), and each XCD walks the slabs and
-// K ranges of one row tile after another, so the work-groups sharing a tile's rows of A run on one
-// XCD together and share them in its L2.
+// list, so every XCD gets the same mix of large and small groups).  An XCD takes its tiles in blocks
+// of kGroupTiles: a block of tiles of one group (a group of many rows) runs slab by slab, its tiles
+// side by side, so the work-groups reading a weight slab run together and share it in the XCD's L2
+// (instead of the slab being streamed again for every row tile); any other block runs tile by tile,
+// a tile's slabs side by side, sharing the tile's token rows in L2.
+constexpr int kGroupTiles = 4;
+
 __device__ __forceinline__ bool tile_of(const TileArgs& p, int& nt, int& ks, TileRows& t) {
   const int per_tile = p.n_ntiles * p.n_ksplit;
-  const int64_t b = blockIdx.x, local = b / kXcds;
-  const int64_t tile64 = (local / per_tile) * kXcds + b % kXcds;
-  if (tile64 >= p.counters[1]) return false;
+  const int64_t b = blockIdx.x, local = b / kXcds, x = b % kXcds;
+  const int64_t n_tiles = p.counters[1];
+  const int64_t blk = local / ((int64_t)kGroupTiles * per_tile);  // block of this XCD's tiles
+  const int q = (int)(local % ((int64_t)kGroupTiles * per_tile));
+  const int64_t j0 = blk * kGroupTiles;                            // first tile of the block, XCD-local
+  int in_blk = 0;                                                  // tiles of this XCD in the block
+  bool one_group = true;
+  for (int i = 0; i < kGroupTiles; ++i) {
+    const int64_t ti = (j0 + i) * kXcds + x;
+    if (ti >= n_tiles) break;
+    ++in_blk;
+    if (p.tiles[2 * ti] != p.tiles[2 * (j0 * kXcds + x)]) one_group = false;
+  }
+  int j, rem;
+  if (one_group && in_blk == kGroupTiles) {
+    j = q % kGroupTiles;
+    rem = q / kGroupTiles;
+  } else {
+    j = q / per_tile;
+    rem = q % per_tile;
+  }
+  const int64_t tile64 = (j0 + j) * kXcds + x;
+  if (j >= in_blk || tile64 >= n_tiles) return false;
   const int tile = (int)tile64;
-  const int rem = (int)(local % per_tile);
   nt = rem / p.n_ksplit;
   ks = rem % p.n_ksplit;
   t.g = p.tiles[2 * tile];
@@ -520,10 +543,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 // Work-groups for up to max_tiles row tiles dealt round-robin to the XCDs: ceil(max_tiles / 8) tiles
-// per XCD, each n_ntiles * n_ksplit work-groups.
+// per XCD in blocks of kGroupTiles, each tile n_ntiles * n_ksplit work-groups.
 unsigned grid_for(int64_t max_tiles, int n_ntiles, int n_ksplit = 1) {
   const int64_t per_xcd = (max_tiles + kXcds - 1) / kXcds;
-  return (unsigned)(per_xcd * n_ntiles * n_ksplit * kXcds);
+  const int64_t blocks = (per_xcd + kGroupTiles - 1) / kGroupTiles;
+  return (unsigned)(blocks * kGroupTiles * n_ntiles * n_ksplit * kXcds);
 }
 
 // Whether row r belongs to a group of the tile list, i.e. of more than stream_rows rows counted as
