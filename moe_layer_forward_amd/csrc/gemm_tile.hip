@@ -80,34 +80,49 @@ struct TileRows {
 // of kGroupTiles: a block of tiles of one group (a group of many rows) runs slab by slab, its tiles
 // side by side, so the work-groups reading a weight slab run together and share it in the XCD's L2
 // (instead of the slab being streamed again for every row tile); any other block runs tile by tile,
-// a tile's slabs side by side, sharing the tile's token rows in L2.
+// a tile's slabs side by side, sharing the tile's token rows in L2.  With fewer tiles than XCDs the
+// tiles' items are spread over all XCDs instead.
 constexpr int kGroupTiles = 4;
 
 __device__ __forceinline__ bool tile_of(const TileArgs& p, int& nt, int& ks, TileRows& t) {
   const int per_tile = p.n_ntiles * p.n_ksplit;
   const int64_t b = blockIdx.x, local = b / kXcds, x = b % kXcds;
   const int64_t n_tiles = p.counters[1];
-  const int64_t blk = local / ((int64_t)kGroupTiles * per_tile);  // block of this XCD's tiles
-  const int q = (int)(local % ((int64_t)kGroupTiles * per_tile));
-  const int64_t j0 = blk * kGroupTiles;                            // first tile of the block, XCD-local
-  int in_blk = 0;                                                  // tiles of this XCD in the block
-  bool one_group = true;
-  for (int i = 0; i < kGroupTiles; ++i) {
-    const int64_t ti = (j0 + i) * kXcds + x;
-    if (ti >= n_tiles) break;
-    ++in_blk;
-    if (p.tiles[2 * ti] != p.tiles[2 * (j0 * kXcds + x)]) one_group = false;
-  }
-  int j, rem;
-  if (one_group && in_blk == kGroupTiles) {
-    j = q % kGroupTiles;
-    rem = q / kGroupTiles;
+  int64_t tile64;
+  int rem;
+  if (n_tiles < kXcds) {
+    // fewer row tiles than XCDs: each tile's items are cut into c chunks dealt round-robin, so that
+    // every XCD has work (unit u = chunk u % c of tile u / c goes to XCD u % 8)
+    if (n_tiles <= 0) return false;
+    const int c = (int)((kXcds + n_tiles - 1) / n_tiles) < per_tile ? (int)((kXcds + n_tiles - 1) / n_tiles) : per_tile;
+    const int cs = (per_tile + c - 1) / c;
+    const int64_t u = (local / cs) * kXcds + x;
+    rem = (int)((u % c) * cs + local % cs);
+    tile64 = u / c;
+    if (tile64 >= n_tiles || rem >= per_tile) return false;
   } else {
-    j = q / per_tile;
-    rem = q % per_tile;
+    const int64_t blk = local / ((int64_t)kGroupTiles * per_tile);  // block of this XCD's tiles
+    const int q = (int)(local % ((int64_t)kGroupTiles * per_tile));
+    const int64_t j0 = blk * kGroupTiles;                            // first tile of the block, XCD-local
+    int in_blk = 0;                                                  // tiles of this XCD in the block
+    bool one_group = true;
+    for (int i = 0; i < kGroupTiles; ++i) {
+      const int64_t ti = (j0 + i) * kXcds + x;
+      if (ti >= n_tiles) break;
+      ++in_blk;
+      if (p.tiles[2 * ti] != p.tiles[2 * (j0 * kXcds + x)]) one_group = false;
+    }
+    int j;
+    if (one_group && in_blk == kGroupTiles) {
+      j = q % kGroupTiles;
+      rem = q / kGroupTiles;
+    } else {
+      j = q / per_tile;
+      rem = q % per_tile;
+    }
+    tile64 = (j0 + j) * kXcds + x;
+    if (j >= in_blk || tile64 >= n_tiles) return false;
   }
-  const int64_t tile64 = (j0 + j) * kXcds + x;
-  if (j >= in_blk || tile64 >= n_tiles) return false;
   const int tile = (int)tile64;
   nt = rem / p.n_ksplit;
   ks = rem % p.n_ksplit;
@@ -543,7 +558,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 // Work-groups for up to max_tiles row tiles dealt round-robin to the XCDs: ceil(max_tiles / 8) tiles
-// per XCD in blocks of kGroupTiles, each tile n_ntiles * n_ksplit work-groups.
+// per XCD in blocks of kGroupTiles, each tile n_ntiles * n_ksplit work-groups (with fewer than 8 tiles,
+// an XCD gets at most two chunks of at most per_tile / 2 work-groups each, which this covers).
 unsigned grid_for(int64_t max_tiles, int n_ntiles, int n_ksplit = 1) {
   const int64_t per_xcd = (max_tiles + kXcds - 1) / kXcds;
   const int64_t blocks = (per_xcd + kGroupTiles - 1) / kGroupTiles;
