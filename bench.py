@@ -59,7 +59,10 @@ KERNEL_SYMBOLS = {
     "down_q4": ("::q_stream_kernel<(moe::QFormat)0, false", ["gemm_quant.hip", "tile_core.h", "kernels.h"]),
     "gateup_fp8": ("::q_stream_kernel<(moe::QFormat)1, true", ["gemm_quant.hip", "tile_core.h", "kernels.h"]),
     "down_fp8": ("::q_stream_kernel<(moe::QFormat)1, false", ["gemm_quant.hip", "tile_core.h", "kernels.h"]),
+    "gateup_tile_fp8": ("::gateup_tile_fp8_kernel", ["gemm_tile.hip", "tile_core.h", "kernels.h"]),
+    "down_tile_fp8": ("::down_tile_fp8_kernel", ["gemm_tile.hip", "tile_core.h", "kernels.h"]),
 }
+QUANT_STREAM = ("gateup_q4", "down_q4", "gateup_fp8", "down_fp8")  # the quantized weight-stream kernels
 Q4_BYTES = 0.5 + 2 / 32    # bytes per 4-bit weight: the code plus its share of a binary16 scale per 32
 FP8_BYTES = 1 + 4 / 128 ** 2  # bytes per FP8 weight: the code plus its share of an fp32 scale per 128 x 128
 QUANT_BYTES = {"int4": Q4_BYTES, "fp8": FP8_BYTES}
@@ -210,8 +213,9 @@ STREAM_ROWS, STREAM_MIN_GROUPS = 32, 16   # the device plan's split (kStreamRows
 def plan_families(w, ids):
     """Which groups the library's plan hands to the weight-stream kernels and which to the tile
     kernels, from the realised routing (host mirror of moe_api.cpp's kernel choice and the device
-    plan's split at kStreamRows).  Returns {family: [(group, rows, tokens)]}, tokens being the set of
-    token ids whose rows the group reads (None = every token)."""
+    plan's split at kStreamRows; 4-bit experts always stream).  Returns {family: [(group, rows,
+    tokens)]}, tokens being the set of token ids whose rows the group reads (None = every token: the
+    shared expert's or the dense FFN's group)."""
     if w.routing == "dense":
         groups = [(0, w.T, None)]
     else:
@@ -226,7 +230,7 @@ def plan_families(w, ids):
             groups.append((w.E, w.T, None))
     n_groups = (1 if w.routing == "dense" else w.E + w.n_shared)
     max_rows = w.T if w.routing == "dense" else w.T * w.K + w.T * w.n_shared
-    if max_rows <= 4 * n_groups:
+    if max_rows <= 4 * n_groups or w.quant == "int4":
         return {"stream": groups, "tile": []}
     cut = STREAM_ROWS if n_groups >= STREAM_MIN_GROUPS else 0
     return {"stream": [g for g in groups if g[1] <= cut], "tile": [g for g in groups if g[1] > cut]}
@@ -234,36 +238,34 @@ def plan_families(w, ids):
 
 def kernel_work(name, w, fams, n_touched):
     """Algorithmic (bytes, flops) of one launch of a grouped-GEMM kernel: the weights of the groups the
-    plan gives that kernel, once each; the token rows those groups read (each token's row once), or
-    their h rows; the outputs written once.  Weight re-reads (per 32-row pass of the stream kernels,
-    per row tile of the tile kernels) are traffic, not algorithmic bytes."""
+    plan gives that kernel, once each (routed experts in their storage format: FP8 or 4-bit codes and
+    scales; the shared expert and unquantized experts in bf16); the token rows those groups read (each
+    token's row once; with quantized experts the routed groups read the binary16 rows, the shared
+    expert the bf16 ones), or their h rows; the outputs written once.  Weight re-reads (per row pass
+    of the stream kernels, per row tile of the tile kernels) are traffic, not algorithmic bytes."""
     eb = 2 if w.dtype == "bf16" else 4
-    if name in ("gateup_q4", "down_q4", "gateup_fp8", "down_fp8"):
-        # routed experts with quantized weights (f16 token rows and h), plus the shared expert's bf16
-        # weights and rows in the same launch; y_rows bf16
-        qb = QUANT_BYTES[w.quant]
-        rows = w.T * w.K + w.T * w.n_shared
-        if name.startswith("gateup"):
-            wbytes = (n_touched * qb + w.n_shared * 2) * 2 * w.I * w.H
-            return wbytes + w.T * w.H * 2 * (1 + w.n_shared) + rows * w.I * 2, rows * 2 * 2 * w.I * w.H
-        wbytes = (n_touched * qb + w.n_shared * 2) * w.H * w.I
-        return wbytes + rows * w.I * 2 + rows * w.H * 2, rows * 2 * w.H * w.I
-    fam = "stream" if name.endswith("_stream") else "tile" if name.endswith("_tile") else None
-    if fam is None or fams is None:
+    if fams is None:
+        return None, None
+    fam = "tile" if "_tile" in name else "stream" if (name.endswith("_stream") or name in QUANT_STREAM) else None
+    if fam is None:
         return None, None
     groups = fams[fam]
     if not groups:
         return None, None
+    qb = QUANT_BYTES.get(w.quant)
     rows = sum(g[1] for g in groups)
-    if any(g[2] is None for g in groups):
-        tokens = w.T
+    every = any(g[2] is None for g in groups)  # the shared expert's (or the dense FFN's) group
+    routed = [g[2] for g in groups if g[2] is not None]
+    tok_routed = len(np.unique(np.concatenate(routed))) if routed else 0
+    w_elems = sum(eb if (qb is None or g[2] is None) else qb for g in groups)  # bytes per weight element
+    if qb is None:
+        a_bytes = (w.T if every else tok_routed) * w.H * eb
     else:
-        tokens = len(np.unique(np.concatenate([g[2] for g in groups])))
+        a_bytes = tok_routed * w.H * 2 + (w.T * w.H * 2 if every else 0)
     if name.startswith("gateup"):
-        return (len(groups) * 2 * w.I * w.H * eb + tokens * w.H * eb + rows * w.I * eb,
-                rows * 2 * 2 * w.I * w.H)
+        return w_elems * 2 * w.I * w.H + a_bytes + rows * w.I * eb, rows * 2 * 2 * w.I * w.H
     if name.startswith("down"):
-        return len(groups) * w.H * w.I * eb + rows * w.I * eb + rows * w.H * eb, rows * 2 * w.H * w.I
+        return w_elems * w.H * w.I + rows * w.I * eb + rows * w.H * eb, rows * 2 * w.H * w.I
     return None, None
 
 
@@ -428,7 +430,7 @@ def run(w, weights, steps, warmup, graph=True):
         counts = np.bincount(ids_np.ravel(), minlength=w.E)
     n_touched = int((counts > 0).sum())
     lb, lf = layer_work(w, n_touched)
-    fams = plan_families(w, None if w.routing == "dense" else ids_np) if w.quant == "none" else None
+    fams = plan_families(w, None if w.routing == "dense" else ids_np)
     per_kernel = {}
     for n, us in kern.items():
         kb, kf = kernel_work(n, w, fams, n_touched)
@@ -676,7 +678,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=list(wl.WORKLOADS))
-    ap.add_argument("--also", default="prefill,skew,ep_share,tiny,dense_decode,dense_prefill,decode_int4,decode_fp8",
+    ap.add_argument("--also", default="prefill,skew,ep_share,tiny,dense_decode,dense_prefill,decode_int4,decode_fp8,"
+                                      "prefill_fp8",
                     help="comma-separated workloads measured in the same run and reported beside it ('none')")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="first run one copy of known size (the traffic summary's counter calibration)")

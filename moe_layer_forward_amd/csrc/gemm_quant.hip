@@ -133,6 +133,11 @@ struct QArgs {
   const uint16_t* sh_w1;        // up weight (gate/up)
   const uint16_t* sh_a;         // bf16 x (gate/up) or h (down) rows
   uint32_t sh_a_bytes;
+  // Calls whose larger groups go to the tile kernels: only the groups active[counters[2] ..) of at
+  // most stream_rows rows, and the shared expert only if it has at most stream_rows rows.
+  int small_only;
+  int stream_rows;
+  int n_routed;  // groups >= n_routed (the shared expert's, when the plan lists it) are not streamed
 };
 
 __device__ __forceinline__ int code_swz(int r) { return (r >> 1) & 7; }
@@ -664,6 +669,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   char* const ring[kD] = {s0, s1, s2, s3};
 
   if ((int)blockIdx.x < p.sh_blocks) {
+    if (p.small_only && p.sh_offsets[1] - p.sh_offsets[0] > p.stream_rows) return;  // a tile-list group
 #if defined(__HIP_DEVICE_COMPILE__)
     shared_part<SWIGLU>(p, ring, blockIdx.x);
 #endif
@@ -671,9 +677,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   static_assert(SWIGLU ? CHAIN == 1 : CHAIN >= 1, "column-block chains are for the down launch");
   const int bid = (int)blockIdx.x - p.sh_blocks;
-  const int slot = bid / p.n_wg, nb = bid % p.n_wg;
+  const int slot = (p.small_only ? p.counters[2] : 0) + bid / p.n_wg, nb = bid % p.n_wg;
   if (slot >= p.counters[0]) return;
   const int g = p.active[slot];
+  if (g >= p.n_routed) return;
   int64_t r0 = p.group_offsets[g], r1 = p.group_offsets[g + 1];
   if (r0 > p.max_rows) r0 = p.max_rows;
   if (r1 > p.max_rows) r1 = p.max_rows;
@@ -773,13 +780,22 @@ bool qshape_ok(QFormat f, int H, int I) {
   return H > 0 && I > 0 && H % 128 == 0 && I % 128 == 0 && H <= kMax && I <= kMax;
 }
 
+// Fields of a call that streams only the small groups (the tile kernels take the others).
+static void set_small(QArgs& p, const Groups& g, int n_routed, bool small_only) {
+  p.small_only = small_only ? 1 : 0;
+  p.stream_rows = g.stream_rows;
+  p.n_routed = n_routed;
+}
+
 hipError_t launch_gateup_q_stream(const Groups& g, const QWeights& w, const uint16_t* x16, int64_t x_rows,
-                                  uint16_t* h16, const SharedBf16* sh, int H, int I, hipStream_t s) {
-  if (!qshape_ok(w.format, H, I)) return hipErrorInvalidValue;
+                                  uint16_t* h16, const SharedBf16* sh, int H, int I, int n_routed, bool small_only,
+                                  hipStream_t s) {
+  if (!qshape_ok(w.format, H, I) || (small_only && g.stream_rows <= 0)) return hipErrorInvalidValue;
   QArgs p{g.group_offsets, g.row_index, g.active, g.counters, g.max_rows, w.gate_codes, w.gate_scales,
           w.up_codes, w.up_scales, x16, operand_bytes(x_rows, H), h16, 0, nullptr, H, I, I / 64};
   set_shared(p, sh, true, H, I);
-  const unsigned grid = (unsigned)(p.sh_blocks + (int64_t)g.n_groups * p.n_wg);
+  set_small(p, g, n_routed, small_only);
+  const unsigned grid = (unsigned)(p.sh_blocks + (int64_t)g.n_groups * p.n_wg);  // one slot per listed group
   if (w.format == QFormat::kInt4)
     q_stream_kernel<QFormat::kInt4, true, 1><<<grid, 256, 0, s>>>(p);
   else
@@ -788,8 +804,8 @@ hipError_t launch_gateup_q_stream(const Groups& g, const QWeights& w, const uint
 }
 
 hipError_t launch_down_q_stream(const Groups& g, const QWeights& w, const uint16_t* h16, uint16_t* y_rows,
-                                const SharedBf16* sh, int H, int I, hipStream_t s) {
-  if (!qshape_ok(w.format, H, I)) return hipErrorInvalidValue;
+                                const SharedBf16* sh, int H, int I, int n_routed, bool small_only, hipStream_t s) {
+  if (!qshape_ok(w.format, H, I) || (small_only && g.stream_rows <= 0)) return hipErrorInvalidValue;
   const bool q4 = w.format == QFormat::kInt4;
   // chained column blocks when they divide the columns and the K steps fill whole 4-bit scale
   // blocks (FP8: while the chain's scales fit one register)
@@ -799,7 +815,8 @@ hipError_t launch_down_q_stream(const Groups& g, const QWeights& w, const uint16
   QArgs p{g.group_offsets, nullptr, g.active, g.counters, g.max_rows, w.down_codes, w.down_scales, nullptr,
           nullptr, h16, operand_bytes(g.max_rows, I), y_rows, 1, nullptr, H, I, H / 128 / (chain ? kDownChain : 1)};
   set_shared(p, sh, false, H, I);
-  const unsigned grid = (unsigned)(p.sh_blocks + (int64_t)g.n_groups * p.n_wg);
+  set_small(p, g, n_routed, small_only);
+  const unsigned grid = (unsigned)(p.sh_blocks + (int64_t)g.n_groups * p.n_wg);  // one slot per listed group
   if (q4) {
     if (chain)
       q_stream_kernel<QFormat::kInt4, false, kDownChain><<<grid, 256, 0, s>>>(p);

@@ -311,18 +311,17 @@ __device__ __forceinline__ void tile_body(const Loads& o, const Rings& r, const 
   epilogue(std::integral_constant<int, NBW>{}, acc);
 }
 
-// One instance per (16-row blocks of this wave, A loads per wave) pair that a row count of
-// 1 .. 256 produces: nblk = ceil(rows / 16) blocks, wave row wr takes ceil((nblk - wr) / 2) of them,
-// and the 2 nblk A pieces of 8 rows are spread over the 8 waves, ceil(nblk / 4) each.  Device pass
-// only: these instances are device code.
-template <class Epilogue>
-__device__ __forceinline__ void run_tile(const Loads& o, int nblk, int wr, const Rings& r, const Frag& f,
-                                         const Epilogue& epilogue) {
+// body(NBW, NAL) for the (16-row blocks of this wave, A loads per wave) pair of a tile of nblk 16-row
+// blocks: wave row wr takes ceil((nblk - wr) / 2) of them, and the 2 nblk A pieces of 8 rows are spread
+// over the 8 waves, ceil(nblk / 4) each.  One instance per pair that a row count of 1 .. 256 produces;
+// device pass only (these instances are device code).
+template <class Body>
+__device__ __forceinline__ void run_tile(int nblk, int wr, const Body& body) {
   const int nbw = (nblk - wr + 1) / 2;
   const int nal = (nblk + 3) / 4;
 #if defined(__HIP_DEVICE_COMPILE__)
 #define MOE_TILE_CASE(B, A) \
-  if (nbw == B && nal == A) return tile_body<B, A>(o, r, f, epilogue);
+  if (nbw == B && nal == A) return body(std::integral_constant<int, B>{}, std::integral_constant<int, A>{});
   MOE_TILE_CASE(8, 4)
   MOE_TILE_CASE(7, 4)
   MOE_TILE_CASE(6, 4)
@@ -337,10 +336,7 @@ __device__ __forceinline__ void run_tile(const Loads& o, int nblk, int wr, const
   MOE_TILE_CASE(0, 1)
 #undef MOE_TILE_CASE
 #else
-  (void)o;
-  (void)r;
-  (void)f;
-  (void)epilogue;
+  (void)body;
   (void)nbw;
   (void)nal;
 #endif
@@ -374,6 +370,13 @@ struct OutTile {
     char* st = stage(r, row / kRowsPer);
     *reinterpret_cast<uint16_t*>(st + (row % kRowsPer) * kRowB + (((col >> 3) ^ out_swz(row)) << 4) + (col & 7) * 2) =
         f32_to_bf16(v);
+  }
+  // binary16, column c at position (c & ~7) | pair_pos(c & 7) (the operand order of the FP8 tiles)
+  __device__ static __forceinline__ void put_f16_pairs(const Rings& r, int row, int col, float v) {
+    char* st = stage(r, row / kRowsPer);
+    const int c = (col & ~7) | (((col & 3) << 1) | ((col >> 2) & 1));
+    *reinterpret_cast<_Float16*>(st + (row % kRowsPer) * kRowB + (((c >> 3) ^ out_swz(row)) << 4) + (c & 7) * 2) =
+        (_Float16)v;
   }
   // rows [0, m_valid) of the staged tile -> out[(rbeg + r) * ld + col0 + ...], columns below col_end
   __device__ static __forceinline__ void store(const Rings& r, int m_valid, uint16_t* out, int64_t ld, int64_t rbeg,
@@ -427,11 +430,8 @@ __device__ __forceinline__ Frag make_frag(int wr, const int (&b_rows)[4]) {
       b2_[kStageBytes];                                                                                        \
   const Rings rings{{a0_, a1_}, {b0_, b1_, b2_}};
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gateup_tile_kernel(TileArgs p) {
-  MOE_TILE_SMEM
-  int nt, ks;
-  TileRows t;
-  if (!tile_of(p, nt, ks, t)) return;
+// Gate/up work item (row tile t, h columns nt*128 ..): h rows in bf16.
+__device__ __forceinline__ void gateup_bf16_item(const TileArgs& p, const Rings& rings, int nt, const TileRows& t) {
   const int H = p.H, I = p.I;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr = w >> 2, wc = w & 3;  // wave row (token-row blocks wr, wr + 2, ...), wave column
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   uint16_t* h = static_cast<uint16_t*>(p.out);
   const int64_t rbeg = t.rbeg;
   const int m_valid = (int)(t.rend - t.rbeg);
-  run_tile(o, (m_valid + 15) / 16, wr, rings, f, [&](auto nbw_c, const auto& acc) {
+  const auto epilogue = [&](auto nbw_c, const auto& acc) {
     constexpr int NBW = decltype(nbw_c)::value;
     using Out = OutTile<128>;
     block_sync_lds();  // every wave is done reading the rings
@@ -478,14 +478,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     });
     block_sync_lds();
     Out::store(rings, m_valid, h, I, rbeg, h0, I);
+  };
+  run_tile((m_valid + 15) / 16, wr, [&](auto b, auto a) {
+    tile_body<decltype(b)::value, decltype(a)::value>(o, rings, f, epilogue);
   });
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void down_tile_kernel(TileArgs p) {
-  MOE_TILE_SMEM
-  int nt, ks;
-  TileRows t;
-  if (!tile_of(p, nt, ks, t)) return;
+// Down work item (row tile t, output columns nt*256 .., K range ks).
+__device__ __forceinline__ void down_bf16_item(const TileArgs& p, const Rings& rings, int nt, int ks,
+                                               const TileRows& t) {
   const int H = p.H, I = p.I;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr = w >> 2, wc = w & 3;
@@ -521,7 +522,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const float* row_scale = p.row_scale;
   const bool split = p.n_ksplit > 1;
   void* out = split ? static_cast<void*>(p.part + (int64_t)ks * p.max_rows * H) : p.out;
-  run_tile(o, (m_valid + 15) / 16, wr, rings, f, [&](auto nbw_c, const auto& acc) {
+  const auto epilogue = [&](auto nbw_c, const auto& acc) {
     constexpr int NBW = decltype(nbw_c)::value;
     if (p.out_bf16 && !split) {
       using Out = OutTile<256>;
@@ -554,7 +555,459 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           if (col < H) static_cast<float*>(out)[r * H + col] = acc[i][s][e] * sc;
         }
       }
+  };
+  run_tile((m_valid + 15) / 16, wr, [&](auto b, auto a) {
+    tile_body<decltype(b)::value, decltype(a)::value>(o, rings, f, epilogue);
   });
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gateup_tile_kernel(TileArgs p) {
+  MOE_TILE_SMEM
+  int nt, ks;
+  TileRows t;
+  if (tile_of(p, nt, ks, t)) gateup_bf16_item(p, rings, nt, t);
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void down_tile_kernel(TileArgs p) {
+  MOE_TILE_SMEM
+  int nt, ks;
+  TileRows t;
+  if (tile_of(p, nt, ks, t)) down_bf16_item(p, rings, nt, ks, t);
+}
+
+// ----------------------------------------------------------------------------- FP8 routed experts
+// The routed experts' weights as E4M3 codes with one fp32 scale per 128 x 128 block (the storage the
+// weight-stream kernels read; see QWeights).  Same tiles, waves, LDS rings and dealing; what changes:
+//   * A B stage holds 256 weight rows x 128 codes: 128 inputs (one scale block along K, whole cache
+//     lines) for two K steps of 64.  Each half (the 128 rows of pieces 0-1, or of pieces 2-3) is
+//     issued 4 steps before its first step, so the in-order vector-memory count never makes a step
+//     wait for weights a later step needs.
+//   * The token rows (A) are binary16 with each group of 8 inputs in the order 0,4,1,5,2,6,3,7, and
+//     v_mfma_f32_16x16x32_f16 runs the products.  Per step a lane reads 16 codes of each of its 4
+//     weight rows in one 16-byte LDS read (inputs 16 g .. 16 g + 15 of the step, g = lane / 16) and
+//     feeds the first 8 to the step's first MFMA k-substep and the next 8 to the second, so A's
+//     fragment of substep kk is chunk 2 g + kk of the step's 128-byte row.
+//   * Decoding: a byte permute puts codes (0,4,1,5) and (2,6,3,7) of 8 inputs into one word each, and
+//     v_cvt_scalef32_pk_f16_fp8 makes two binary16 values of a word's low or high code pair.  That
+//     conversion multiplies by 2^floor(log2 s) of its scale operand s (only the exponent counts), so
+//     passing the block scale applies its power of two exactly; the mantissa part m = s / 2^floor(log2 s)
+//     (in [1, 2), exact in binary16 to 11 bits) follows as one packed binary16 multiply.  A weight is
+//     thus f16(f16(e4m3(c) 2^e) f16(m)), within 2^-10 of e4m3(c) s relative (binary16 subnormals
+//     below 2^-14 absolute).  A wave's 64 weight rows lie in one 128-row scale block, so its scales
+//     are one per K block: lane j holds K block j's (at most 64 blocks, K <= 8192).
+//   * The shared expert (bf16 weights) is a group of the same tile list: its tiles run the bf16 body.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct QTileArgs {
+  TileArgs p;             // plan, bf16 operands of the shared expert (a: bf16 rows), output
+  const uint16_t* a16;    // routed rows' binary16 A rows (gate/up: x16 through row_index; down: h)
+  const uint8_t* codes0;  // gate (gate/up) or down codes [E, N, K]
+  const uint8_t* codes1;  // up codes
+  const float* scales0;   // [E, N / 128, K / 128]
+  const float* scales1;
+};
+
+// Lane j's block scale (K block j of the wave's 128-row block): s for the conversion and f16(m) twice.
+struct LaneScale {
+  float s;
+  uint32_t m2;
+};
+
+__device__ __forceinline__ LaneScale lane_scale(const float* blocks, int nkb) {
+  const int lane = threadIdx.x & 63;
+  const float s = lane < nkb ? blocks[lane] : 1.f;
+  // m: s with its exponent field replaced by that of 1.0 (the sign stays with m)
+  const float m = __uint_as_float((__float_as_uint(s) & 0x807fffffu) | 0x3f800000u);
+  const uint32_t h = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)m);
+  return LaneScale{s, h | (h << 16)};
+}
+
+// The scales of one K block, uniform over the wave (gate/up: [0] gate rows, [1] up rows).
+struct StepScale {
+  float s[2];
+  f16x2 m[2];
+};
+
+__device__ __forceinline__ StepScale step_scale(const LaneScale (&ls)[2], int j) {
+  StepScale r;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    r.s[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[i].s), j));
+    r.m[i] = __builtin_bit_cast(f16x2, (uint32_t)__builtin_amdgcn_readlane((int)ls[i].m2, j));
+  }
+  return r;
+}
+
+// 8 codes (inputs 0..7: the bytes of lo, then of hi) -> binary16 weights in the order 0,4,1,5,2,6,3,7.
+__device__ __forceinline__ f16x8 dequant8(uint32_t lo, uint32_t hi, float s, f16x2 m) {
+  const uint32_t p0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // bytes: codes 0, 4, 1, 5
+  const uint32_t p1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // codes 2, 6, 3, 7
+  const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(p0, s, false) * m;
+  const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(p0, s, true) * m;
+  const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(p1, s, false) * m;
+  const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(p1, s, true) * m;
+  return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+// LDS read geometry of the FP8 tiles (16-row blocks as in Frag).
+struct QFrag {
+  uint32_t a_off[2];  // A, k-substep kk: logical chunk 2 g + kk of row x
+  uint32_t b_off[2];  // B, step half hf (the step's 64 codes of the stage's 128): chunk 4 hf + g
+  uint32_t a_row0;
+  uint32_t b_row0[4];
+};
+
+__device__ __forceinline__ QFrag make_qfrag(int wr, const int (&b_rows)[4]) {
+  const int lane = threadIdx.x & 63, x = lane & 15, g = lane >> 4;
+  QFrag f;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    f.a_off[kk] = (uint32_t)(x * kRowBytes + (((2 * g + kk) ^ swz(x)) << 4));
+    f.b_off[kk] = (uint32_t)(x * kRowBytes + (((4 * kk + g) ^ swz(x)) << 4));
+  }
+  f.a_row0 = (uint32_t)(wr * 16 * kRowBytes);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) f.b_row0[s] = (uint32_t)(b_rows[s] * kRowBytes);
+  return f;
+}
+
+// Lane offset of B piece j inside a code tensor whose rows are K bytes (row rl of the tile at weight
+// row wrow); K block b adds 128 b.
+__device__ __forceinline__ uint32_t qb_offset(int j, int64_t wrow, int K) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rl = (w + kWaves * j) * 8 + (lane >> 3);
+  const int chunk = (lane & 7) ^ swz(rl);
+  return (uint32_t)(wrow * K + 16 * chunk);
+}
+
+// Half HF of K block s / 2 (the loads of step index s = 2 b + HF): B pieces 2 HF and 2 HF + 1.
+template <int HF>
+__device__ __forceinline__ void issue_qb(const Loads& o, int s, char* stage) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t kb = (uint32_t)(s >> 1) * kRowBytes;
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int j = 2 * HF + jj;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(operand_rsrc(o.b_base[j]), (LdsPtr)(stage + (w + kWaves * j) * 1024), 16,
+                                             o.b_off[j] + kb, 0, 0, 0);
+  }
+}
+
+// Weights carried from one K step to the next: the first k-substep's decoded fragments of the 4 column
+// blocks, and the raw codes of the second's.
+struct QCarry {
+  f16x8 b0[4];
+  u32x2 zw[4];
+};
+
+// Fragment of the substep (0 .. NBW-1) in which column block s is decoded: spread over the first
+// min(NBW, 4) fragments, so each fragment's MFMAs cover about one column block's decoding.
+template <int NBW>
+constexpr int decode_frag(int s) {
+  return s * (NBW < 4 ? NBW : 4) / 4;
+}
+
+// Reads the 16 codes per column block of step half HF of a B stage.
+template <int HF>
+__device__ __forceinline__ void read_codes(const char* Bs, const QFrag& f, u32x4 (&q)[4]) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) q[s] = *reinterpret_cast<const u32x4*>(Bs + f.b_row0[s] + f.b_off[HF]);
+}
+
+// MFMAs of one K step, in compute_step's fragment order, software-pipelined with the decoding: the
+// step's second-substep weights are decoded from the carried codes during its first substep, the next
+// step's codes are read from LDS (their stage is complete and visible since this step's barrier, and
+// no load of this step writes it) and its first-substep weights decoded during the second substep.
+// Each fragment's MFMAs are independent of the decoding placed beside them.  Column block s uses scale
+// set GU && s >= 2 (the up rows).  kFirst: the step decodes its own first substep first (the tile's
+// first step).  HF, HFN: this and the next step's half of their B stages.
+template <int NBW, int HF, int HFN, bool GU, bool kFirst>
+__device__ __forceinline__ void q_compute_step(const char* As, const char* Bs, const char* Bn, bool has_next,
+                                               const QFrag& f, const StepScale& sc, const StepScale& scn,
+                                               QCarry& c, f32x4 (&acc)[NBW > 0 ? NBW : 1][4]) {
+  if constexpr (NBW > 0) {
+    constexpr int NF = 2 * NBW;
+    constexpr int kReadNext = NBW < 5 ? NBW - 1 : 4;  // fragment that reads the next step's codes
+    auto set = [](int s) { return GU && s >= 2 ? 1 : 0; };
+    if constexpr (kFirst) {
+      u32x4 q[4];
+      read_codes<HF>(Bs, f, q);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        c.b0[s] = dequant8(q[s][0], q[s][1], sc.s[set(s)], sc.m[set(s)]);
+        c.zw[s] = u32x2{q[s][2], q[s][3]};
+      }
+    } else {
+      (void)Bs;
+    }
+    auto read_a = [&](int fi) {
+      return *reinterpret_cast<const f16x8*>(As + f.a_row0 + f.a_off[fi / NBW] + (fi % NBW) * 2 * 16 * kRowBytes);
+    };
+    f16x8 b1[4];
+    u32x4 qn[4];
+    f16x8 a[NF];
+    a[0] = read_a(0);
+    a[1] = read_a(1);
+#pragma unroll
+    for (int fi = 0; fi < NF; ++fi) {
+      if (fi + 2 < NF) a[fi + 2] = read_a(fi + 2);
+      if (fi < NBW) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          if (decode_frag<NBW>(s) == fi) b1[s] = dequant8(c.zw[s][0], c.zw[s][1], sc.s[set(s)], sc.m[set(s)]);
+        if (fi == kReadNext && has_next) read_codes<HFN>(Bn, f, qn);
+      } else if (has_next) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          if (decode_frag<NBW>(s) == fi - NBW) {
+            c.b0[s] = dequant8(qn[s][0], qn[s][1], scn.s[set(s)], scn.m[set(s)]);
+            c.zw[s] = u32x2{qn[s][2], qn[s][3]};
+          }
+      }
+      const int kk = fi / NBW, i = fi % NBW;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[fi], kk == 0 ? c.b0[s] : b1[s], acc[i][s], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    (void)As;
+    (void)Bs;
+    (void)Bn;
+    (void)has_next;
+    (void)f;
+    (void)sc;
+    (void)scn;
+    (void)c;
+    (void)acc;
+  }
+}
+
+// LDS rings of the FP8 tiles: three stages of token rows, two of codes (each two K steps), over the
+// same five 32 KiB arrays as Rings.
+struct QRings {
+  char* a[3];
+  char* b[2];
+};
+
+// One K step kt (kt % 12 == D) of the FP8 tiles.  Per wave the vector-memory order is
+// B(0) A(0) B(1) A(1) B(2) | A(2) B(3) | A(3) B(4) | ... with B(s) the half-stage of step index s:
+// step kt issues A(kt + 2) and B(kt + 3), and when it starts only the loads of step kt - 1 (A(kt + 1),
+// B(kt + 2)) may still be in flight, so every load has about two steps to land.  After the barrier
+// A(kt) and B(kt + 1), i.e. the next step's half of its K block, are visible.  A(kt + 2) overwrites the
+// rows of step kt - 1; B(kt + 3) the K block two blocks earlier, whose codes were last read from LDS in
+// step kt - 1 or before (a block b is read in steps 2b - 1 and 2b, for the first substep of the step
+// after each).
+template <int NBW, int NAL, int D, bool kTail, bool GU, bool kFirst = false>
+__device__ __forceinline__ void q_kstep(const Loads& o, int kt, int nk, const QRings& r, const QFrag& f,
+                                        const LaneScale (&ls)[2], QCarry& c, f32x4 (&acc)[NBW > 0 ? NBW : 1][4]) {
+  if (!kTail || kt + 2 < nk)
+    wait_vmcnt<NAL + 2>();
+  else if (kt + 1 < nk)
+    wait_vmcnt<NAL>();
+  else
+    wait_vmcnt<0>();
+  block_sync_lds();
+  if (!kTail || kt + 2 < nk) issue_a<NAL>(o, kt + 2, r.a[(D + 2) % 3]);
+  if (!kTail || kt + 3 < nk) issue_qb<(D + 1) % 2>(o, kt + 3, r.b[((D + 3) / 2) % 2]);
+  const bool has_next = !kTail || kt + 1 < nk;
+  const StepScale sc = step_scale(ls, kt >> 1);
+  const StepScale scn = step_scale(ls, has_next ? (kt + 1) >> 1 : kt >> 1);
+  __builtin_amdgcn_sched_barrier(0);
+  q_compute_step<NBW, D % 2, (D + 1) % 2, GU, kFirst>(r.a[D % 3], r.b[(D / 2) % 2], r.b[((D + 1) / 2) % 2], has_next,
+                                                      f, sc, scn, c, acc);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int NBW, int NAL, bool GU>
+__device__ __forceinline__ void q_kloop(const Loads& o, int nk, const QRings& r, const QFrag& f,
+                                        const LaneScale (&ls)[2], f32x4 (&acc)[NBW > 0 ? NBW : 1][4]) {
+  // prologue in the steady state's issue order (nk is even: whole K blocks), fenced
+  issue_qb<0>(o, 0, r.b[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_a<NAL>(o, 0, r.a[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_qb<1>(o, 1, r.b[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_a<NAL>(o, 1, r.a[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  if (nk > 2) issue_qb<0>(o, 2, r.b[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  QCarry c;
+  q_kstep<NBW, NAL, 0, true, GU, true>(o, 0, nk, r, f, ls, c, acc);
+  int kt = 1;
+  // steady state: every load these twelve steps issue exists (kt + 14 < nk)
+  for (; kt + 15 <= nk; kt += 12) {
+    static_for<12>([&](auto ic) {
+      constexpr int j = decltype(ic)::value;
+      q_kstep<NBW, NAL, (j + 1) % 12, false, GU>(o, kt + j, nk, r, f, ls, c, acc);
+    });
+  }
+  // the last 0 .. 13 steps (kt % 12 == 1 here)
+  while (kt < nk) {
+    bool done = false;
+    static_for<12>([&](auto ic) {
+      constexpr int j = decltype(ic)::value;
+      if (!done) {
+        q_kstep<NBW, NAL, (j + 1) % 12, true, GU>(o, kt, nk, r, f, ls, c, acc);
+        if (++kt == nk) done = true;
+      }
+    });
+  }
+}
+
+template <int NBW, int NAL, bool GU, class Epilogue>
+__device__ __forceinline__ void q_tile_body(const Loads& o, const QRings& r, const QFrag& f, const LaneScale (&ls)[2],
+                                            const Epilogue& epilogue) {
+  f32x4 acc[NBW > 0 ? NBW : 1][4];
+#pragma unroll
+  for (int i = 0; i < (NBW > 0 ? NBW : 1); ++i)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc[i][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  q_kloop<NBW, NAL, GU>(o, o.nk, r, f, ls, acc);
+  epilogue(std::integral_constant<int, NBW>{}, acc);
+}
+
+// Gate/up work item of a routed group: h rows in binary16 (operand order), as the bf16 item.
+__device__ __forceinline__ void gateup_fp8_item(const QTileArgs& q, const Rings& rings, int nt, const TileRows& t) {
+  const TileArgs& p = q.p;
+  const int H = p.H, I = p.I;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = w >> 2, wc = w & 3;
+  const int64_t gsz = (int64_t)I * H;
+  const uint8_t* cg = q.codes0 + t.g * gsz;
+  const uint8_t* cu = q.codes1 + t.g * gsz;
+  const int h0 = nt * 128;
+
+  Loads o;
+  o.a_base = reinterpret_cast<const char*>(q.a16);
+  a_offsets(o, H, [&](int rl) -> int64_t {
+    const int64_t r = t.rbeg + rl;
+    const int64_t rr = r < t.rend ? r : t.rbeg;
+    return p.row_index ? (int64_t)p.row_index[rr] : rr;
+  });
+#pragma unroll
+  for (int j = 0; j < kBLoads; ++j) {  // pieces w, w + 8: gate rows; w + 16, w + 24: up rows
+    const int rl = (w + kWaves * j) * 8 + (lane >> 3);
+    o.b_base[j] = reinterpret_cast<const char*>(j < 2 ? cg : cu);
+    o.b_off[j] = qb_offset(j, h0 + (rl & 127), H);
+  }
+  o.nk = H / kBK;
+  o.skew = 0;
+  // every h column of the tile lies in scale block row nt of W_gate and of W_up
+  const int nkb = H / 128;
+  const LaneScale ls[2] = {lane_scale(q.scales0 + ((int64_t)t.g * (I / 128) + nt) * nkb, nkb),
+                           lane_scale(q.scales1 + ((int64_t)t.g * (I / 128) + nt) * nkb, nkb)};
+
+  const int b_rows[4] = {32 * wc, 32 * wc + 16, 128 + 32 * wc, 128 + 32 * wc + 16};
+  const QFrag f = make_qfrag(wr, b_rows);
+  uint16_t* h = static_cast<uint16_t*>(p.out);
+  const int64_t rbeg = t.rbeg;
+  const int m_valid = (int)(t.rend - t.rbeg);
+  const auto epilogue = [&](auto nbw_c, const auto& acc) {
+    constexpr int NBW = decltype(nbw_c)::value;
+    using Out = OutTile<128>;
+    block_sync_lds();  // every wave is done reading the rings
+    static_for<NBW>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * (wr + 2 * i) + 4 * (lane >> 4) + e;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          Out::put_f16_pairs(rings, row, 32 * wc + 16 * s + (lane & 15), swiglu_f32(acc[i][s][e], acc[i][s + 2][e]));
+      }
+    });
+    block_sync_lds();
+    Out::store(rings, m_valid, h, I, rbeg, h0, I);
+  };
+  const QRings qr{{rings.a[0], rings.a[1], rings.b[0]}, {rings.b[1], rings.b[2]}};
+  run_tile((m_valid + 15) / 16, wr, [&](auto b, auto a) {
+    q_tile_body<decltype(b)::value, decltype(a)::value, true>(o, qr, f, ls, epilogue);
+  });
+}
+
+// Down work item of a routed group: y rows in bf16.
+__device__ __forceinline__ void down_fp8_item(const QTileArgs& q, const Rings& rings, int nt, const TileRows& t) {
+  const TileArgs& p = q.p;
+  const int H = p.H, I = p.I;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = w >> 2, wc = w & 3;
+  const uint8_t* cd = q.codes0 + t.g * ((int64_t)H * I);
+  const int n0 = nt * 256;
+
+  Loads o;
+  o.a_base = reinterpret_cast<const char*>(q.a16);
+  a_offsets(o, I, [&](int rl) -> int64_t {
+    const int64_t r = t.rbeg + rl;
+    return r < t.rend ? r : t.rbeg;
+  });
+#pragma unroll
+  for (int j = 0; j < kBLoads; ++j) {  // output columns past H re-read row n0, never stored
+    const int rl = (w + kWaves * j) * 8 + (lane >> 3);
+    o.b_base[j] = reinterpret_cast<const char*>(cd);
+    o.b_off[j] = qb_offset(j, n0 + rl < H ? n0 + rl : n0, I);
+  }
+  o.nk = I / kBK;
+  o.skew = 0;
+  // the wave's 64 output columns lie in scale block row (n0 + 64 wc) / 128 (past H: the last one)
+  const int nkb = I / 128;
+  int rb = (n0 + 64 * wc) / 128;
+  if (rb > H / 128 - 1) rb = H / 128 - 1;
+  const LaneScale l0 = lane_scale(q.scales0 + ((int64_t)t.g * (H / 128) + rb) * nkb, nkb);
+  const LaneScale ls[2] = {l0, l0};
+
+  const int b_rows[4] = {64 * wc, 64 * wc + 16, 64 * wc + 32, 64 * wc + 48};
+  const QFrag f = make_qfrag(wr, b_rows);
+  const int64_t rbeg = t.rbeg;
+  const int m_valid = (int)(t.rend - t.rbeg);
+  uint16_t* y = static_cast<uint16_t*>(p.out);
+  const auto epilogue = [&](auto nbw_c, const auto& acc) {
+    constexpr int NBW = decltype(nbw_c)::value;
+    using Out = OutTile<256>;
+    block_sync_lds();
+    static_for<NBW>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * (wr + 2 * i) + 4 * (lane >> 4) + e;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) Out::put(rings, row, 64 * wc + 16 * s + (lane & 15), acc[i][s][e]);
+      }
+    });
+    block_sync_lds();
+    Out::store(rings, m_valid, y, H, rbeg, n0, H);
+  };
+  const QRings qr{{rings.a[0], rings.a[1], rings.b[0]}, {rings.b[1], rings.b[2]}};
+  run_tile((m_valid + 15) / 16, wr, [&](auto b, auto a) {
+    q_tile_body<decltype(b)::value, decltype(a)::value, false>(o, qr, f, ls, epilogue);
+  });
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gateup_tile_fp8_kernel(
+    QTileArgs q) {
+  MOE_TILE_SMEM
+  int nt, ks;
+  TileRows t;
+  if (!tile_of(q.p, nt, ks, t)) return;
+  if (t.g == q.p.w.shared_group)
+    gateup_bf16_item(q.p, rings, nt, t);
+  else
+    gateup_fp8_item(q, rings, nt, t);
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void down_tile_fp8_kernel(
+    QTileArgs q) {
+  MOE_TILE_SMEM
+  int nt, ks;
+  TileRows t;
+  if (!tile_of(q.p, nt, ks, t)) return;
+  if (t.g == q.p.w.shared_group)
+    down_bf16_item(q.p, rings, nt, 0, t);
+  else
+    down_fp8_item(q, rings, nt, t);
 }
 
 // Work-groups for up to max_tiles row tiles dealt round-robin to the XCDs: ceil(max_tiles / 8) tiles
@@ -672,6 +1125,38 @@ hipError_t launch_down_tile_bf16(const Groups& g, const Weights& w, const uint16
   if (blocks > 4096) blocks = 4096;
   ksplit_reduce_kernel<<<(unsigned)blocks, 256, 0, s>>>(part, split, g.group_offsets, g.n_groups, g.max_rows,
                                                         g.stream_rows, H, y_rows, y_bf16 ? 1 : 0);
+  return hipGetLastError();
+}
+
+bool tile_fp8_shape_ok(int H, int I) {
+  return H > 0 && I > 0 && H % 128 == 0 && I % 128 == 0 && H <= 128 * 64 && I <= 128 * 64;
+}
+
+hipError_t launch_gateup_tile_fp8(const Groups& g, const Weights& w, const QWeights& q, const uint16_t* x,
+                                  const uint16_t* x16, uint16_t* h, int H, int I, hipStream_t s) {
+  if (q.format != QFormat::kFp8 || !tile_fp8_shape_ok(H, I)) return hipErrorInvalidValue;
+  QTileArgs a{{g.group_offsets, g.row_index, g.tiles, g.counters, g.max_rows, w, x, h, 1, nullptr, H, I, I / 128, 1,
+               nullptr},
+              x16,
+              static_cast<const uint8_t*>(q.gate_codes),
+              static_cast<const uint8_t*>(q.up_codes),
+              static_cast<const float*>(q.gate_scales),
+              static_cast<const float*>(q.up_scales)};
+  gateup_tile_fp8_kernel<<<grid_for(g.max_tiles, a.p.n_ntiles), kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_tile_fp8(const Groups& g, const Weights& w, const QWeights& q, const uint16_t* h,
+                                uint16_t* y_rows, int H, int I, hipStream_t s) {
+  if (q.format != QFormat::kFp8 || !tile_fp8_shape_ok(H, I)) return hipErrorInvalidValue;
+  QTileArgs a{{g.group_offsets, nullptr, g.tiles, g.counters, g.max_rows, w, h, y_rows, 1, nullptr, H, I,
+               (H + 255) / 256, 1, nullptr},
+              h,
+              static_cast<const uint8_t*>(q.down_codes),
+              nullptr,
+              static_cast<const float*>(q.down_scales),
+              nullptr};
+  down_tile_fp8_kernel<<<grid_for(g.max_tiles, a.p.n_ntiles), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -170,12 +170,29 @@ hipError_t launch_f16_rows(const uint16_t* x, uint16_t* y16, int64_t rows, int c
 // multiples of 128, at most 8192).
 bool qshape_ok(QFormat f, int H, int I);
 // h16[r, I] (f16, same column order) = SiLU(a Wg^T) * (a Wu^T), a = x16 rows (x_rows of them) through
-// row_index; plus the shared expert's h rows (bf16) when sh is given.
+// row_index; plus the shared expert's h rows (bf16) when sh is given.  Groups g < n_routed of the plan
+// are routed experts (a plan that also lists the shared expert's rows as group n_routed leaves that
+// group to sh).  small_only: only the plan's small groups (active[n_large ..)), and the shared expert
+// only if it has at most g.stream_rows rows; the tile kernels take the rest.
 hipError_t launch_gateup_q_stream(const Groups& g, const QWeights& w, const uint16_t* x16, int64_t x_rows,
-                                  uint16_t* h16, const SharedBf16* sh, int H, int I, hipStream_t s);
-// y_rows[r, H] (bf16) = h16[r] Wd^T, plus the shared expert's rows when sh is given.
+                                  uint16_t* h16, const SharedBf16* sh, int H, int I, int n_routed, bool small_only,
+                                  hipStream_t s);
+// y_rows[r, H] (bf16) = h16[r] Wd^T, plus the shared expert's rows when sh is given (as above).
 hipError_t launch_down_q_stream(const Groups& g, const QWeights& w, const uint16_t* h16, uint16_t* y_rows,
-                                const SharedBf16* sh, int H, int I, hipStream_t s);
+                                const SharedBf16* sh, int H, int I, int n_routed, bool small_only, hipStream_t s);
+
+// grouped SwiGLU, FP8 routed experts, many rows per group (tile kernels) -------------------
+// The groups of the tile list: routed groups from E4M3 codes and block scales (A rows binary16 in
+// the order of launch_f16_rows, h likewise), the shared group (g == w.shared_group) in bf16 from
+// w.s_* (A: x or h rows in bf16).  H, I multiples of 128, at most 8192.
+bool tile_fp8_shape_ok(int H, int I);
+// h[r, I] = SiLU(a Wg^T) * (a Wu^T): routed rows binary16 from x16 rows, shared rows bf16 from x rows
+// (both through row_index).
+hipError_t launch_gateup_tile_fp8(const Groups& g, const Weights& w, const QWeights& q, const uint16_t* x,
+                                  const uint16_t* x16, uint16_t* h, int H, int I, hipStream_t s);
+// y_rows[r, H] (bf16) = h[r] Wd^T (h binary16 for routed rows, bf16 for the shared group's rows).
+hipError_t launch_down_tile_fp8(const Groups& g, const Weights& w, const QWeights& q, const uint16_t* h,
+                                uint16_t* y_rows, int H, int I, hipStream_t s);
 
 // grouped SwiGLU, fp32 (plain kernels) ---------------------------------------------
 hipError_t launch_gateup_f32(const Groups& g, const Weights& w, const float* x, float* h, int H, int I,

@@ -310,11 +310,21 @@ struct QuantWs {
   void* y_rows;
 };
 
-QuantWs carve_quant(Carver& cv, const moe_config* c, int64_t T) {
+// Whether a quantized forward runs its larger groups on the tile kernels (FP8, many rows per group);
+// their plan then also lists the shared expert's rows, as group E.
+bool quant_tiles(const moe_config* c, moe::QFormat f, int64_t T) {
+  const bool shared = c->n_shared_experts == 1;
+  const int64_t rows = T * c->top_k + (shared ? T : 0);
+  return f == moe::QFormat::kFp8 && moe::tile_fp8_shape_ok(c->hidden_size, c->moe_intermediate_size) &&
+         !use_stream_kernels(rows, c->n_routed_experts + (shared ? 1 : 0));
+}
+
+QuantWs carve_quant(Carver& cv, const moe_config* c, int64_t T, moe::QFormat f) {
   const int H = c->hidden_size, I = c->moe_intermediate_size, E = c->n_routed_experts, K = c->top_k;
   const bool shared = c->n_shared_experts == 1;
   const int64_t P = T * K;
   const int64_t rows = P + (shared ? T : 0);
+  const bool tiles = quant_tiles(c, f, T);
   QuantWs w{};
   w.ids = cv.take<int32_t>(P);
   w.weights = cv.take<float>(P);
@@ -325,7 +335,7 @@ QuantWs carve_quant(Carver& cv, const moe_config* c, int64_t T) {
   w.perm_scratch = cv.take<int32_t>(moe::permute_scratch_ints(P, E));
   w.x16 = cv.take<uint16_t>(T * H);
   w.h = cv.take<uint16_t>(rows * I);
-  w.routed = carve_plan(cv, E, P);
+  w.routed = tiles ? carve_plan(cv, E + (shared ? 1 : 0), rows) : carve_plan(cv, E, P);
   w.y_rows = cv.take<uint16_t>(rows * H);
   return w;
 }
@@ -409,7 +419,7 @@ int forward_quant(const char* name, const moe_config* cfg, int64_t T, const void
   const int H = cfg->hidden_size, I = cfg->moe_intermediate_size, E = cfg->n_routed_experts, K = cfg->top_k;
   const int64_t P = T * K;
   Carver cv(workspace);
-  QuantWs w = carve_quant(cv, cfg, T);
+  QuantWs w = carve_quant(cv, cfg, T, qw.format);
   if ((st = check_ws(workspace, workspace_bytes, cv.used))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* ids = topk_ids_out ? topk_ids_out : w.ids;
@@ -423,7 +433,9 @@ int forward_quant(const char* name, const moe_config* cfg, int64_t T, const void
   });
   if (e != hipSuccess) return device_status(e, "top-k");
   // routed experts: groups 0..E-1 over rows [0, P); the shared expert (bf16) runs in the same
-  // launches over rows [P, P + T) (row P + t is token t)
+  // launches over rows [P, P + T) (row P + t is token t).  With many rows per group (FP8) the plan
+  // lists the shared rows as group E too, and the tile kernels take every group of more than
+  // stream_rows rows, the stream kernels the others.
   moe::Groups gr = w.routed;
   gr.group_offsets = w.offsets;
   gr.row_index = w.row_token;
@@ -458,12 +470,36 @@ int forward_quant(const char* name, const moe_config* cfg, int64_t T, const void
   uint16_t* y_rows = static_cast<uint16_t*>(w.y_rows);
   if (!fused) e = timed("plan", s, [&] { return moe::launch_plan(gr, s); });
   const bool q4 = qw.format == moe::QFormat::kInt4;
-  if (e == hipSuccess)
-    e = timed(q4 ? "gateup_q4" : "gateup_fp8", s,
-              [&] { return moe::launch_gateup_q_stream(gr, qw, w.x16, T, w.h, shp, H, I, s); });
-  if (e == hipSuccess)
-    e = timed(q4 ? "down_q4" : "down_fp8", s,
-              [&] { return moe::launch_down_q_stream(gr, qw, w.h, y_rows, shp, H, I, s); });
+  if (quant_tiles(cfg, qw.format, T)) {
+    moe::Weights wsh;  // the shared expert's bf16 weights for its tiles
+    if (shared) {
+      wsh.s_gate = ws_gate;
+      wsh.s_up = ws_up;
+      wsh.s_down = ws_down;
+      wsh.shared_group = E;
+    }
+    const bool small = gr.stream_rows > 0;
+    if (e == hipSuccess && small)
+      e = timed("gateup_fp8", s,
+                [&] { return moe::launch_gateup_q_stream(gr, qw, w.x16, T, w.h, shp, H, I, E, true, s); });
+    if (e == hipSuccess)
+      e = timed("gateup_tile_fp8", s, [&] {
+        return moe::launch_gateup_tile_fp8(gr, wsh, qw, static_cast<const uint16_t*>(x), w.x16, w.h, H, I, s);
+      });
+    if (e == hipSuccess && small)
+      e = timed("down_fp8", s,
+                [&] { return moe::launch_down_q_stream(gr, qw, w.h, y_rows, shp, H, I, E, true, s); });
+    if (e == hipSuccess)
+      e = timed("down_tile_fp8", s,
+                [&] { return moe::launch_down_tile_fp8(gr, wsh, qw, w.h, y_rows, H, I, s); });
+  } else {
+    if (e == hipSuccess)
+      e = timed(q4 ? "gateup_q4" : "gateup_fp8", s,
+                [&] { return moe::launch_gateup_q_stream(gr, qw, w.x16, T, w.h, shp, H, I, E, false, s); });
+    if (e == hipSuccess)
+      e = timed(q4 ? "down_q4" : "down_fp8", s,
+                [&] { return moe::launch_down_q_stream(gr, qw, w.h, y_rows, shp, H, I, E, false, s); });
+  }
   if (e != hipSuccess) return device_status(e, "experts");
 
   e = timed("combine", s, [&] {
@@ -547,7 +583,7 @@ size_t moe_workspace_size(const moe_config* cfg, int32_t op, int64_t rows, int32
       if (check_config_quant(cfg, op == MOE_OP_FORWARD_Q4 ? moe::QFormat::kInt4 : moe::QFormat::kFp8) != MOE_OK ||
           check_tokens(rows, cfg) != MOE_OK)
         return 0;
-      carve_quant(cv, cfg, rows);
+      carve_quant(cv, cfg, rows, op == MOE_OP_FORWARD_Q4 ? moe::QFormat::kInt4 : moe::QFormat::kFp8);
       break;
     default:
       fail(MOE_ERR_INVALID_ARG, "unknown op %d", op);

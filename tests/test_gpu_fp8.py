@@ -2,13 +2,20 @@
 
 The oracle evaluates the layer in float64 on the dequantized weights (E4M3 value times its 128 x 128
 block scale, from the host quantizer's codes and scales); the GPU multiplies in binary16 with fp32
-accumulation, so the bf16 output bar (per-row relative L2 <= 2e-2) applies.  Cases: small sizes on
-every token (several 16-row passes per expert and a ragged tail; no shared expert; odd numbers of
-128-blocks, where the down kernel runs one column block per work-group and the K loops end on
-padded steps; a long W_down row whose scales do not fit the chained down kernel; hidden_size at
-its 8192 limit; more than 4096 (token, expert) pairs), and the full decode shape on sampled tokens.
-The two quantizers (device for the GPU inputs, host for the oracle) are checked bit-exact against
-each other.
+accumulation, so the bf16 output bar (per-row relative L2 <= 2e-2) applies.
+
+Two kernel families run the experts: with at most 4 rows per group on average the weight-stream
+kernels take every group; otherwise the tile kernels take the groups of more than 32 rows (all of
+them with fewer than 16 groups), the shared expert's included, and the stream kernels the rest.
+Cases, every token: stream-only shapes (no shared expert; a long W_down row whose scales do not fit
+the chained down kernel; hidden_size at its 8192 limit; a skewed routing whose hot experts take
+several 16-row passes; a single token) and tile shapes (groups of one or more 256-row tiles with
+ragged tails; odd numbers of 128-blocks and a last output slab of 128 columns; K loops long enough
+for the unrolled steady state and short ones that are all tail; small groups beside tiles; a shared
+expert small enough for the stream kernels beside an empty tile list; no shared expert; more than
+4096 (token, expert) pairs); and the full decode and prefill shapes (every decode token, a seeded
+sample of prefill tokens, in one oracle pass).  The two quantizers (device for the GPU inputs, host
+for the oracle) are checked bit-exact against each other.
 """
 import numpy as np
 import pytest
@@ -17,7 +24,8 @@ import moe_layer_forward_amd as moe
 from moe_layer_forward_amd import synth
 from moe_layer_forward_amd import workloads as wl
 
-from parity import Y_TOL, check_routing, oracle_forward_tokens, oracle_route, rel_l2, to_np
+from parity import (Y_TOL, check_routing, oracle_forward_tokens, oracle_outputs_shared_weights, oracle_route, rel_l2,
+                    to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,17 +59,34 @@ def _check(w, t, tokens=None, bias=None):
 
 
 @pytest.mark.parametrize("T,H,I,E,K,shared", [
-    (70, 512, 256, 8, 2, 1),     # ~17.5 rows per expert: two 16-row passes, ragged
+    # stream kernels only (at most 4 rows per group)
     (5, 768, 512, 40, 4, 0),     # one or two rows per expert, no shared expert; chained down blocks
-    (40, 384, 640, 12, 3, 1),    # 3 x 5 blocks: one down column block per work-group, padded K steps
     (8, 256, 4608, 8, 2, 1),     # W_down rows of 36 blocks: scales too many for the chained down kernel
     (6, 8192, 256, 8, 2, 1),     # hidden_size 8192: 64 gate/up scale blocks per row, one per lane
-    (200, 256, 512, 16, 2, 1),   # the shared expert's 200 rows in seven 32-row passes
+    # tile kernels
+    (70, 512, 256, 8, 2, 1),     # ~17.5 rows per expert in one partial tile each; K loops all tail
+    (40, 384, 640, 12, 3, 1),    # 3 x 5 blocks: a down output slab of 128 columns (its scales clamp)
+    (600, 896, 640, 8, 2, 1),    # ~150 rows per expert, 600 shared rows in 3 tiles (ragged); gate/up
+                                 # K loop through the steady state, down (10 steps) all tail
+    (256, 1024, 768, 32, 4, 1),  # 17 groups or more: groups of <= 32 rows on the stream kernels
+                                 # beside tiles; both K loops through the steady state
+    (32, 512, 256, 16, 2, 1),    # every group small, the 32-row shared expert too: empty tile list
+    (300, 512, 384, 8, 3, 0),    # tiles without a shared expert
+    (200, 256, 512, 16, 2, 1),   # the shared expert's 200 rows in one tile
     (600, 256, 256, 32, 8, 1),   # 4800 pairs: the chunked permutation, separate binary16 rows and plan
-], ids=["passes", "no_shared", "odd_blocks", "long_down_rows", "h_8192", "shared_passes", "many_pairs"])
+], ids=["no_shared", "long_down_rows", "h_8192", "tile_ragged", "odd_blocks", "tile_steady",
+        "small_beside_tiles", "empty_tile_list", "tile_no_shared", "shared_tile", "many_pairs"])
 def test_fp8_small_every_token(T, H, I, E, K, shared):
     _torch()
     w = wl.custom(f"fp8_{T}", T, H, I, E, K, x_seed=41, w_seed=42, n_shared=shared, quant="fp8")
+    _check(w, wl.device_inputs(w))
+
+
+def test_fp8_stream_skewed_passes():
+    # at most 4 rows per group on average (stream kernels only), hot experts of up to 32 rows: two
+    # 16-row passes
+    _torch()
+    w = wl.custom("fp8_stream_skew", 32, 512, 256, 40, 4, x_seed=49, w_seed=50, routing="skew", quant="fp8")
     _check(w, wl.device_inputs(w))
 
 
@@ -120,14 +145,41 @@ def test_fp8_rejects_f32_and_unsupported_sizes():
         assert e.value.status == moe.MOE_ERR_UNSUPPORTED
 
 
-@pytest.mark.timeout(900)
-def test_decode_fp8_full_size():
+PREFILL_SAMPLE = 256  # seeded prefill tokens whose outputs are compared
+
+
+@pytest.mark.timeout(1200)
+def test_fp8_full_size():
+    """decode_fp8 (every token) and prefill_fp8 (routing of every token, outputs of a seeded sample:
+    every expert, groups of ~170 rows on the tile kernels) at the full shape, one weight set, each in
+    the benchmark's launch configuration (one moe_forward_fp8 call)."""
     torch = _torch()
-    w = wl.WORKLOADS["decode_fp8"]
-    t = wl.device_inputs(w)
-    torch.cuda.synchronize()
-    y, ids, wts = _check(w, t)  # every token
-    x, ids_ref, w_ref, gap, _ = oracle_route(w, np.arange(w.T))
-    check_routing(to_np(ids), to_np(wts), ids_ref, w_ref, gap)
+    wd, wp = wl.WORKLOADS["decode_fp8"], wl.WORKLOADS["prefill_fp8"]
+    t = wl.device_weights(wd)
+    runs = {}
+    for w in (wd, wp):
+        print(f"running {w.name} (T={w.T}) on the GPU", flush=True)
+        tw = dict(t, **wl.device_activations(w))
+        y, ids, wts = moe.moe_forward_fp8(moe.config_for(w), tw["x"], tw["w_router"], {k: tw[k] for k in moe.QUANT_KEYS},
+                                          tw.get("ws_gate"), tw.get("ws_up"), tw.get("ws_down"), return_routing=True)
+        torch.cuda.synchronize()
+        runs[w.name] = (to_np(y), to_np(ids), to_np(wts))
+        del tw, y, ids, wts
     del t
     torch.cuda.empty_cache()
+    # routing of every prefill token
+    _, ids_p, wts_p = runs[wp.name]
+    x, ids_ref, w_ref, gap, _ = oracle_route(wp, np.arange(wp.T))
+    check_routing(ids_p, wts_p, ids_ref, w_ref, gap)
+    rng = np.random.default_rng(20261204)
+    sample = np.sort(rng.choice(wp.T, PREFILL_SAMPLE, replace=False))
+    cases = [(wd, np.arange(wd.T), runs[wd.name][1]), (wp, sample, ids_p[sample])]
+    refs = oracle_outputs_shared_weights(cases)
+    for (w, tokens, ids_g), (y_ref, ids_r, w_r, gap_r) in zip(cases, refs):
+        y_g, _, w_g = runs[w.name]
+        check_routing(ids_g, w_g[tokens], ids_r, w_r, gap_r)
+        err = rel_l2(y_g[tokens], y_ref)
+        print(f"{w.name}: outputs of {len(tokens)} tokens checked, max rel L2 {err.max():.3g}, "
+              f"p99 {np.percentile(err, 99):.3g}", flush=True)
+        assert np.isfinite(y_g).all()
+        assert err.max() <= Y_TOL["bf16"]
