@@ -579,9 +579,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // The routed experts' weights as E4M3 codes with one fp32 scale per 128 x 128 block (the storage the
 // weight-stream kernels read; see QWeights).  Same tiles, waves, LDS rings and dealing; what changes:
 //   * A B stage holds 256 weight rows x 128 codes: 128 inputs (one scale block along K, whole cache
-//     lines) for two K steps of 64.  Each half (the 128 rows of pieces 0-1, or of pieces 2-3) is
-//     issued 4 steps before its first step, so the in-order vector-memory count never makes a step
-//     wait for weights a later step needs.
+//     lines) for two K steps of 64.  LDS holds three stages of token rows and two of codes (the same
+//     5 x 32 KiB), so token rows are loaded two steps ahead and each K block two steps before the
+//     step that first reads it.
 //   * The token rows (A) are binary16 with each group of 8 inputs in the order 0,4,1,5,2,6,3,7, and
 //     v_mfma_f32_16x16x32_f16 runs the products.  Per step a lane reads 16 codes of each of its 4
 //     weight rows in one 16-byte LDS read (inputs 16 g .. 16 g + 15 of the step, g = lane / 16) and
@@ -624,16 +624,19 @@ __device__ __forceinline__ LaneScale lane_scale(const float* blocks, int nkb) {
   return LaneScale{s, h | (h << 16)};
 }
 
-// The scales of one K block, uniform over the wave (gate/up: [0] gate rows, [1] up rows).
+// The scales of one K block, uniform over the wave: NS sets (gate/up: [0] gate rows, [1] up rows; down:
+// one).
+template <int NS>
 struct StepScale {
-  float s[2];
-  f16x2 m[2];
+  float s[NS];
+  f16x2 m[NS];
 };
 
-__device__ __forceinline__ StepScale step_scale(const LaneScale (&ls)[2], int j) {
-  StepScale r;
+template <int NS>
+__device__ __forceinline__ StepScale<NS> step_scale(const LaneScale (&ls)[NS], int j) {
+  StepScale<NS> r;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < NS; ++i) {
     r.s[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[i].s), j));
     r.m[i] = __builtin_bit_cast(f16x2, (uint32_t)__builtin_amdgcn_readlane((int)ls[i].m2, j));
   }
@@ -682,17 +685,14 @@ __device__ __forceinline__ uint32_t qb_offset(int j, int64_t wrow, int K) {
   return (uint32_t)(wrow * K + 16 * chunk);
 }
 
-// Half HF of K block s / 2 (the loads of step index s = 2 b + HF): B pieces 2 HF and 2 HF + 1.
-template <int HF>
-__device__ __forceinline__ void issue_qb(const Loads& o, int s, char* stage) {
+// K block b of the codes (128 inputs) of all 256 weight rows of the tile: B pieces 0 .. 3.
+__device__ __forceinline__ void issue_qblock(const Loads& o, int b, char* stage) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t kb = (uint32_t)(s >> 1) * kRowBytes;
+  const uint32_t kb = (uint32_t)b * kRowBytes;
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj) {
-    const int j = 2 * HF + jj;
+  for (int j = 0; j < kBLoads; ++j)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(operand_rsrc(o.b_base[j]), (LdsPtr)(stage + (w + kWaves * j) * 1024), 16,
                                              o.b_off[j] + kb, 0, 0, 0);
-  }
 }
 
 // Weights carried from one K step to the next: the first k-substep's decoded fragments of the 4 column
@@ -723,9 +723,9 @@ __device__ __forceinline__ void read_codes(const char* Bs, const QFrag& f, u32x4
 // Each fragment's MFMAs are independent of the decoding placed beside them.  Column block s uses scale
 // set GU && s >= 2 (the up rows).  kFirst: the step decodes its own first substep first (the tile's
 // first step).  HF, HFN: this and the next step's half of their B stages.
-template <int NBW, int HF, int HFN, bool GU, bool kFirst>
+template <int NBW, int HF, int HFN, bool GU, bool kFirst, int NS = GU ? 2 : 1>
 __device__ __forceinline__ void q_compute_step(const char* As, const char* Bs, const char* Bn, bool has_next,
-                                               const QFrag& f, const StepScale& sc, const StepScale& scn,
+                                               const QFrag& f, const StepScale<NS>& sc, const StepScale<NS>& scn,
                                                QCarry& c, f32x4 (&acc)[NBW > 0 ? NBW : 1][4]) {
   if constexpr (NBW > 0) {
     constexpr int NF = 2 * NBW;
@@ -792,48 +792,55 @@ struct QRings {
   char* b[2];
 };
 
-// One K step kt (kt % 12 == D) of the FP8 tiles.  Per wave the vector-memory order is
-// B(0) A(0) B(1) A(1) B(2) | A(2) B(3) | A(3) B(4) | ... with B(s) the half-stage of step index s:
-// step kt issues A(kt + 2) and B(kt + 3), and when it starts only the loads of step kt - 1 (A(kt + 1),
-// B(kt + 2)) may still be in flight, so every load has about two steps to land.  After the barrier
-// A(kt) and B(kt + 1), i.e. the next step's half of its K block, are visible.  A(kt + 2) overwrites the
-// rows of step kt - 1; B(kt + 3) the K block two blocks earlier, whose codes were last read from LDS in
-// step kt - 1 or before (a block b is read in steps 2b - 1 and 2b, for the first substep of the step
-// after each).
-template <int NBW, int NAL, int D, bool kTail, bool GU, bool kFirst = false>
+// One K step kt (kt % 12 == D) of the FP8 tiles.  A K step reads 64 codes of every one of the 256
+// weight rows, so a K block (two steps) is loaded whole: block b at step 2 b - 3.  Per wave the
+// vector-memory order is Q(0) A(0) A(1) Q(1) | A(2) | A(3) Q(2) | A(4) | A(5) Q(3) | ... (Q(b): the 4
+// loads of block b): step kt issues A(kt + 2) and, when kt is odd, Q((kt + 3) / 2).  When step kt
+// starts, only the loads of step kt - 1 may still be in flight (A(kt + 1), and Q((kt + 2) / 2) when kt
+// is even), so A(kt) and the block of step kt + 1 have landed: after the barrier they are visible to
+// every wave, and the step reads the next step's codes during its own MFMAs.  A(kt + 2) overwrites the
+// rows of step kt - 1; Q(b) the block two earlier, whose codes were last read in step 2 b - 4.
+template <int NBW, int NAL, int D, bool kTail, bool GU, bool kFirst = false, int NS = GU ? 2 : 1>
 __device__ __forceinline__ void q_kstep(const Loads& o, int kt, int nk, const QRings& r, const QFrag& f,
-                                        const LaneScale (&ls)[2], QCarry& c, f32x4 (&acc)[NBW > 0 ? NBW : 1][4]) {
-  if (!kTail || kt + 2 < nk)
-    wait_vmcnt<NAL + 2>();
-  else if (kt + 1 < nk)
-    wait_vmcnt<NAL>();
-  else
-    wait_vmcnt<0>();
+                                        const LaneScale (&ls)[NS], QCarry& c, f32x4 (&acc)[NBW > 0 ? NBW : 1][4]) {
+  if constexpr (D % 2 == 0) {
+    if (!kTail || kt + 2 < nk)
+      wait_vmcnt<NAL + kBLoads>();
+    else if (kt + 1 < nk)
+      wait_vmcnt<NAL>();
+    else
+      wait_vmcnt<0>();
+  } else {
+    if (!kTail || kt + 1 < nk)
+      wait_vmcnt<NAL>();
+    else
+      wait_vmcnt<0>();
+  }
   block_sync_lds();
   if (!kTail || kt + 2 < nk) issue_a<NAL>(o, kt + 2, r.a[(D + 2) % 3]);
-  if (!kTail || kt + 3 < nk) issue_qb<(D + 1) % 2>(o, kt + 3, r.b[((D + 3) / 2) % 2]);
+  if constexpr (D % 2 == 1) {
+    if (!kTail || kt + 3 < nk) issue_qblock(o, (kt + 3) / 2, r.b[((D + 3) / 2) % 2]);
+  }
   const bool has_next = !kTail || kt + 1 < nk;
-  const StepScale sc = step_scale(ls, kt >> 1);
-  const StepScale scn = step_scale(ls, has_next ? (kt + 1) >> 1 : kt >> 1);
+  const StepScale<NS> sc = step_scale(ls, kt >> 1);
+  const StepScale<NS> scn = step_scale(ls, has_next ? (kt + 1) >> 1 : kt >> 1);
   __builtin_amdgcn_sched_barrier(0);
   q_compute_step<NBW, D % 2, (D + 1) % 2, GU, kFirst>(r.a[D % 3], r.b[(D / 2) % 2], r.b[((D + 1) / 2) % 2], has_next,
                                                       f, sc, scn, c, acc);
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int NBW, int NAL, bool GU>
+template <int NBW, int NAL, bool GU, int NS = GU ? 2 : 1>
 __device__ __forceinline__ void q_kloop(const Loads& o, int nk, const QRings& r, const QFrag& f,
-                                        const LaneScale (&ls)[2], f32x4 (&acc)[NBW > 0 ? NBW : 1][4]) {
+                                        const LaneScale (&ls)[NS], f32x4 (&acc)[NBW > 0 ? NBW : 1][4]) {
   // prologue in the steady state's issue order (nk is even: whole K blocks), fenced
-  issue_qb<0>(o, 0, r.b[0]);
+  issue_qblock(o, 0, r.b[0]);
   __builtin_amdgcn_sched_barrier(0);
   issue_a<NAL>(o, 0, r.a[0]);
   __builtin_amdgcn_sched_barrier(0);
-  issue_qb<1>(o, 1, r.b[0]);
-  __builtin_amdgcn_sched_barrier(0);
   issue_a<NAL>(o, 1, r.a[1]);
   __builtin_amdgcn_sched_barrier(0);
-  if (nk > 2) issue_qb<0>(o, 2, r.b[1]);
+  if (nk > 2) issue_qblock(o, 1, r.b[1]);
   __builtin_amdgcn_sched_barrier(0);
   QCarry c;
   q_kstep<NBW, NAL, 0, true, GU, true>(o, 0, nk, r, f, ls, c, acc);
@@ -845,7 +852,7 @@ __device__ __forceinline__ void q_kloop(const Loads& o, int nk, const QRings& r,
       q_kstep<NBW, NAL, (j + 1) % 12, false, GU>(o, kt + j, nk, r, f, ls, c, acc);
     });
   }
-  // the last 0 .. 13 steps (kt % 12 == 1 here)
+  // the last 3 .. 14 steps, or all of a short loop (kt % 12 == 1 here)
   while (kt < nk) {
     bool done = false;
     static_for<12>([&](auto ic) {
@@ -858,8 +865,8 @@ __device__ __forceinline__ void q_kloop(const Loads& o, int nk, const QRings& r,
   }
 }
 
-template <int NBW, int NAL, bool GU, class Epilogue>
-__device__ __forceinline__ void q_tile_body(const Loads& o, const QRings& r, const QFrag& f, const LaneScale (&ls)[2],
+template <int NBW, int NAL, bool GU, class Epilogue, int NS = GU ? 2 : 1>
+__device__ __forceinline__ void q_tile_body(const Loads& o, const QRings& r, const QFrag& f, const LaneScale (&ls)[NS],
                                             const Epilogue& epilogue) {
   f32x4 acc[NBW > 0 ? NBW : 1][4];
 #pragma unroll
@@ -956,8 +963,7 @@ __device__ __forceinline__ void down_fp8_item(const QTileArgs& q, const Rings& r
   const int nkb = I / 128;
   int rb = (n0 + 64 * wc) / 128;
   if (rb > H / 128 - 1) rb = H / 128 - 1;
-  const LaneScale l0 = lane_scale(q.scales0 + ((int64_t)t.g * (H / 128) + rb) * nkb, nkb);
-  const LaneScale ls[2] = {l0, l0};
+  const LaneScale ls[1] = {lane_scale(q.scales0 + ((int64_t)t.g * (H / 128) + rb) * nkb, nkb)};
 
   const int b_rows[4] = {64 * wc, 64 * wc + 16, 64 * wc + 32, 64 * wc + 48};
   const QFrag f = make_qfrag(wr, b_rows);

@@ -11,9 +11,10 @@ Cases, every token: stream-only shapes (no shared expert; a long W_down row whos
 the chained down kernel; hidden_size at its 8192 limit; a skewed routing whose hot experts take
 several 16-row passes; a single token) and tile shapes (groups of one or more 256-row tiles with
 ragged tails; odd numbers of 128-blocks and a last output slab of 128 columns; K loops long enough
-for the unrolled steady state and short ones that are all tail; small groups beside tiles; a shared
-expert small enough for the stream kernels beside an empty tile list; no shared expert; more than
-4096 (token, expert) pairs); and the full decode and prefill shapes (every decode token, a seeded
+for the unrolled steady state and short ones that are all tail; small groups beside tiles, also while
+other work loads HBM concurrently; a shared expert small enough for the stream kernels beside an
+empty tile list; no shared expert; more than 4096 (token, expert) pairs); and the full decode and
+prefill shapes (every decode token, a seeded
 sample of prefill tokens, in one oracle pass).  The two quantizers (device for the GPU inputs, host
 for the oracle) are checked bit-exact against each other.
 """
@@ -80,6 +81,38 @@ def test_fp8_small_every_token(T, H, I, E, K, shared):
     _torch()
     w = wl.custom(f"fp8_{T}", T, H, I, E, K, x_seed=41, w_seed=42, n_shared=shared, quant="fp8")
     _check(w, wl.device_inputs(w))
+
+
+def test_fp8_tiles_under_concurrent_memory_traffic():
+    # the tile kernels' loads land late when other work loads HBM: each call runs while a torch stream
+    # copies 1 GiB buffers concurrently, and every call must match the oracle (a K step reads every
+    # weight row of its K block, so the whole block has to have landed, not only part of its rows)
+    torch = _torch()
+    w = wl.custom("fp8_traffic", 256, 1024, 768, 32, 4, x_seed=41, w_seed=42, quant="fp8")
+    t = wl.device_inputs(w)
+    big = torch.empty(256 << 20, dtype=torch.float32, device="cuda")
+    big2 = torch.empty_like(big)
+    side = torch.cuda.Stream()
+    cfg = moe.config_for(w)
+    y_ref = None
+    for rep in range(3):
+        ws = moe.alloc_workspace(cfg, moe.MOE_OP_FORWARD_FP8, w.T)
+        ws.fill_(0)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            for _ in range(12):
+                big2.copy_(big)
+        y, ids, wts = moe.moe_forward_fp8(cfg, t["x"], t["w_router"], {k: t[k] for k in moe.QUANT_KEYS},
+                                          t["ws_gate"], t["ws_up"], t["ws_down"], return_routing=True, workspace=ws)
+        torch.cuda.synchronize()
+        if y_ref is None:
+            tokens = np.arange(w.T)
+            y_ref, ids_ref, w_ref, gap = oracle_forward_tokens(w, tokens, ids_gpu=to_np(ids))
+            check_routing(to_np(ids), to_np(wts), ids_ref, w_ref, gap)
+        err = rel_l2(to_np(y), y_ref)
+        print(f"fp8 under traffic, call {rep}: max rel L2 {err.max():.3g}", flush=True)
+        assert err.max() <= Y_TOL["bf16"]
+    del big, big2
 
 
 def test_fp8_stream_skewed_passes():
