@@ -67,6 +67,7 @@ struct TileArgs {
   int H, I, n_ntiles;
   int n_ksplit;  // down: K ranges per output tile (partial sums go to part, then a reduction kernel)
   float* part;   // [n_ksplit, max_rows, H] fp32 when n_ksplit > 1
+  int tile_m;    // rows per row tile of the plan (kTileM, or kTileMFp8 for the FP8 tiles)
 };
 
 struct TileRows {
@@ -133,7 +134,7 @@ __device__ __forceinline__ bool tile_of(const TileArgs& p, int& nt, int& ks, Til
   if (r1 > p.max_rows) r1 = p.max_rows;
   if (r1 < r0) r1 = r0;
   t.rbeg = r0 + m0;
-  t.rend = t.rbeg + kTileM < r1 ? t.rbeg + kTileM : r1;
+  t.rend = t.rbeg + p.tile_m < r1 ? t.rbeg + p.tile_m : r1;
   return t.rbeg < t.rend;
 }
 
@@ -151,6 +152,7 @@ struct Loads {
   const char* b_base[kBLoads];  // B piece w + 8j: its weight tensor (uniform)
   uint32_t b_off[kBLoads];
   int skew, nk;              // step kt loads K step (kt + skew) mod nk (uniform over the work-group)
+  int wave;                  // w, uniform: the LDS destinations derive from it, not from threadIdx
 };
 
 typedef __amdgpu_buffer_rsrc_t Rsrc;
@@ -172,7 +174,7 @@ __device__ __forceinline__ uint32_t kbytes(const Loads& o, int kt) {
 
 template <int NAL>
 __device__ __forceinline__ void issue_a(const Loads& o, int kt, char* stage) {
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = o.wave;
   const uint32_t kb = kbytes(o, kt);
   const Rsrc rs = operand_rsrc(o.a_base);
 #pragma unroll
@@ -182,7 +184,7 @@ __device__ __forceinline__ void issue_a(const Loads& o, int kt, char* stage) {
 }
 
 __device__ __forceinline__ void issue_b(const Loads& o, int kt, char* stage) {
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = o.wave;
   const uint32_t kb = kbytes(o, kt);
 #pragma unroll
   for (int j = 0; j < kBLoads; ++j)
@@ -315,14 +317,16 @@ __device__ __forceinline__ void tile_body(const Loads& o, const Rings& r, const 
 // blocks: wave row wr takes ceil((nblk - wr) / 2) of them, and the 2 nblk A pieces of 8 rows are spread
 // over the 8 waves, ceil(nblk / 4) each.  One instance per pair that a row count of 1 .. 256 produces;
 // device pass only (these instances are device code).
-template <class Body>
+template <int kMaxNbw = 8, class Body>
 __device__ __forceinline__ void run_tile(int nblk, int wr, const Body& body) {
   const int nbw = (nblk - wr + 1) / 2;
   const int nal = (nblk + 3) / 4;
 #if defined(__HIP_DEVICE_COMPILE__)
 #define MOE_TILE_CASE(B, A) \
   if (nbw == B && nal == A) return body(std::integral_constant<int, B>{}, std::integral_constant<int, A>{});
-  MOE_TILE_CASE(8, 4)
+  if constexpr (kMaxNbw >= 8) {
+    MOE_TILE_CASE(8, 4)
+  }
   MOE_TILE_CASE(7, 4)
   MOE_TILE_CASE(6, 4)
   MOE_TILE_CASE(6, 3)
@@ -441,6 +445,7 @@ __device__ __forceinline__ void gateup_bf16_item(const TileArgs& p, const Rings&
   const int h0 = nt * 128;  // first h column of the tile; B tile rows 0-127 gate, 128-255 up
 
   Loads o;
+  o.wave = w;
   o.a_base = reinterpret_cast<const char*>(p.a);
   a_offsets(o, H, [&](int rl) -> int64_t {
     const int64_t r = t.rbeg + rl;
@@ -497,6 +502,7 @@ __device__ __forceinline__ void down_bf16_item(const TileArgs& p, const Rings& r
   // this item's K range [k0, k0 + kc) of the h rows and of W_down's rows
   const int kc = I / p.n_ksplit, k0 = ks * kc;
   Loads o;
+  o.wave = w;
   o.a_base = reinterpret_cast<const char*>(p.a + k0);
   a_offsets(o, I, [&](int rl) -> int64_t {
     const int64_t r = t.rbeg + rl;
@@ -510,10 +516,10 @@ __device__ __forceinline__ void down_bf16_item(const TileArgs& p, const Rings& r
   }
   // W_down rows a multiple of 4 KiB apart put the same K step of all 256 rows on few HBM channels:
   // the column slabs then start their K loops at different steps (and wrap around).  Only while the
-  // tile's h block is small (I <= 4096: at most 2 MiB): the slabs of a tile share it through L2 only
-  // while they walk K together.
+  // tile's block of h for this K range is small (kc <= 4096: at most 2 MiB): the slabs of a tile
+  // share it through L2 only while they walk K together.
   o.nk = kc / kBK;
-  o.skew = (I * 2) % 4096 == 0 && I <= 4096 ? nt * 5 % o.nk : 0;
+  o.skew = (I * 2) % 4096 == 0 && kc <= 4096 ? nt * 5 % o.nk : 0;
 
   const int b_rows[4] = {64 * wc, 64 * wc + 16, 64 * wc + 32, 64 * wc + 48};
   const Frag f = make_frag(wr, b_rows);
@@ -596,6 +602,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 //     below 2^-14 absolute).  A wave's 64 weight rows lie in one 128-row scale block, so its scales
 //     are one per K block: lane j holds K block j's (at most 64 blocks, K <= 8192).
 //   * The shared expert (bf16 weights) is a group of the same tile list: its tiles run the bf16 body.
+//   * Row tiles are 224 rows (kTileMFp8): at most 7 16-row blocks per wave, 112 accumulator VGPRs,
+//     so that the decode's registers fit beside them without spills (a spill reload inside the K
+//     loop waits for every load in flight).  A K2 prefill expert (~170 rows) is still one tile.
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -609,23 +618,27 @@ struct QTileArgs {
   const float* scales1;
 };
 
-// Lane j's block scale (K block j of the wave's 128-row block): s for the conversion and f16(m) twice.
+// Lane j's block scale s (K block j of the wave's 128-row block); 1.0 past the last block.
 struct LaneScale {
   float s;
-  uint32_t m2;
 };
 
 __device__ __forceinline__ LaneScale lane_scale(const float* blocks, int nkb) {
   const int lane = threadIdx.x & 63;
-  const float s = lane < nkb ? blocks[lane] : 1.f;
-  // m: s with its exponent field replaced by that of 1.0 (the sign stays with m)
-  const float m = __uint_as_float((__float_as_uint(s) & 0x807fffffu) | 0x3f800000u);
-  const uint32_t h = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)m);
-  return LaneScale{s, h | (h << 16)};
+  return LaneScale{lane < nkb ? blocks[lane] : 1.f};
+}
+
+// f16(m) twice, m = s with its exponent field replaced by that of 1.0 (the sign stays with m), from
+// the bits of s: the 23 mantissa bits rounded to nearest even into 10 (a carry gives 2.0 exactly).
+// Integer operations on a uniform value (scalar unit).
+__device__ __forceinline__ uint32_t mantissa_f16x2(uint32_t sb) {
+  const uint32_t mant = sb & 0x7fffffu;
+  const uint32_t h = (0x3c00u + ((mant + 0xfffu + ((mant >> 13) & 1u)) >> 13)) | ((sb >> 16) & 0x8000u);
+  return h | (h << 16);
 }
 
 // The scales of one K block, uniform over the wave: NS sets (gate/up: [0] gate rows, [1] up rows; down:
-// one).
+// one).  s goes to the conversion, which applies its power of two; m is the rest.
 template <int NS>
 struct StepScale {
   float s[NS];
@@ -637,8 +650,9 @@ __device__ __forceinline__ StepScale<NS> step_scale(const LaneScale (&ls)[NS], i
   StepScale<NS> r;
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
-    r.s[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[i].s), j));
-    r.m[i] = __builtin_bit_cast(f16x2, (uint32_t)__builtin_amdgcn_readlane((int)ls[i].m2, j));
+    const uint32_t sb = (uint32_t)__builtin_amdgcn_readlane(__float_as_int(ls[i].s), j);
+    r.s[i] = __uint_as_float(sb);
+    r.m[i] = __builtin_bit_cast(f16x2, mantissa_f16x2(sb));
   }
   return r;
 }
@@ -687,7 +701,7 @@ __device__ __forceinline__ uint32_t qb_offset(int j, int64_t wrow, int K) {
 
 // K block b of the codes (128 inputs) of all 256 weight rows of the tile: B pieces 0 .. 3.
 __device__ __forceinline__ void issue_qblock(const Loads& o, int b, char* stage) {
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = o.wave;
   const uint32_t kb = (uint32_t)b * kRowBytes;
 #pragma unroll
   for (int j = 0; j < kBLoads; ++j)
@@ -889,17 +903,21 @@ __device__ __forceinline__ void gateup_fp8_item(const QTileArgs& q, const Rings&
   const int h0 = nt * 128;
 
   Loads o;
+  o.wave = w;
   o.a_base = reinterpret_cast<const char*>(q.a16);
   a_offsets(o, H, [&](int rl) -> int64_t {
     const int64_t r = t.rbeg + rl;
     const int64_t rr = r < t.rend ? r : t.rbeg;
     return p.row_index ? (int64_t)p.row_index[rr] : rr;
   });
+  // pieces w, w + 8: gate rows h0 + 8 w .. and h0 + 64 + 8 w ..; w + 16, w + 24: the same up rows.  The
+  // piece's first row goes into its (uniform) base, so one lane offset serves all four (a lane's
+  // swizzled chunk is the same in each piece: the pieces are 64 rows apart).
+  const uint32_t b_lane = qb_offset(0, 8 * w + (lane >> 3), H);
 #pragma unroll
-  for (int j = 0; j < kBLoads; ++j) {  // pieces w, w + 8: gate rows; w + 16, w + 24: up rows
-    const int rl = (w + kWaves * j) * 8 + (lane >> 3);
-    o.b_base[j] = reinterpret_cast<const char*>(j < 2 ? cg : cu);
-    o.b_off[j] = qb_offset(j, h0 + (rl & 127), H);
+  for (int j = 0; j < kBLoads; ++j) {
+    o.b_base[j] = reinterpret_cast<const char*>(j < 2 ? cg : cu) + (int64_t)(h0 + 64 * (j & 1)) * H;
+    o.b_off[j] = b_lane;
   }
   o.nk = H / kBK;
   o.skew = 0;
@@ -931,7 +949,7 @@ __device__ __forceinline__ void gateup_fp8_item(const QTileArgs& q, const Rings&
     Out::store(rings, m_valid, h, I, rbeg, h0, I);
   };
   const QRings qr{{rings.a[0], rings.a[1], rings.b[0]}, {rings.b[1], rings.b[2]}};
-  run_tile((m_valid + 15) / 16, wr, [&](auto b, auto a) {
+  run_tile<kTileMFp8 / 32>((m_valid + 15) / 16, wr, [&](auto b, auto a) {
     q_tile_body<decltype(b)::value, decltype(a)::value, true>(o, qr, f, ls, epilogue);
   });
 }
@@ -946,16 +964,21 @@ __device__ __forceinline__ void down_fp8_item(const QTileArgs& q, const Rings& r
   const int n0 = nt * 256;
 
   Loads o;
+  o.wave = w;
   o.a_base = reinterpret_cast<const char*>(q.a16);
   a_offsets(o, I, [&](int rl) -> int64_t {
     const int64_t r = t.rbeg + rl;
     return r < t.rend ? r : t.rbeg;
   });
+  // piece w + 8 j: W_down rows n0 + 64 j + 8 w .. (first row in the uniform base, one lane offset for
+  // all four).  With H a multiple of 128 a piece lies wholly inside or past H; a piece past H (the
+  // last slab's pieces 2 and 3) re-reads the rows of piece j - 2, whose columns are never stored.
+  const uint32_t b_lane = qb_offset(0, 8 * w + (lane >> 3), I);
 #pragma unroll
-  for (int j = 0; j < kBLoads; ++j) {  // output columns past H re-read row n0, never stored
-    const int rl = (w + kWaves * j) * 8 + (lane >> 3);
-    o.b_base[j] = reinterpret_cast<const char*>(cd);
-    o.b_off[j] = qb_offset(j, n0 + rl < H ? n0 + rl : n0, I);
+  for (int j = 0; j < kBLoads; ++j) {
+    const int r0 = n0 + 64 * j < H ? n0 + 64 * j : n0 + 64 * (j - 2);
+    o.b_base[j] = reinterpret_cast<const char*>(cd) + (int64_t)r0 * I;
+    o.b_off[j] = b_lane;
   }
   o.nk = I / kBK;
   o.skew = 0;
@@ -987,7 +1010,7 @@ __device__ __forceinline__ void down_fp8_item(const QTileArgs& q, const Rings& r
     Out::store(rings, m_valid, y, H, rbeg, n0, H);
   };
   const QRings qr{{rings.a[0], rings.a[1], rings.b[0]}, {rings.b[1], rings.b[2]}};
-  run_tile((m_valid + 15) / 16, wr, [&](auto b, auto a) {
+  run_tile<kTileMFp8 / 32>((m_valid + 15) / 16, wr, [&](auto b, auto a) {
     q_tile_body<decltype(b)::value, decltype(a)::value, false>(o, qr, f, ls, epilogue);
   });
 }
@@ -1111,8 +1134,9 @@ int down_tile_ksplit(int64_t max_rows, int G, int H, int I) {
 
 hipError_t launch_gateup_tile_bf16(const Groups& g, const Weights& w, const uint16_t* x, uint16_t* h, int H, int I,
                                    hipStream_t s) {
+  if (g.tile_m != kTileM) return hipErrorInvalidValue;
   TileArgs p{g.group_offsets, g.row_index, g.tiles, g.counters, g.max_rows, w, x, h, 1, nullptr, H, I, I / 128,
-             1, nullptr};
+             1, nullptr, kTileM};
   gateup_tile_kernel<<<grid_for(g.max_tiles, p.n_ntiles), kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
@@ -1120,9 +1144,9 @@ hipError_t launch_gateup_tile_bf16(const Groups& g, const Weights& w, const uint
 hipError_t launch_down_tile_bf16(const Groups& g, const Weights& w, const uint16_t* h, void* y_rows, bool y_bf16,
                                  const float* row_scale, float* part, int H, int I, hipStream_t s) {
   const int split = down_tile_ksplit(g.max_rows, g.n_groups, H, I);
-  if (split > 1 && !part) return hipErrorInvalidValue;
+  if ((split > 1 && !part) || g.tile_m != kTileM) return hipErrorInvalidValue;
   TileArgs p{g.group_offsets, nullptr, g.tiles, g.counters, g.max_rows, w, h, y_rows, y_bf16 ? 1 : 0, row_scale,
-             H, I, (H + 255) / 256, split, part};
+             H, I, (H + 255) / 256, split, part, kTileM};
   down_tile_kernel<<<grid_for(g.max_tiles, p.n_ntiles, split), kThreads, 0, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || split == 1) return e;
@@ -1140,9 +1164,9 @@ bool tile_fp8_shape_ok(int H, int I) {
 
 hipError_t launch_gateup_tile_fp8(const Groups& g, const Weights& w, const QWeights& q, const uint16_t* x,
                                   const uint16_t* x16, uint16_t* h, int H, int I, hipStream_t s) {
-  if (q.format != QFormat::kFp8 || !tile_fp8_shape_ok(H, I)) return hipErrorInvalidValue;
+  if (q.format != QFormat::kFp8 || !tile_fp8_shape_ok(H, I) || g.tile_m != kTileMFp8) return hipErrorInvalidValue;
   QTileArgs a{{g.group_offsets, g.row_index, g.tiles, g.counters, g.max_rows, w, x, h, 1, nullptr, H, I, I / 128, 1,
-               nullptr},
+               nullptr, kTileMFp8},
               x16,
               static_cast<const uint8_t*>(q.gate_codes),
               static_cast<const uint8_t*>(q.up_codes),
@@ -1154,9 +1178,9 @@ hipError_t launch_gateup_tile_fp8(const Groups& g, const Weights& w, const QWeig
 
 hipError_t launch_down_tile_fp8(const Groups& g, const Weights& w, const QWeights& q, const uint16_t* h,
                                 uint16_t* y_rows, int H, int I, hipStream_t s) {
-  if (q.format != QFormat::kFp8 || !tile_fp8_shape_ok(H, I)) return hipErrorInvalidValue;
+  if (q.format != QFormat::kFp8 || !tile_fp8_shape_ok(H, I) || g.tile_m != kTileMFp8) return hipErrorInvalidValue;
   QTileArgs a{{g.group_offsets, nullptr, g.tiles, g.counters, g.max_rows, w, h, y_rows, 1, nullptr, H, I,
-               (H + 255) / 256, 1, nullptr},
+               (H + 255) / 256, 1, nullptr, kTileMFp8},
               h,
               static_cast<const uint8_t*>(q.down_codes),
               nullptr,

@@ -148,7 +148,8 @@ hipError_t launch_down_tile_bf16(const Groups& g, const Weights& w, const uint16
                                  bool y_bf16, const float* row_scale, float* part, int H, int I, hipStream_t s);
 int down_tile_ksplit(int64_t max_rows, int G, int H, int I);
 // Rows per tile used by the tile kernels' plan.
-constexpr int kTileM = 256;  // rows per tile of the tile GEMMs
+constexpr int kTileM = 256;     // rows per tile of the tile GEMMs
+constexpr int kTileMFp8 = 224;  // rows per tile of the FP8 tile GEMMs (their plan's tile_m)
 
 // grouped SwiGLU, 4-bit routed experts (weight streaming) ----------------------------
 // The shared expert (bf16), computed by the first work-groups of the 4-bit launches: its rows are

@@ -149,13 +149,13 @@ struct SwigluWs {
 };
 
 // Plan buffers of G groups over at most max_rows rows.
-moe::Groups carve_plan(Carver& cv, int G, int64_t max_rows) {
+moe::Groups carve_plan(Carver& cv, int G, int64_t max_rows, int tile_m = moe::kTileM) {
   moe::Groups g;
   g.n_groups = G;
   g.max_rows = max_rows;
-  g.tile_m = moe::kTileM;
+  g.tile_m = tile_m;
   g.stream_rows = G >= moe::kStreamMinGroups ? moe::kStreamRows : 0;
-  g.max_tiles = (int32_t)((max_rows + moe::kTileM - 1) / moe::kTileM + G);
+  g.max_tiles = (int32_t)((max_rows + tile_m - 1) / tile_m + G);
   g.active = cv.take<int32_t>(G);
   g.counters = cv.take<int32_t>(3);
   g.tiles = cv.take<int32_t>(2LL * g.max_tiles);
@@ -335,7 +335,7 @@ QuantWs carve_quant(Carver& cv, const moe_config* c, int64_t T, moe::QFormat f) 
   w.perm_scratch = cv.take<int32_t>(moe::permute_scratch_ints(P, E));
   w.x16 = cv.take<uint16_t>(T * H);
   w.h = cv.take<uint16_t>(rows * I);
-  w.routed = tiles ? carve_plan(cv, E + (shared ? 1 : 0), rows) : carve_plan(cv, E, P);
+  w.routed = tiles ? carve_plan(cv, E + (shared ? 1 : 0), rows, moe::kTileMFp8) : carve_plan(cv, E, P);
   w.y_rows = cv.take<uint16_t>(rows * H);
   return w;
 }

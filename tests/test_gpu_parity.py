@@ -211,19 +211,22 @@ def test_dense_ffn_every_token(T):
     assert err.max() <= Y_TOL["bf16"]
 
 
-def test_dense_ffn_split_k_every_token():
-    """Few rows and a wide layer: the down GEMM splits K (16 ranges of fp32 partial sums, reduced in
-    K-range order); every token against the oracle."""
+@pytest.mark.parametrize("T,H,I", [(16, 2048, 4096), (300, 4096, 1024)], ids=["one_tile", "two_tiles"])
+def test_dense_ffn_split_k_every_token(T, H, I):
+    """Few row tiles and a wide layer: the down GEMM splits K into ranges of fp32 partial sums, reduced
+    in K-range order (one_tile: 16 ranges; two_tiles, the second one ragged: the layer too narrow to
+    split); every token against the oracle."""
     _torch()
-    w = wl.custom("dense_split", T=16, H=2048, I=4096, E=1, K=1, routing="dense", n_shared=0)
+    w = wl.custom("dense_split", T=T, H=H, I=I, E=1, K=1, routing="dense", n_shared=0)
     # the workspace holds the K-range partial sums only when K is split: at least 2 ranges of
-    # 16 rows x H fp32 (256 KiB) beside h (128 KiB) and the plan
+    # T rows x H fp32 beside h and the plan
     ws = moe.moe_workspace_size(moe.config_for(w), moe.MOE_OP_GROUPED_SWIGLU, w.T, 1)
-    assert ws >= 2 * w.T * w.H * 4 + w.T * w.I * 2
+    if T == 16:
+        assert ws >= 2 * w.T * w.H * 4 + w.T * w.I * 2
     t = wl.device_inputs(w)
     y = _dense(w, t)
     err = rel_l2(to_np(y), oracle.swiglu_expert(wl.host_x(w), *wl.host_expert(w, 0)))
-    print(f"dense split-K T={w.T}: max rel L2 {err.max():.3g}", flush=True)
+    print(f"dense split-K T={w.T} H={w.H} I={w.I}: max rel L2 {err.max():.3g}", flush=True)
     assert err.max() <= Y_TOL["bf16"]
 
 
