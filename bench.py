@@ -20,6 +20,7 @@ under profiles/):
     rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 \
               SQ_INSTS_VALU_MFMA_MOPS_F16 -d DIR -o run --output-format csv -- python bench.py ...
     python bench.py --mfma-summary WORKLOAD DIR            # matrix-core busy % per dispatch
+    python bench.py --lds-summary WORKLOAD DIR             # LDS busy % per dispatch
 """
 import argparse
 import csv
@@ -665,7 +666,45 @@ def mfma_summary(workload, d):
     print("\n```json\n" + json.dumps(recs, indent=1) + "\n```")
 
 
+LDS_COUNTERS = ("SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE")
+CUS = 256                  # MI355X compute units
+
+
+def lds_summary(workload, d):
+    """LDS use of the library's kernels from one rocprofv3 --pmc pass over LDS_COUNTERS: LDS busy % of
+    cycles = SQ_LDS_IDX_ACTIVE (summed over CUs) / (GPU cycles x CUs), the expression of rocprofv3's
+    LdsUtil metric (GPU cycles: GRBM_GUI_ACTIVE of one XCD, the CSV summing the XCDs' instances);
+    bank-conflict cycles per LDS-active cycle, and LDS instructions per dispatch."""
+    per = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if r["Counter_Name"] not in LDS_COUNTERS:
+            continue
+        rec = per.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"],
+                                                "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        rec[r["Counter_Name"]] = float(r["Counter_Value"])
+    print("| kernel | dispatches | µs | LDS busy % of cycles | bank-conflict cycles per LDS-active cycle | "
+          "LDS instructions / dispatch |")
+    print("|---|---|---|---|---|---|")
+    recs = []
+    for name, (sym, _) in KERNEL_SYMBOLS.items():
+        hits = [v for v in per.values() if sym in v["name"] and all(c in v for c in LDS_COUNTERS)]
+        if not hits:
+            continue
+        n = len(hits)
+        mean = {c: sum(h[c] for h in hits) / n for c in LDS_COUNTERS}
+        us = sum(h["ns"] for h in hits) / n / 1e3
+        cycles = mean["GRBM_GUI_ACTIVE"] / XCDS
+        busy = 100 * mean["SQ_LDS_IDX_ACTIVE"] / (cycles * CUS)
+        conf = mean["SQ_LDS_BANK_CONFLICT"] / max(mean["SQ_LDS_IDX_ACTIVE"], 1.0)
+        print(f"| {name} | {n} | {us:.1f} | {busy:.1f} | {conf:.3f} | {mean['SQ_INSTS_LDS']:.4g} |")
+        recs.append({"workload": workload, "kernel": name, "dispatches": n, "us": us, "lds_busy_pct": busy,
+                     "bank_conflicts_per_active": conf, **{c: mean[c] for c in LDS_COUNTERS}})
+    print("\n```json\n" + json.dumps(recs, indent=1) + "\n```")
+
+
 def main():
+    if len(sys.argv) >= 2 and sys.argv[1] == "--lds-summary":
+        return lds_summary(sys.argv[2], sys.argv[3])
     if len(sys.argv) >= 2 and sys.argv[1] == "--profile-summary":
         return profile_summary(sys.argv[2])
     if len(sys.argv) >= 2 and sys.argv[1] == "--traffic-summary":
