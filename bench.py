@@ -49,6 +49,8 @@ F32_PEAK = 157.3e12        # fp32 vector FLOP/s
 KERNEL_SYMBOLS = {
     "gateup_stream": ("::stream_kernel<true", ["gemm_stream.hip", "tile_core.h", "kernels.h"]),
     "down_stream": ("::stream_kernel<false", ["gemm_stream.hip", "tile_core.h", "kernels.h"]),
+    "gateup_skinny": ("::skinny_kernel<true", ["gemm_skinny.hip", "tile_core.h", "kernels.h"]),
+    "down_skinny": ("::skinny_kernel<false", ["gemm_skinny.hip", "tile_core.h", "kernels.h"]),
     "gateup_tile": ("::gateup_tile_kernel", ["gemm_tile.hip", "tile_core.h", "kernels.h"]),
     "down_tile": ("::down_tile_kernel", ["gemm_tile.hip", "tile_core.h", "kernels.h"]),
     "router_logits": ("::router_logits_kernel", ["route.hip", "tile_core.h", "kernels.h"]),
@@ -209,6 +211,7 @@ def vendor_gemm(E=385, M=192, H=7168, I=2048, reps=10):
 
 
 STREAM_ROWS, STREAM_MIN_GROUPS = 32, 16   # the device plan's split (kStreamRows, kStreamMinGroups)
+SKINNY_ROWS = 64   # calls of at most this many rows in all (and more than the stream kernels take) run skinny
 
 
 def plan_families(w, ids):
@@ -232,9 +235,11 @@ def plan_families(w, ids):
     n_groups = (1 if w.routing == "dense" else w.E + w.n_shared)
     max_rows = w.T if w.routing == "dense" else w.T * w.K + w.T * w.n_shared
     if max_rows <= 4 * n_groups or w.quant == "int4":
-        return {"stream": groups, "tile": []}
+        return {"stream": groups, "tile": [], "skinny": []}
+    if w.quant == "none" and w.dtype == "bf16" and max_rows <= SKINNY_ROWS and w.H % 64 == 0 and w.I % 64 == 0:
+        return {"stream": [], "tile": [], "skinny": groups}
     cut = STREAM_ROWS if n_groups >= STREAM_MIN_GROUPS else 0
-    return {"stream": [g for g in groups if g[1] <= cut], "tile": [g for g in groups if g[1] > cut]}
+    return {"stream": [g for g in groups if g[1] <= cut], "tile": [g for g in groups if g[1] > cut], "skinny": []}
 
 
 def kernel_work(name, w, fams, n_touched):
@@ -247,7 +252,8 @@ def kernel_work(name, w, fams, n_touched):
     eb = 2 if w.dtype == "bf16" else 4
     if fams is None:
         return None, None
-    fam = "tile" if "_tile" in name else "stream" if (name.endswith("_stream") or name in QUANT_STREAM) else None
+    fam = ("tile" if "_tile" in name else "skinny" if "_skinny" in name
+           else "stream" if (name.endswith("_stream") or name in QUANT_STREAM) else None)
     if fam is None:
         return None, None
     groups = fams[fam]
@@ -455,6 +461,7 @@ def run(w, weights, steps, warmup, graph=True):
     if fams is not None:
         layer["groups_on_stream_kernels"] = len(fams["stream"])
         layer["groups_on_tile_kernels"] = len(fams["tile"])
+        layer["groups_on_skinny_kernels"] = len(fams["skinny"])
     return {"tokens_per_s": T / s, "ms_per_step": ms, "roofline": roof, "layer": layer,
             "kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
             "kernels_roofline": {k: {f: v[f] for f in ("bound", "achieved", "unit", "frac", "bytes_per_launch",

@@ -11,9 +11,12 @@ compiles, next to their sources:
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -29,7 +32,7 @@ HIP_FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 
-MOE_SOURCES = ["moe_api.cpp", "route.hip", "permute.hip", "gemm_stream.hip", "gemm_tile.hip",
+MOE_SOURCES = ["moe_api.cpp", "route.hip", "permute.hip", "gemm_stream.hip", "gemm_tile.hip", "gemm_skinny.hip",
                "gemm_quant.hip", "gemm_simple.hip", "combine.hip"]
 
 
@@ -56,17 +59,25 @@ def build_synth_dev(verbose=False):
     return out
 
 
-def build_moe(verbose=False):
+def build_moe(verbose=False, jobs=None):
+    """libmoe.so: every source compiled to an object in parallel (one hipcc process each, at most
+    `jobs` at a time), then linked."""
     out = os.path.join(PKG, "libmoe.so")
-    srcs = [os.path.join(CSRC, s) for s in MOE_SOURCES]
-    cmd = [HIPCC, *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}"]
-    for s in srcs:
-        if s.endswith(".cpp"):
-            cmd += ["-x", "hip", s]
-        else:
-            cmd += [s]
-    cmd += ["-o", out]
-    _run(cmd, verbose)
+    objdir = tempfile.mkdtemp(prefix="moe_objs_")
+    try:
+        def compile_one(name):
+            obj = os.path.join(objdir, os.path.splitext(name)[0] + ".o")
+            flags = [f for f in HIP_FLAGS if f != "-shared"]
+            _run([HIPCC, *flags, "-c", f"-I{INCLUDE}", f"-I{CSRC}", "-x", "hip", os.path.join(CSRC, name),
+                  "-o", obj], verbose)
+            return obj
+
+        jobs = jobs or max(1, min(len(MOE_SOURCES), os.cpu_count() or 1, 8))
+        with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+            objs = list(pool.map(compile_one, MOE_SOURCES))
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out], verbose)
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
     return out
 
 

@@ -100,15 +100,6 @@ static_assert(a_stage_bytes<QFormat::kInt4>() == 2048 && a_stage_bytes<QFormat::
 static_assert(2 * (4 * stage_bytes<QFormat::kFp8>()) <= 160 * 1024, "LDS");
 static_assert(2 * (4 * stage_bytes<QFormat::kInt4>() + kWaves * kScaleWaveB) <= 160 * 1024, "LDS");
 
-// Compile-time loop: f(integral_constant<int, I>) for I = 0 .. N-1.
-template <int N, int I = 0, class F>
-__device__ __forceinline__ void static_for(const F& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<N, I + 1>(f);
-  }
-}
-
 struct QArgs {
   const int32_t* group_offsets;
   const int32_t* row_index;  // gate/up: token row of each routed row

@@ -346,15 +346,6 @@ __device__ __forceinline__ void run_tile(int nblk, int wr, const Body& body) {
 #endif
 }
 
-// Compile-time loop helper: f(integral_constant<int, I>) for I = 0 .. N-1.
-template <int N, int I = 0, class F>
-__device__ __forceinline__ void static_for(const F& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<N, I + 1>(f);
-  }
-}
-
 // Output tiles leave through LDS so that global stores are whole 16-byte chunks of contiguous rows.
 // A bf16 tile of kCols columns is staged over the free ring arrays in order (a0, a1, b0, b1, b2),
 // kRowsPer rows each; 16-byte chunk c of row r at position c ^ out_swz(r).
@@ -1150,11 +1141,17 @@ hipError_t launch_down_tile_bf16(const Groups& g, const Weights& w, const uint16
   down_tile_kernel<<<grid_for(g.max_tiles, p.n_ntiles, split), kThreads, 0, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || split == 1) return e;
+  return launch_ksplit_reduce(part, split, g, g.stream_rows, H, y_rows, y_bf16, s);
+}
+
+hipError_t launch_ksplit_reduce(const float* part, int split, const Groups& g, int stream_rows, int H, void* y_rows,
+                                bool y_bf16, hipStream_t s) {
   const int64_t n = g.max_rows * (H / 8);
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
   ksplit_reduce_kernel<<<(unsigned)blocks, 256, 0, s>>>(part, split, g.group_offsets, g.n_groups, g.max_rows,
-                                                        g.stream_rows, H, y_rows, y_bf16 ? 1 : 0);
+                                                        stream_rows, H, y_rows, y_bf16 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -147,6 +147,25 @@ hipError_t launch_down_stream_bf16(const Groups& g, const Weights& w, const uint
 hipError_t launch_down_tile_bf16(const Groups& g, const Weights& w, const uint16_t* h, void* y_rows,
                                  bool y_bf16, const float* row_scale, float* part, int H, int I, hipStream_t s);
 int down_tile_ksplit(int64_t max_rows, int G, int H, int I);
+// y_rows[r, :] = sum over ks of part[ks, r, :] (K-range order) for the rows of the groups (those of more
+// than stream_rows rows when stream_rows > 0), bf16 or fp32.
+hipError_t launch_ksplit_reduce(const float* part, int split, const Groups& g, int stream_rows, int H, void* y_rows,
+                                bool y_bf16, hipStream_t s);
+// Groups of at most 64 rows in all (skinny kernels: weight streaming with the token rows shared in
+// LDS, one work-group of nw waves per CU).  H, I multiples of 64.
+bool skinny_ok(int64_t max_rows, int H, int I);
+struct SkinnyPlan {
+  int nw;    // waves per work-group, one 16-weight-row granule each
+  int nblk;  // work-groups per group and K range
+  int ks;    // K ranges (down; their fp32 partial sums go to part, [ks, max_rows, H])
+};
+SkinnyPlan skinny_gateup_plan(int G, int H, int I);
+SkinnyPlan skinny_down_plan(int G, int64_t max_rows, int H, int I);
+hipError_t launch_gateup_skinny_bf16(const Groups& g, const Weights& w, const uint16_t* x, uint16_t* h, int H,
+                                     int I, hipStream_t s);
+// With more than one K range the partial sums go to part, then launch_ksplit_reduce adds them.
+hipError_t launch_down_skinny_bf16(const Groups& g, const Weights& w, const uint16_t* h, void* y_rows, bool y_bf16,
+                                   const float* row_scale, float* part, int H, int I, hipStream_t s);
 // Rows per tile used by the tile kernels' plan.
 constexpr int kTileM = 256;     // rows per tile of the tile GEMMs
 constexpr int kTileMFp8 = 224;  // rows per tile of the FP8 tile GEMMs (their plan's tile_m)

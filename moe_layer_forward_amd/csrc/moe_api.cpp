@@ -141,6 +141,12 @@ int check_forward_spans(const moe_config* c, int64_t T) {
 
 bool use_stream_kernels(int64_t max_rows, int G) { return max_rows <= 4LL * G; }
 
+// bf16 calls of at most 64 rows in all that the stream kernels do not take: the skinny kernels.
+bool use_skinny_kernels(const moe_config* c, int64_t max_rows, int G) {
+  return c->dtype == MOE_BF16 && !use_stream_kernels(max_rows, G) &&
+         moe::skinny_ok(max_rows, c->hidden_size, c->moe_intermediate_size);
+}
+
 // Grouped SwiGLU scratch: h, the plan, and the down GEMM's K-range partial sums when it splits K.
 struct SwigluWs {
   void* h;
@@ -168,8 +174,10 @@ SwigluWs carve_swiglu(Carver& cv, const moe_config* c, int G, int64_t max_rows) 
   w.g = carve_plan(cv, G, max_rows);
   w.part = nullptr;
   if (c->dtype == MOE_BF16 && !use_stream_kernels(max_rows, G)) {
-    const int split = moe::down_tile_ksplit(max_rows, G, c->hidden_size, c->moe_intermediate_size);
-    if (split > 1) w.part = cv.take<float>((int64_t)split * max_rows * c->hidden_size);
+    const int H = c->hidden_size, I = c->moe_intermediate_size;
+    const bool skinny = use_skinny_kernels(c, max_rows, G);
+    const int split = skinny ? moe::skinny_down_plan(G, max_rows, H, I).ks : moe::down_tile_ksplit(max_rows, G, H, I);
+    if (split > 1) w.part = cv.take<float>((int64_t)split * max_rows * H);
   }
   return w;
 }
@@ -179,6 +187,18 @@ hipError_t run_swiglu(const moe_config* c, const moe::Groups& g, const moe::Weig
                       float* part, const float* row_scale, void* y_rows, bool y_bf16, hipStream_t s,
                       bool planned = false) {
   const int H = c->hidden_size, I = c->moe_intermediate_size;
+  if (use_skinny_kernels(c, g.max_rows, g.n_groups)) {
+    // the skinny kernels read the group offsets themselves: no plan
+    hipError_t e = timed("gateup_skinny", s, [&] {
+      return moe::launch_gateup_skinny_bf16(g, w, static_cast<const uint16_t*>(x), static_cast<uint16_t*>(h), H, I,
+                                            s);
+    });
+    if (e != hipSuccess) return e;
+    return timed("down_skinny", s, [&] {
+      return moe::launch_down_skinny_bf16(g, w, static_cast<const uint16_t*>(h), y_rows, y_bf16, row_scale, part, H,
+                                          I, s);
+    });
+  }
   hipError_t e = planned ? hipSuccess : timed("plan", s, [&] { return moe::launch_plan(g, s); });
   if (e != hipSuccess) return e;
   if (c->dtype == MOE_F32) {

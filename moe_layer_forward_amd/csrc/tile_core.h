@@ -16,6 +16,8 @@
 // load lane picks the global chunk that belongs in its LDS slot, so every load still reads whole
 // contiguous row segments.
 #pragma once
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace moe {
@@ -53,6 +55,15 @@ struct TileShape {
   // First row of the i-th sub-tile of wave row wm.
   __device__ static __forceinline__ int sub_row(int wm, int i) { return (2 * i + wm) * 32; }
 };
+
+// Compile-time loop: f(integral_constant<int, I>) for I = 0 .. N-1.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(const F& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
 
 // Work-group barrier that waits only for this wave's LDS traffic, not for its global loads in flight
 // (a full __syncthreads() also drains the vector-memory counter, which would stall the prefetch).

@@ -200,7 +200,8 @@ def _dense(w, t):
     return y
 
 
-@pytest.mark.parametrize("T", [3, 200], ids=["stream_kernels", "tile_kernels"])
+@pytest.mark.parametrize("T", [3, 17, 40, 64, 200],
+                         ids=["stream_kernels", "skinny_2_blocks", "skinny_ragged", "skinny_64_rows", "tile_kernels"])
 def test_dense_ffn_every_token(T):
     _torch()
     w = wl.custom("dense_small", T=T, H=512, I=1152, E=1, K=1, routing="dense", n_shared=0)
@@ -211,23 +212,28 @@ def test_dense_ffn_every_token(T):
     assert err.max() <= Y_TOL["bf16"]
 
 
-@pytest.mark.parametrize("T,H,I", [(16, 2048, 4096), (300, 4096, 1024)], ids=["one_tile", "two_tiles"])
+@pytest.mark.parametrize("T,H,I", [(16, 2048, 4096), (100, 2048, 4096), (300, 4096, 1024)],
+                         ids=["skinny", "one_tile", "two_tiles"])
 def test_dense_ffn_split_k_every_token(T, H, I):
-    """Few row tiles and a wide layer: the down GEMM splits K into ranges of fp32 partial sums, reduced
-    in K-range order (one_tile: 16 ranges; two_tiles, the second one ragged: the layer too narrow to
-    split); every token against the oracle."""
+    """Few rows and a wide layer: the down GEMM splits K into ranges of fp32 partial sums, reduced in
+    K-range order (skinny: at most 64 rows, K ranges of the skinny kernels, W_down rows 8 KiB apart so
+    the work-groups start at different K steps; one_tile: 16 ranges of the tile kernels; two_tiles, the
+    second one ragged: the layer too narrow to split); every token against the oracle."""
     _torch()
     w = wl.custom("dense_split", T=T, H=H, I=I, E=1, K=1, routing="dense", n_shared=0)
     # the workspace holds the K-range partial sums only when K is split: at least 2 ranges of
     # T rows x H fp32 beside h and the plan
     ws = moe.moe_workspace_size(moe.config_for(w), moe.MOE_OP_GROUPED_SWIGLU, w.T, 1)
-    if T == 16:
+    if T <= 100:
         assert ws >= 2 * w.T * w.H * 4 + w.T * w.I * 2
     t = wl.device_inputs(w)
     y = _dense(w, t)
     err = rel_l2(to_np(y), oracle.swiglu_expert(wl.host_x(w), *wl.host_expert(w, 0)))
     print(f"dense split-K T={w.T} H={w.H} I={w.I}: max rel L2 {err.max():.3g}", flush=True)
     assert err.max() <= Y_TOL["bf16"]
+    # the K ranges are added in K-range order whichever work-group finishes last: bit-identical reruns
+    for _ in range(3):
+        assert _torch().equal(_dense(w, t), y)
 
 
 @pytest.mark.timeout(600)
@@ -284,10 +290,13 @@ def test_permute_call_integer_exact():
 
 
 @pytest.mark.parametrize("y_bf16", [False, True])
-@pytest.mark.parametrize("sizes", [[30, 0, 55, 0, 95], [3, 0, 5, 1, 0],
+@pytest.mark.parametrize("sizes", [[30, 0, 55, 0, 95], [3, 0, 5, 1, 0], [16, 0, 17, 0, 31], [1, 0, 63],
                                    [2, 40, 0, 7, 300, 1, 33, 32, 0, 5, 17, 64, 3, 0, 9, 120, 1, 31, 0, 2, 8, 0, 50, 4]],
-                         ids=["tile_kernels", "stream_kernels", "many_groups_both"])
+                         ids=["tile_kernels", "stream_kernels", "skinny_kernels", "skinny_one_and_63",
+                              "many_groups_both"])
 def test_grouped_swiglu_and_combine_calls(y_bf16, sizes):
+    # skinny_*: at most 64 rows in all and more than 4 per group: the skinny kernels (16 / 17 / 31 rows:
+    # one, two and two MFMA row blocks; empty groups between and at the end)
     # many_groups_both: 24 groups, so the groups of at most 32 rows go to the weight-stream kernels and
     # the others (33 .. 300 rows) to the tile kernels in the same call
     torch = _torch()
