@@ -51,8 +51,8 @@ KERNEL_SYMBOLS = {
     "down_stream": ("::stream_kernel<false", ["gemm_stream.hip", "tile_core.h", "kernels.h"]),
     "gateup_skinny": ("::skinny_kernel<true", ["gemm_skinny.hip", "tile_core.h", "kernels.h"]),
     "down_skinny": ("::skinny_kernel<false", ["gemm_skinny.hip", "tile_core.h", "kernels.h"]),
-    "gateup_tile": ("::gateup_tile_kernel", ["gemm_tile.hip", "tile_core.h", "kernels.h"]),
-    "down_tile": ("::down_tile_kernel", ["gemm_tile.hip", "tile_core.h", "kernels.h"]),
+    "gateup_tile": ("::gateup_tile_kernel", ["gemm_tile.hip", "tile_gemm.h", "tile_core.h", "kernels.h"]),
+    "down_tile": ("::down_tile_kernel", ["gemm_tile.hip", "tile_gemm.h", "tile_core.h", "kernels.h"]),
     "router_logits": ("::router_logits_kernel", ["route.hip", "tile_core.h", "kernels.h"]),
     "combine": ("::combine_kernel", ["combine.hip", "kernels.h"]),
     "router_logits_f32": ("::router_logits_f32_kernel", ["route.hip", "tile_core.h", "kernels.h"]),
@@ -62,8 +62,10 @@ KERNEL_SYMBOLS = {
     "down_q4": ("::q_stream_kernel<(moe::QFormat)0, false", ["gemm_quant.hip", "tile_core.h", "kernels.h"]),
     "gateup_fp8": ("::q_stream_kernel<(moe::QFormat)1, true", ["gemm_quant.hip", "tile_core.h", "kernels.h"]),
     "down_fp8": ("::q_stream_kernel<(moe::QFormat)1, false", ["gemm_quant.hip", "tile_core.h", "kernels.h"]),
-    "gateup_tile_fp8": ("::gateup_tile_fp8_kernel", ["gemm_tile.hip", "tile_core.h", "kernels.h"]),
-    "down_tile_fp8": ("::down_tile_fp8_kernel", ["gemm_tile.hip", "tile_core.h", "kernels.h"]),
+    "gateup_tile_fp8": ("::gateup_tile_fp8_kernel", ["gemm_tile.hip", "tile_gemm.h", "tile_core.h", "kernels.h"]),
+    "down_tile_fp8": ("::down_tile_fp8_kernel", ["gemm_tile.hip", "tile_gemm.h", "tile_core.h", "kernels.h"]),
+    "gateup_tile_q4": ("::gateup_tile_q4_kernel", ["gemm_tile_q4.hip", "tile_gemm.h", "tile_core.h", "kernels.h"]),
+    "down_tile_q4": ("::down_tile_q4_kernel", ["gemm_tile_q4.hip", "tile_gemm.h", "tile_core.h", "kernels.h"]),
 }
 QUANT_STREAM = ("gateup_q4", "down_q4", "gateup_fp8", "down_fp8")  # the quantized weight-stream kernels
 Q4_BYTES = 0.5 + 2 / 32    # bytes per 4-bit weight: the code plus its share of a binary16 scale per 32
@@ -217,7 +219,7 @@ SKINNY_ROWS = 64   # calls of at most this many rows in all (and more than the s
 def plan_families(w, ids):
     """Which groups the library's plan hands to the weight-stream kernels and which to the tile
     kernels, from the realised routing (host mirror of moe_api.cpp's kernel choice and the device
-    plan's split at kStreamRows; 4-bit experts always stream).  Returns {family: [(group, rows,
+    plan's split at kStreamRows).  Returns {family: [(group, rows,
     tokens)]}, tokens being the set of token ids whose rows the group reads (None = every token: the
     shared expert's or the dense FFN's group)."""
     if w.routing == "dense":
@@ -234,7 +236,7 @@ def plan_families(w, ids):
             groups.append((w.E, w.T, None))
     n_groups = (1 if w.routing == "dense" else w.E + w.n_shared)
     max_rows = w.T if w.routing == "dense" else w.T * w.K + w.T * w.n_shared
-    if max_rows <= 4 * n_groups or w.quant == "int4":
+    if max_rows <= 4 * n_groups:
         return {"stream": groups, "tile": [], "skinny": []}
     if w.quant == "none" and w.dtype == "bf16" and max_rows <= SKINNY_ROWS and w.H % 64 == 0 and w.I % 64 == 0:
         return {"stream": [], "tile": [], "skinny": groups}

@@ -32,7 +32,8 @@ HIP_FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 
-MOE_SOURCES = ["moe_api.cpp", "route.hip", "permute.hip", "gemm_stream.hip", "gemm_tile.hip", "gemm_skinny.hip",
+MOE_SOURCES = ["moe_api.cpp", "route.hip", "permute.hip", "gemm_stream.hip", "gemm_tile.hip", "gemm_tile_q4.hip",
+               "gemm_skinny.hip",
                "gemm_quant.hip", "gemm_simple.hip", "combine.hip"]
 
 

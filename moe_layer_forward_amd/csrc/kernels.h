@@ -168,7 +168,8 @@ hipError_t launch_down_skinny_bf16(const Groups& g, const Weights& w, const uint
                                    const float* row_scale, float* part, int H, int I, hipStream_t s);
 // Rows per tile used by the tile kernels' plan.
 constexpr int kTileM = 256;     // rows per tile of the tile GEMMs
-constexpr int kTileMFp8 = 224;  // rows per tile of the FP8 tile GEMMs (their plan's tile_m)
+constexpr int kTileMQ = 224;   // rows per tile of the FP8 tile GEMMs (their plan's tile_m)
+constexpr int kTileMQ4 = 192;  // rows per tile of the 4-bit tile GEMMs
 
 // grouped SwiGLU, 4-bit routed experts (weight streaming) ----------------------------
 // The shared expert (bf16), computed by the first work-groups of the 4-bit launches: its rows are
@@ -201,18 +202,25 @@ hipError_t launch_gateup_q_stream(const Groups& g, const QWeights& w, const uint
 hipError_t launch_down_q_stream(const Groups& g, const QWeights& w, const uint16_t* h16, uint16_t* y_rows,
                                 const SharedBf16* sh, int H, int I, int n_routed, bool small_only, hipStream_t s);
 
-// grouped SwiGLU, FP8 routed experts, many rows per group (tile kernels) -------------------
-// The groups of the tile list: routed groups from E4M3 codes and block scales (A rows binary16 in
-// the order of launch_f16_rows, h likewise), the shared group (g == w.shared_group) in bf16 from
-// w.s_* (A: x or h rows in bf16).  H, I multiples of 128, at most 8192.
-bool tile_fp8_shape_ok(int H, int I);
+// grouped SwiGLU, quantized routed experts, many rows per group (tile kernels) -------------
+// The groups of the tile list: routed groups from their codes and scales (FP8: E4M3 codes with one
+// fp32 scale per 128 x 128 block; 4-bit: the stream kernels' codes and binary16 scales per 32
+// inputs), A rows binary16 in the order of launch_f16_rows (h likewise); the shared group
+// (g == w.shared_group) in bf16 from w.s_* (A: x or h rows in bf16).
+// FP8: H, I multiples of 128, at most 8192.  4-bit: H, I multiples of 256.
+bool tile_quant_shape_ok(QFormat f, int H, int I);
 // h[r, I] = SiLU(a Wg^T) * (a Wu^T): routed rows binary16 from x16 rows, shared rows bf16 from x rows
 // (both through row_index).
-hipError_t launch_gateup_tile_fp8(const Groups& g, const Weights& w, const QWeights& q, const uint16_t* x,
-                                  const uint16_t* x16, uint16_t* h, int H, int I, hipStream_t s);
+hipError_t launch_gateup_tile_quant(const Groups& g, const Weights& w, const QWeights& q, const uint16_t* x,
+                                    const uint16_t* x16, uint16_t* h, int H, int I, hipStream_t s);
 // y_rows[r, H] (bf16) = h[r] Wd^T (h binary16 for routed rows, bf16 for the shared group's rows).
-hipError_t launch_down_tile_fp8(const Groups& g, const Weights& w, const QWeights& q, const uint16_t* h,
-                                uint16_t* y_rows, int H, int I, hipStream_t s);
+hipError_t launch_down_tile_quant(const Groups& g, const Weights& w, const QWeights& q, const uint16_t* h,
+                                  uint16_t* y_rows, int H, int I, hipStream_t s);
+// The 4-bit forms of the two (gemm_tile_q4.hip), which the two above call for QFormat::kInt4.
+hipError_t launch_gateup_tile_q4(const Groups& g, const Weights& w, const QWeights& q, const uint16_t* x,
+                                 const uint16_t* x16, uint16_t* h, int H, int I, hipStream_t s);
+hipError_t launch_down_tile_q4(const Groups& g, const Weights& w, const QWeights& q, const uint16_t* h,
+                               uint16_t* y_rows, int H, int I, hipStream_t s);
 
 // grouped SwiGLU, fp32 (plain kernels) ---------------------------------------------
 hipError_t launch_gateup_f32(const Groups& g, const Weights& w, const float* x, float* h, int H, int I,

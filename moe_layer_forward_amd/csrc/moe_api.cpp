@@ -330,12 +330,12 @@ struct QuantWs {
   void* y_rows;
 };
 
-// Whether a quantized forward runs its larger groups on the tile kernels (FP8, many rows per group);
-// their plan then also lists the shared expert's rows, as group E.
+// Whether a quantized forward runs its larger groups on the tile kernels (many rows per group); their
+// plan then also lists the shared expert's rows, as group E.
 bool quant_tiles(const moe_config* c, moe::QFormat f, int64_t T) {
   const bool shared = c->n_shared_experts == 1;
   const int64_t rows = T * c->top_k + (shared ? T : 0);
-  return f == moe::QFormat::kFp8 && moe::tile_fp8_shape_ok(c->hidden_size, c->moe_intermediate_size) &&
+  return moe::tile_quant_shape_ok(f, c->hidden_size, c->moe_intermediate_size) &&
          !use_stream_kernels(rows, c->n_routed_experts + (shared ? 1 : 0));
 }
 
@@ -355,7 +355,8 @@ QuantWs carve_quant(Carver& cv, const moe_config* c, int64_t T, moe::QFormat f) 
   w.perm_scratch = cv.take<int32_t>(moe::permute_scratch_ints(P, E));
   w.x16 = cv.take<uint16_t>(T * H);
   w.h = cv.take<uint16_t>(rows * I);
-  w.routed = tiles ? carve_plan(cv, E + (shared ? 1 : 0), rows, moe::kTileMFp8) : carve_plan(cv, E, P);
+  w.routed = tiles ? carve_plan(cv, E + (shared ? 1 : 0), rows, f == moe::QFormat::kInt4 ? moe::kTileMQ4 : moe::kTileMQ)
+                   : carve_plan(cv, E, P);
   w.y_rows = cv.take<uint16_t>(rows * H);
   return w;
 }
@@ -500,18 +501,18 @@ int forward_quant(const char* name, const moe_config* cfg, int64_t T, const void
     }
     const bool small = gr.stream_rows > 0;
     if (e == hipSuccess && small)
-      e = timed("gateup_fp8", s,
+      e = timed(q4 ? "gateup_q4" : "gateup_fp8", s,
                 [&] { return moe::launch_gateup_q_stream(gr, qw, w.x16, T, w.h, shp, H, I, E, true, s); });
     if (e == hipSuccess)
-      e = timed("gateup_tile_fp8", s, [&] {
-        return moe::launch_gateup_tile_fp8(gr, wsh, qw, static_cast<const uint16_t*>(x), w.x16, w.h, H, I, s);
+      e = timed(q4 ? "gateup_tile_q4" : "gateup_tile_fp8", s, [&] {
+        return moe::launch_gateup_tile_quant(gr, wsh, qw, static_cast<const uint16_t*>(x), w.x16, w.h, H, I, s);
       });
     if (e == hipSuccess && small)
-      e = timed("down_fp8", s,
+      e = timed(q4 ? "down_q4" : "down_fp8", s,
                 [&] { return moe::launch_down_q_stream(gr, qw, w.h, y_rows, shp, H, I, E, true, s); });
     if (e == hipSuccess)
-      e = timed("down_tile_fp8", s,
-                [&] { return moe::launch_down_tile_fp8(gr, wsh, qw, w.h, y_rows, H, I, s); });
+      e = timed(q4 ? "down_tile_q4" : "down_tile_fp8", s,
+                [&] { return moe::launch_down_tile_quant(gr, wsh, qw, w.h, y_rows, H, I, s); });
   } else {
     if (e == hipSuccess)
       e = timed(q4 ? "gateup_q4" : "gateup_fp8", s,

@@ -17,6 +17,7 @@ decode_int4    64  7168  2048  384   8  bf16    as decode; routed experts stored
 decode_fp8     64  7168  2048  384   8  bf16    as decode; routed experts stored as
                                                  E4M3 codes + fp32 128x128-block scales
 prefill_fp8  8192  7168  2048  384   8  bf16    as prefill; routed experts as decode_fp8
+prefill_int4 8192  7168  2048  384   8  bf16    as prefill; routed experts as decode_int4
 ==========  =====  ====  ====  ===  ==  ======  ==================================
 
 
@@ -36,7 +37,8 @@ weights quantized per group of 32 inputs (s = f16(max|w| / 7), q = clamp(rint(w 
 -8, 7)) -- the checkpoint-conversion step, done on the device for the GPU and on
 the host for the oracle by two implementations of the same rule (``synth``).
 decode_fp8 likewise quantizes them per 128 x 128 block (s = max|w| / 448, c = E4M3
-round-to-nearest-even of w / s); prefill_fp8 has prefill's tokens and those codes.
+round-to-nearest-even of w / s); prefill_fp8 and prefill_int4 have prefill's tokens and
+those codes.
 
 Synthetic streams: 0 activations, 1 router, 2 gate, 3 up, 4 down, 5/6/7 shared
 gate/up/down, 11/12/13 dense gate/up/down (Philox, index = expert id); 8 skew
@@ -116,6 +118,7 @@ WORKLOADS = {
     "decode_int4": Workload("decode_int4", 64, 7168, 2048, 384, 8, "bf16", x_seed=2, w_seed=100, quant="int4"),
     "decode_fp8": Workload("decode_fp8", 64, 7168, 2048, 384, 8, "bf16", x_seed=2, w_seed=100, quant="fp8"),
     "prefill_fp8": Workload("prefill_fp8", 8192, 7168, 2048, 384, 8, "bf16", x_seed=3, w_seed=100, quant="fp8"),
+    "prefill_int4": Workload("prefill_int4", 8192, 7168, 2048, 384, 8, "bf16", x_seed=3, w_seed=100, quant="int4"),
 }
 
 
