@@ -217,12 +217,16 @@ int moe_forward_routed(const moe_config* cfg, int64_t T, const void* x, const in
  * i.e. gate_codes, up_codes [E, I, H/8], gate_scales, up_scales [E, I, H/32],
  *      down_codes [E, H, I/8], down_scales [E, H, I/32].
  * Precision: dtype must be MOE_BF16.  The routed experts multiply in binary16 with fp32
- * accumulation: x is rounded once to binary16 (|x| must stay below 65504), each decoded weight
- * q*s is rounded once to binary16, SiLU(g)*u is rounded to binary16 between the two matmuls,
- * y_rows to bf16.  The shared expert and the combine are as in moe_forward.
+ * accumulation: x is rounded once to binary16 (|x| must stay below 65504); SiLU(g)*u is rounded to
+ * binary16 between the two matmuls, y_rows to bf16.  On the weight-stream kernels every code enters
+ * the matmul as an exact integer and each 32-input group's fp32 partial sum is multiplied by its
+ * scale; on the tile kernels each decoded weight q*s is rounded once to binary16 (within 2^-11
+ * relative).  The shared expert and the combine are as in moe_forward.
  * Shapes: as moe_forward, with hidden_size and moe_intermediate_size multiples of 256.
- * Each routed expert that received tokens has its codes and scales read once per 4 of its rows
- * (the kernels stream weights; they are built for decode-sized T, about one row per expert).
+ * Kernels: with at most 4 rows per group on average (decode-sized T) every group streams its
+ * codes and scales once per 4 of its rows.  Otherwise the groups run on tile GEMMs that read a
+ * group's codes once per 192-row tile (the shared expert's rows too), except that in calls of 16 or
+ * more groups those of at most 32 rows keep streaming.
  * Workspace: moe_workspace_size(cfg, MOE_OP_FORWARD_Q4, T, 0). */
 int moe_forward_q4(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
                    const float* score_bias, const float* logit_offset, const uint32_t* gate_codes,
@@ -245,14 +249,17 @@ int moe_forward_q4(const moe_config* cfg, int64_t T, const void* x, const void* 
  * i.e. gate_codes, up_codes [E, I, H], gate_scales, up_scales [E, I/128, H/128],
  *      down_codes [E, H, I], down_scales [E, H/128, I/128].
  * Precision: dtype must be MOE_BF16.  The routed experts multiply in binary16 with fp32
- * accumulation: x is rounded once to binary16 (|x| must stay below 65504), every code enters the
- * matmul exactly (E4M3 values are binary16 values), each 128-input block's partial sum is
- * multiplied by its scale in fp32, SiLU(g)*u is rounded to binary16 between the two matmuls,
- * y_rows to bf16.  The shared expert and the combine are as in moe_forward.
+ * accumulation: x is rounded once to binary16 (|x| must stay below 65504); SiLU(g)*u is rounded to
+ * binary16 between the two matmuls, y_rows to bf16.  On the weight-stream kernels every code enters
+ * the matmul exactly (E4M3 values are binary16 values) and each 128-input block's partial sum is
+ * multiplied by its scale in fp32; on the tile kernels each weight is decoded with its block scale
+ * to binary16 (within 2^-10 relative).  The shared expert and the combine are as in moe_forward.
  * Shapes: as moe_forward, with hidden_size and moe_intermediate_size multiples of 128 and at
  * most 8192 (else MOE_ERR_UNSUPPORTED).
- * Each routed expert that received tokens has its codes read once per 16 of its rows (the kernels
- * stream weights; they are built for decode-sized T, about one row per expert).
+ * Kernels: with at most 4 rows per group on average (decode-sized T) every group streams its codes
+ * once per 16 of its rows.  Otherwise the groups run on tile GEMMs that read a group's codes once
+ * per 224-row tile (the shared expert's rows too), except that in calls of 16 or more groups those
+ * of at most 32 rows keep streaming.
  * Workspace: moe_workspace_size(cfg, MOE_OP_FORWARD_FP8, T, 0). */
 int moe_forward_fp8(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
                     const float* score_bias, const float* logit_offset, const uint8_t* gate_codes,
