@@ -727,7 +727,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=list(wl.WORKLOADS))
     ap.add_argument("--also", default="prefill,skew,ep_share,tiny,dense_decode,dense_prefill,decode_int4,decode_fp8,"
-                                      "prefill_fp8",
+                                      "prefill_fp8,prefill_int4",
                     help="comma-separated workloads measured in the same run and reported beside it ('none')")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="first run one copy of known size (the traffic summary's counter calibration)")

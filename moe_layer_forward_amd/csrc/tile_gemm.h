@@ -83,13 +83,14 @@ struct TileRows {
 };
 
 // Work-group -> (row tile, column slab nt, K range ks).  The hardware hands work-group b to XCD b % 8;
-// row tiles are dealt to the XCDs round-robin (tile t to XCD t % 8, from the plan's largest-first
-// list, so every XCD gets the same mix of large and small groups).  An XCD takes its tiles in blocks
-// of kGroupTiles: a block of tiles of one group (a group of many rows) runs slab by slab, its tiles
-// side by side, so the work-groups reading a weight slab run together and share it in the XCD's L2
-// (instead of the slab being streamed again for every row tile); any other block runs tile by tile,
-// a tile's slabs side by side, sharing the tile's token rows in L2.  With fewer tiles than XCDs the
-// tiles' items are spread over all XCDs instead.
+// the plan's tile list (largest groups first, a group's tiles consecutive) is cut into blocks of
+// kGroupTiles consecutive tiles, dealt to the XCDs round-robin (block c to XCD c % 8, so every XCD gets
+// the same mix of large and small groups, and the tiles of a group of many rows share blocks; with
+// fewer than 8 blocks, single tiles are dealt round-robin and an XCD's blocks are every 8th tile).  A block of tiles of one group (a group of many rows) runs
+// slab by slab, its tiles side by side, so the work-groups reading a weight slab run together and share
+// it in the XCD's L2 (instead of the slab being streamed again for every row tile); any other block
+// runs tile by tile, a tile's slabs side by side, sharing the tile's token rows in L2.  With fewer
+// tiles than XCDs the tiles' items are spread over all XCDs instead.
 constexpr int kGroupTiles = 4;
 
 __device__ __forceinline__ bool tile_of(const TileArgs& p, int& nt, int& ks, TileRows& t) {
@@ -111,14 +112,19 @@ __device__ __forceinline__ bool tile_of(const TileArgs& p, int& nt, int& ks, Til
   } else {
     const int64_t blk = local / ((int64_t)kGroupTiles * per_tile);  // block of this XCD's tiles
     const int q = (int)(local % ((int64_t)kGroupTiles * per_tile));
-    const int64_t j0 = blk * kGroupTiles;                            // first tile of the block, XCD-local
-    int in_blk = 0;                                                  // tiles of this XCD in the block
+    // tile i of the block: kGroupTiles consecutive tiles of the list once every XCD gets a whole
+    // block; with fewer tiles single tiles go round-robin (XCD-local tile j is tile j * 8 + x)
+    const bool chunked = n_tiles >= (int64_t)kXcds * kGroupTiles;
+    const auto tile_at = [&](int i) -> int64_t {
+      return chunked ? (blk * kXcds + x) * kGroupTiles + i : (blk * kGroupTiles + i) * kXcds + x;
+    };
+    int in_blk = 0;  // tiles of the block
     bool one_group = true;
     for (int i = 0; i < kGroupTiles; ++i) {
-      const int64_t ti = (j0 + i) * kXcds + x;
+      const int64_t ti = tile_at(i);
       if (ti >= n_tiles) break;
       ++in_blk;
-      if (p.tiles[2 * ti] != p.tiles[2 * (j0 * kXcds + x)]) one_group = false;
+      if (p.tiles[2 * ti] != p.tiles[2 * tile_at(0)]) one_group = false;
     }
     int j;
     if (one_group && in_blk == kGroupTiles) {
@@ -128,8 +134,8 @@ __device__ __forceinline__ bool tile_of(const TileArgs& p, int& nt, int& ks, Til
       j = q / per_tile;
       rem = q % per_tile;
     }
-    tile64 = (j0 + j) * kXcds + x;
-    if (j >= in_blk || tile64 >= n_tiles) return false;
+    if (j >= in_blk) return false;
+    tile64 = tile_at(j);
   }
   const int tile = (int)tile64;
   nt = rem / p.n_ksplit;
@@ -678,9 +684,10 @@ __device__ __forceinline__ void q_tile_body(const Loads& o, const QRings& r, con
   epilogue(std::integral_constant<int, NBW>{}, acc);
 }
 
-// Work-groups for up to max_tiles row tiles dealt round-robin to the XCDs: ceil(max_tiles / 8) tiles
-// per XCD in blocks of kGroupTiles, each tile n_ntiles * n_ksplit work-groups (with fewer than 8 tiles,
-// an XCD gets at most two chunks of at most per_tile / 2 work-groups each, which this covers).
+// Work-groups for up to max_tiles row tiles dealt to the XCDs in blocks of kGroupTiles: at most
+// ceil(max_tiles / (8 kGroupTiles)) blocks per XCD either way, each tile n_ntiles * n_ksplit work-groups
+// (with fewer than 8 tiles, an XCD gets at most two chunks of at most per_tile / 2 work-groups each,
+// which this covers).
 inline unsigned grid_for(int64_t max_tiles, int n_ntiles, int n_ksplit = 1) {
   const int64_t per_xcd = (max_tiles + kXcds - 1) / kXcds;
   const int64_t blocks = (per_xcd + kGroupTiles - 1) / kGroupTiles;
