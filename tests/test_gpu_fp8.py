@@ -75,8 +75,10 @@ def _check(w, t, tokens=None, bias=None):
     (300, 512, 384, 8, 3, 0),    # tiles without a shared expert
     (200, 256, 512, 16, 2, 1),   # the shared expert's 200 rows in one tile
     (600, 256, 256, 32, 8, 1),   # 4800 pairs: the chunked permutation, separate binary16 rows and plan
+    (2000, 256, 256, 8, 4, 1),   # ~1000 rows per expert + 2000 shared rows: 32 or more row tiles, dealt to
+                                 # the XCDs in blocks of 4 consecutive tiles (one group's, and straddling)
 ], ids=["no_shared", "long_down_rows", "h_8192", "tile_ragged", "odd_blocks", "tile_steady",
-        "small_beside_tiles", "empty_tile_list", "tile_no_shared", "shared_tile", "many_pairs"])
+        "small_beside_tiles", "empty_tile_list", "tile_no_shared", "shared_tile", "many_pairs", "block_dealing"])
 def test_fp8_small_every_token(T, H, I, E, K, shared):
     _torch()
     w = wl.custom(f"fp8_{T}", T, H, I, E, K, x_seed=41, w_seed=42, n_shared=shared, quant="fp8")

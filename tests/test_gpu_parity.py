@@ -291,14 +291,17 @@ def test_permute_call_integer_exact():
 
 @pytest.mark.parametrize("y_bf16", [False, True])
 @pytest.mark.parametrize("sizes", [[30, 0, 55, 0, 95], [3, 0, 5, 1, 0], [16, 0, 17, 0, 31], [1, 0, 63],
-                                   [2, 40, 0, 7, 300, 1, 33, 32, 0, 5, 17, 64, 3, 0, 9, 120, 1, 31, 0, 2, 8, 0, 50, 4]],
+                                   [2, 40, 0, 7, 300, 1, 33, 32, 0, 5, 17, 64, 3, 0, 9, 120, 1, 31, 0, 2, 8, 0, 50, 4],
+                                   [2100, 0, 1500, 1100, 800, 600, 400, 300, 260, 40, 20]],
                          ids=["tile_kernels", "stream_kernels", "skinny_kernels", "skinny_one_and_63",
-                              "many_groups_both"])
+                              "many_groups_both", "chunked_dealing"])
 def test_grouped_swiglu_and_combine_calls(y_bf16, sizes):
     # skinny_*: at most 64 rows in all and more than 4 per group: the skinny kernels (16 / 17 / 31 rows:
     # one, two and two MFMA row blocks; empty groups between and at the end)
     # many_groups_both: 24 groups, so the groups of at most 32 rows go to the weight-stream kernels and
     # the others (33 .. 300 rows) to the tile kernels in the same call
+    # chunked_dealing: 35 row tiles (groups of 1 to 9 tiles), so blocks of 4 consecutive tiles go to the
+    # XCDs: blocks of one group's tiles (run slab by slab) beside blocks that straddle groups
     torch = _torch()
     w = wl.custom("gs", T=90, H=256, I=384, E=len(sizes), K=2)
     t = wl.device_inputs(w)
