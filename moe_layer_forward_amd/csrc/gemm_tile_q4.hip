@@ -16,7 +16,8 @@ namespace {
 //     18 KiB of an FP8 code stage.  Per wave and block: 2 code pieces of 16 rows x 64 bytes (16-byte
 //     lanes) and one scale piece of 32 rows x 8 bytes (4-byte lanes), 3 loads.
 //   * LDS: 16-byte chunk c (0 .. 3) of a 64-byte code row r sits at c ^ ((r >> 2) & 3), so the 8-byte
-//     reads of the 16 rows of one 16-lane group cover all 64 banks.
+//     reads of two 16-lane groups (the 16 rows of a column block, both halves of one chunk) fall in
+//     all 64 banks.
 //   * A lane of group g (lane / 16) takes inputs 16 g .. 16 g + 15 of a step, as in the FP8 tiles:
 //     two words of codes (k-substeps 0 and 1) and one scale (group (64 (kt mod 2) + 16 g) / 32 of the
 //     block) per column block and step.
