@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 //     below 2^-14 absolute).  A wave's 64 weight rows lie in one 128-row scale block, so its scales
 //     are one per K block: lane j holds K block j's (at most 64 blocks, K <= 8192).
 //   * The shared expert (bf16 weights) is a group of the same tile list: its tiles run the bf16 body.
-//   * Row tiles are 224 rows (kTileMQ): at most 7 16-row blocks per wave, 112 accumulator VGPRs,
+//   * Row tiles are 224 rows (kTileMFp8): at most 7 16-row blocks per wave, 112 accumulator VGPRs,
 //     so that the decode's registers fit beside them without spills (a spill reload inside the K
 //     loop waits for every load in flight).  A K2 prefill expert (~170 rows) is still one tile.
 // Lane j's block scale s (K block j of the wave's 128-row block); 1.0 past the last block.
@@ -298,7 +298,7 @@ __device__ __forceinline__ void gateup_fp8_item(const QTileArgs& q, const Rings&
     Out::store(rings, m_valid, h, I, rbeg, h0, I);
   };
   const QRings qr{{rings.a[0], rings.a[1], rings.b[0]}, {rings.b[1], rings.b[2]}};
-  run_tile<kTileMQ / 32>((m_valid + 15) / 16, wr, [&](auto b, auto a) {
+  run_tile<kTileMFp8 / 32>((m_valid + 15) / 16, wr, [&](auto b, auto a) {
     q_tile_body<Fp8Tiles<true>, decltype(b)::value, decltype(a)::value>(o, qr, x, epilogue);
   });
 }
@@ -359,7 +359,7 @@ __device__ __forceinline__ void down_fp8_item(const QTileArgs& q, const Rings& r
     Out::store(rings, m_valid, y, H, rbeg, n0, H);
   };
   const QRings qr{{rings.a[0], rings.a[1], rings.b[0]}, {rings.b[1], rings.b[2]}};
-  run_tile<kTileMQ / 32>((m_valid + 15) / 16, wr, [&](auto b, auto a) {
+  run_tile<kTileMFp8 / 32>((m_valid + 15) / 16, wr, [&](auto b, auto a) {
     q_tile_body<Fp8Tiles<false>, decltype(b)::value, decltype(a)::value>(o, qr, x, epilogue);
   });
 }
@@ -512,9 +512,9 @@ bool tile_quant_shape_ok(QFormat f, int H, int I) {
 hipError_t launch_gateup_tile_quant(const Groups& g, const Weights& w, const QWeights& q, const uint16_t* x,
                                     const uint16_t* x16, uint16_t* h, int H, int I, hipStream_t s) {
   if (q.format == QFormat::kInt4) return launch_gateup_tile_q4(g, w, q, x, x16, h, H, I, s);
-  if (!tile_quant_shape_ok(q.format, H, I) || g.tile_m != kTileMQ) return hipErrorInvalidValue;
+  if (!tile_quant_shape_ok(q.format, H, I) || g.tile_m != kTileMFp8) return hipErrorInvalidValue;
   QTileArgs a{{g.group_offsets, g.row_index, g.tiles, g.counters, g.max_rows, w, x, h, 1, nullptr, H, I, I / 128, 1,
-               nullptr, kTileMQ},
+               nullptr, kTileMFp8},
               x16,
               static_cast<const uint8_t*>(q.gate_codes),
               static_cast<const uint8_t*>(q.up_codes),
@@ -527,9 +527,9 @@ hipError_t launch_gateup_tile_quant(const Groups& g, const Weights& w, const QWe
 hipError_t launch_down_tile_quant(const Groups& g, const Weights& w, const QWeights& q, const uint16_t* h,
                                   uint16_t* y_rows, int H, int I, hipStream_t s) {
   if (q.format == QFormat::kInt4) return launch_down_tile_q4(g, w, q, h, y_rows, H, I, s);
-  if (!tile_quant_shape_ok(q.format, H, I) || g.tile_m != kTileMQ) return hipErrorInvalidValue;
+  if (!tile_quant_shape_ok(q.format, H, I) || g.tile_m != kTileMFp8) return hipErrorInvalidValue;
   QTileArgs a{{g.group_offsets, nullptr, g.tiles, g.counters, g.max_rows, w, h, y_rows, 1, nullptr, H, I,
-               (H + 255) / 256, 1, nullptr, kTileMQ},
+               (H + 255) / 256, 1, nullptr, kTileMFp8},
               h,
               static_cast<const uint8_t*>(q.down_codes),
               nullptr,

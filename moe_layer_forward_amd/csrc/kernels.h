@@ -168,7 +168,7 @@ hipError_t launch_down_skinny_bf16(const Groups& g, const Weights& w, const uint
                                    const float* row_scale, float* part, int H, int I, hipStream_t s);
 // Rows per tile used by the tile kernels' plan.
 constexpr int kTileM = 256;     // rows per tile of the tile GEMMs
-constexpr int kTileMQ = 224;   // rows per tile of the FP8 tile GEMMs (their plan's tile_m)
+constexpr int kTileMFp8 = 224;  // rows per tile of the FP8 tile GEMMs (their plan's tile_m)
 constexpr int kTileMQ4 = 192;  // rows per tile of the 4-bit tile GEMMs
 
 // grouped SwiGLU, 4-bit routed experts (weight streaming) ----------------------------

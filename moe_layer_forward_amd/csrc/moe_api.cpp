@@ -355,8 +355,8 @@ QuantWs carve_quant(Carver& cv, const moe_config* c, int64_t T, moe::QFormat f) 
   w.perm_scratch = cv.take<int32_t>(moe::permute_scratch_ints(P, E));
   w.x16 = cv.take<uint16_t>(T * H);
   w.h = cv.take<uint16_t>(rows * I);
-  w.routed = tiles ? carve_plan(cv, E + (shared ? 1 : 0), rows, f == moe::QFormat::kInt4 ? moe::kTileMQ4 : moe::kTileMQ)
-                   : carve_plan(cv, E, P);
+  const int tile_m = f == moe::QFormat::kInt4 ? moe::kTileMQ4 : moe::kTileMFp8;
+  w.routed = tiles ? carve_plan(cv, E + (shared ? 1 : 0), rows, tile_m) : carve_plan(cv, E, P);
   w.y_rows = cv.take<uint16_t>(rows * H);
   return w;
 }

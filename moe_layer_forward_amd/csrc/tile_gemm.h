@@ -74,7 +74,7 @@ struct TileArgs {
   int H, I, n_ntiles;
   int n_ksplit;  // down: K ranges per output tile (partial sums go to part, then a reduction kernel)
   float* part;   // [n_ksplit, max_rows, H] fp32 when n_ksplit > 1
-  int tile_m;    // rows per row tile of the plan (kTileM, or kTileMQ for the FP8 tiles)
+  int tile_m;    // rows per row tile of the plan (kTileM; kTileMFp8 or kTileMQ4 for the quantized tiles)
 };
 
 struct TileRows {
@@ -381,7 +381,7 @@ struct OutTile {
     *reinterpret_cast<uint16_t*>(st + (row % kRowsPer) * kRowB + (((col >> 3) ^ out_swz(row)) << 4) + (col & 7) * 2) =
         f32_to_bf16(v);
   }
-  // binary16, column c at position (c & ~7) | pair_pos(c & 7) (the operand order of the FP8 tiles)
+  // binary16, column c at position (c & ~7) | pair_pos(c & 7) (the operand order of the quantized tiles)
   __device__ static __forceinline__ void put_f16_pairs(const Rings& r, int row, int col, float v) {
     char* st = stage(r, row / kRowsPer);
     const int c = (col & ~7) | (((col & 3) << 1) | ((col >> 2) & 1));
