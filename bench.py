@@ -723,8 +723,8 @@ def main():
     from moe_layer_forward_amd import workloads as wl
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode", choices=list(wl.WORKLOADS))
     ap.add_argument("--also", default="prefill,skew,ep_share,tiny,dense_decode,dense_prefill,decode_int4,decode_fp8,"
                                       "prefill_fp8,prefill_int4",
