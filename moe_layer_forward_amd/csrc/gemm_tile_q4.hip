@@ -115,7 +115,9 @@ __device__ __forceinline__ void read_codes4(const char* Bs, const Q4Frag& f, u32
   }
 }
 
-// MFMAs of one K step of the 4-bit tiles, pipelined with the decoding exactly as q_compute_step.
+// MFMAs of one K step of the 4-bit tiles, pipelined with the decoding exactly as q_compute_step, with
+// the weights as the MFMA's first operand: the accumulators hold their blocks transposed, as in
+// compute_step (the FP8 tiles keep the other order, which their registers need).
 template <int NBW, int HF, int HFN, bool GU, bool kFirst>
 __device__ __forceinline__ void q4_compute_step(const char* As, const char* Bs, const char* Bn, bool has_next,
                                                 const Q4Frag& f, Q4Carry& c, f32x4 (&acc)[NBW > 0 ? NBW : 1][4]) {
@@ -162,7 +164,7 @@ __device__ __forceinline__ void q4_compute_step(const char* As, const char* Bs, 
       const int kk = fi / NBW, i = fi % NBW;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[fi], kk == 0 ? c.b0[s] : b1[s], acc[i][s], 0, 0, 0);
+        acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kk == 0 ? c.b0[s] : b1[s], a[fi], acc[i][s], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
@@ -234,13 +236,13 @@ __device__ __forceinline__ void gateup_q4_item(const QTileArgs& q, const Rings& 
     block_sync_lds();  // every wave is done reading the rings
     static_for<NBW>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
+      const int row = 16 * (wr + 2 * i) + (lane & 15);  // accumulators transposed, as in compute_step
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * (wr + 2 * i) + 4 * (lane >> 4) + e;
+      for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-          Out::put_f16_pairs(rings, row, 32 * wc + 16 * s + (lane & 15), swiglu_f32(acc[i][s][e], acc[i][s + 2][e]));
-      }
+        for (int e = 0; e < 4; ++e)
+          Out::put_f16_pairs(rings, row, 32 * wc + 16 * s + 4 * (lane >> 4) + e,
+                             swiglu_f32(acc[i][s][e], acc[i][s + 2][e]));
     });
     block_sync_lds();
     Out::store(rings, m_valid, h, I, rbeg, h0, I);
@@ -291,11 +293,11 @@ __device__ __forceinline__ void down_q4_item(const QTileArgs& q, const Rings& ri
     block_sync_lds();
     static_for<NBW>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
+      const int row = 16 * (wr + 2 * i) + (lane & 15);  // accumulators transposed, as in compute_step
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * (wr + 2 * i) + 4 * (lane >> 4) + e;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) Out::put(rings, row, 64 * wc + 16 * s + (lane & 15), acc[i][s][e]);
+      for (int s = 0; s < 4; ++s) {
+        const float v[4] = {acc[i][s][0], acc[i][s][1], acc[i][s][2], acc[i][s][3]};
+        Out::put4(rings, row, 64 * wc + 16 * s + 4 * (lane >> 4), v);
       }
     });
     block_sync_lds();

@@ -48,6 +48,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 512, kWaves = 8;
 constexpr int kBK = 64;                              // k per step
@@ -214,8 +215,10 @@ struct Frag {
 };
 
 // MFMAs of one K step: NBW 16-row blocks x 4 column blocks x 2 k-substeps, as one sequence of 2 NBW
-// fragments (fragment fi: k-substep fi / NBW, row block fi % NBW).  acc[i][s]: lane l, element e =
-// row 16 (wr + 2i) + 4 (l >> 4) + e, column block s, column l & 15.  Each A fragment is read from LDS
+// fragments (fragment fi: k-substep fi / NBW, row block fi % NBW).  The weight fragment is the MFMA's
+// first operand, so acc[i][s] holds the block transposed: lane l, element e = token row
+// 16 (wr + 2i) + (l & 15), column 4 (l >> 4) + e of column block s (4 consecutive columns per lane,
+// which the epilogues write as one 8-byte piece).  Each A fragment is read from LDS
 // two fragments ahead of its MFMAs and the second k-substep's 4 B fragments two fragments before
 // that substep starts, in a fixed order (a scheduling barrier after each fragment's MFMAs), so each
 // LDS read has 8 MFMAs to land behind.
@@ -242,7 +245,7 @@ __device__ __forceinline__ void compute_step(const char* As, const char* Bs, con
       }
       const int kk = fi / NBW, i = fi % NBW;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fi], b[kk][s], acc[i][s], 0, 0, 0);
+      for (int s = 0; s < 4; ++s) acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[kk][s], a[fi], acc[i][s], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
@@ -381,6 +384,14 @@ struct OutTile {
     *reinterpret_cast<uint16_t*>(st + (row % kRowsPer) * kRowB + (((col >> 3) ^ out_swz(row)) << 4) + (col & 7) * 2) =
         f32_to_bf16(v);
   }
+  // columns col .. col + 3 (col a multiple of 4) of a row: one 8-byte write
+  __device__ static __forceinline__ void put4(const Rings& r, int row, int col, const float (&v)[4]) {
+    char* st = stage(r, row / kRowsPer);
+    const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    *reinterpret_cast<u32x2*>(st + (row % kRowsPer) * kRowB + (((col >> 3) ^ out_swz(row)) << 4) + (col & 7) * 2) =
+        u32x2{lo, hi};
+  }
   // binary16, column c at position (c & ~7) | pair_pos(c & 7) (the operand order of the quantized tiles)
   __device__ static __forceinline__ void put_f16_pairs(const Rings& r, int row, int col, float v) {
     char* st = stage(r, row / kRowsPer);
@@ -479,12 +490,13 @@ __device__ __forceinline__ void gateup_bf16_item(const TileArgs& p, const Rings&
     block_sync_lds();  // every wave is done reading the rings
     static_for<NBW>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
+      const int row = 16 * (wr + 2 * i) + (lane & 15);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * (wr + 2 * i) + 4 * (lane >> 4) + e;
+      for (int s = 0; s < 2; ++s) {  // gate block s and up block s + 2 hold the same h columns
+        float hv[4];
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-          Out::put(rings, row, 32 * wc + 16 * s + (lane & 15), swiglu_f32(acc[i][s][e], acc[i][s + 2][e]));
+        for (int e = 0; e < 4; ++e) hv[e] = swiglu_f32(acc[i][s][e], acc[i][s + 2][e]);
+        Out::put4(rings, row, 32 * wc + 16 * s + 4 * (lane >> 4), hv);
       }
     });
     block_sync_lds();
@@ -541,12 +553,12 @@ __device__ __forceinline__ void down_bf16_item(const TileArgs& p, const Rings& r
       block_sync_lds();  // every wave is done reading the rings
       static_for<NBW>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
+        const int row = 16 * (wr + 2 * i) + (lane & 15);
+        const float sc = row_scale && row < m_valid ? row_scale[rbeg + row] : 1.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 16 * (wr + 2 * i) + 4 * (lane >> 4) + e;
-          const float sc = row_scale && row < m_valid ? row_scale[rbeg + row] : 1.f;
-#pragma unroll
-          for (int s = 0; s < 4; ++s) Out::put(rings, row, 64 * wc + 16 * s + (lane & 15), acc[i][s][e] * sc);
+        for (int s = 0; s < 4; ++s) {
+          const float v[4] = {acc[i][s][0] * sc, acc[i][s][1] * sc, acc[i][s][2] * sc, acc[i][s][3] * sc};
+          Out::put4(rings, row, 64 * wc + 16 * s + 4 * (lane >> 4), v);
         }
       });
       block_sync_lds();
@@ -555,18 +567,18 @@ __device__ __forceinline__ void down_bf16_item(const TileArgs& p, const Rings& r
     }
     // fp32 rows (a caller's choice in moe_grouped_swiglu, or a K range's partial sums): direct stores
 #pragma unroll
-    for (int i = 0; i < NBW; ++i)
+    for (int i = 0; i < NBW; ++i) {
+      const int64_t r = rbeg + 16 * (wr + 2 * i) + (lane & 15);
+      if (r >= rend) continue;
+      const float sc = row_scale ? row_scale[r] : 1.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t r = rbeg + 16 * (wr + 2 * i) + 4 * (lane >> 4) + e;
-        if (r >= rend) continue;
-        const float sc = row_scale ? row_scale[r] : 1.f;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int col = n0 + 64 * wc + 16 * s + (lane & 15);
-          if (col < H) static_cast<float*>(out)[r * H + col] = acc[i][s][e] * sc;
-        }
+      for (int s = 0; s < 4; ++s) {  // 4 consecutive columns: all below H or none (H is a multiple of 128)
+        const int col = n0 + 64 * wc + 16 * s + 4 * (lane >> 4);
+        if (col < H)
+          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + r * H + col) =
+              f32x4{acc[i][s][0] * sc, acc[i][s][1] * sc, acc[i][s][2] * sc, acc[i][s][3] * sc};
       }
+    }
   };
   run_tile((m_valid + 15) / 16, wr, [&](auto b, auto a) {
     tile_body<decltype(b)::value, decltype(a)::value>(o, rings, f, epilogue);
@@ -576,7 +588,6 @@ __device__ __forceinline__ void down_bf16_item(const TileArgs& p, const Rings& r
 // ----------------------------------------------------------------------------- quantized weights
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct QTileArgs {
   TileArgs p;             // plan, bf16 operands of the shared expert (a: bf16 rows), output
