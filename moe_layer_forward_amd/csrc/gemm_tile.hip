@@ -148,7 +148,9 @@ __device__ __forceinline__ void read_codes(const char* Bs, const QFrag& f, u32x4
   for (int s = 0; s < 4; ++s) q[s] = *reinterpret_cast<const u32x4*>(Bs + f.b_row0[s] + f.b_off[HF]);
 }
 
-// MFMAs of one K step, in compute_step's fragment order, software-pipelined with the decoding: the
+// MFMAs of one K step, in compute_step's fragment order, software-pipelined with the decoding (the down
+// GEMM with the weights as the MFMA's first operand, its accumulators transposed as in compute_step;
+// the gate/up GEMM in the plain order, which its registers need): the
 // step's second-substep weights are decoded from the carried codes during its first substep, the next
 // step's codes are read from LDS (their stage is complete and visible since this step's barrier, and
 // no load of this step writes it) and its first-substep weights decoded during the second substep.
@@ -201,7 +203,8 @@ __device__ __forceinline__ void q_compute_step(const char* As, const char* Bs, c
       const int kk = fi / NBW, i = fi % NBW;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[fi], kk == 0 ? c.b0[s] : b1[s], acc[i][s], 0, 0, 0);
+        acc[i][s] = GU ? __builtin_amdgcn_mfma_f32_16x16x32_f16(a[fi], kk == 0 ? c.b0[s] : b1[s], acc[i][s], 0, 0, 0)
+                       : __builtin_amdgcn_mfma_f32_16x16x32_f16(kk == 0 ? c.b0[s] : b1[s], a[fi], acc[i][s], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
@@ -348,11 +351,11 @@ __device__ __forceinline__ void down_fp8_item(const QTileArgs& q, const Rings& r
     block_sync_lds();
     static_for<NBW>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
+      const int row = 16 * (wr + 2 * i) + (lane & 15);  // accumulators transposed (q_compute_step, !GU)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * (wr + 2 * i) + 4 * (lane >> 4) + e;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) Out::put(rings, row, 64 * wc + 16 * s + (lane & 15), acc[i][s][e]);
+      for (int s = 0; s < 4; ++s) {
+        const float v[4] = {acc[i][s][0], acc[i][s][1], acc[i][s][2], acc[i][s][3]};
+        Out::put4(rings, row, 64 * wc + 16 * s + 4 * (lane >> 4), v);
       }
     });
     block_sync_lds();
