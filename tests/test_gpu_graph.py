@@ -73,11 +73,12 @@ def test_forward_graph_replays_match_eager(T):
     del g
 
 
-@pytest.mark.parametrize("quant", ["int4", "fp8"])
-def test_quantized_forward_graph_replays_match_eager(quant):
+@pytest.mark.parametrize("quant,T,E", [("int4", 24, 40), ("fp8", 24, 40), ("int4", 300, 8), ("fp8", 300, 8)],
+                         ids=["int4_stream", "fp8_stream", "int4_tiles", "fp8_tiles"])
+def test_quantized_forward_graph_replays_match_eager(quant, T, E):
+    # T=24 over 40 experts: the weight-stream kernels; T=300 over 8: the tile kernels (~150 rows per group)
     torch = _torch()
-    T = 24
-    w = wl.custom(f"graph_{quant}", T=T, H=512, I=256, E=40, K=4, x_seed=43, w_seed=44, quant=quant)
+    w = wl.custom(f"graph_{quant}_{T}", T=T, H=512, I=256, E=E, K=4, x_seed=43, w_seed=44, quant=quant)
     t = wl.device_inputs(w)
     cfg = moe.config_for(w)
     fwd, op = ((moe.moe_forward_q4, moe.MOE_OP_FORWARD_Q4) if quant == "int4"
