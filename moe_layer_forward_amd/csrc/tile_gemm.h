@@ -366,8 +366,11 @@ __device__ __forceinline__ void run_tile(int nblk, int wr, const Body& body) {
 
 // Output tiles leave through LDS so that global stores are whole 16-byte chunks of contiguous rows.
 // A bf16 tile of kCols columns is staged over the free ring arrays in order (a0, a1, b0, b1, b2),
-// kRowsPer rows each; 16-byte chunk c of row r at position c ^ out_swz(r).
-__device__ __forceinline__ int out_swz(int r) { return ((r >> 2) & 3) << 1; }
+// kRowsPer rows each; 16-byte chunk c of row r at position c ^ out_swz(r).  A row is 256 or 512 bytes,
+// so position p of any row lies in bank group p mod 16: the 16 consecutive rows of an 8-byte staging
+// write (transposed accumulators), the 4 rows 4 apart of a 2-byte write (plain order) and the chunks
+// of one row that a store reads all fall in distinct bank groups.
+__device__ __forceinline__ int out_swz(int r) { return r & 15; }
 
 template <int kCols>
 struct OutTile {
